@@ -1,0 +1,262 @@
+"""Benchmark of the BF16 delta hot path on one MI355X.
+
+Workload: a 7B-shaped BF16 checkpoint pair: 32 layers, hidden 4096, FFN
+11008, vocab 32000, 291 tensors and 6.74e9 elements per checkpoint.  Both
+checkpoints sit in HBM.  2% of each tensor's elements change, with a
+95/4.5/0.5 mantissa/exponent/sign mix.  In 2-D tensors the changes are
+clustered: 70% fall in 10% of the rows.
+
+One step is the whole hot path over the checkpoint:
+  - one batched compress of all 291 tensors (old, new -> payloads +
+    checksums);
+  - one batched, checksum-verified, in-place decompress of those payloads
+    into a receiver copy of the weights.
+The receiver copy alternates between old and new.  A payload depends only on
+the XOR mask, so the same payload takes new back to old, verified against
+old's checksum.
+
+Reported:
+  value     : GB/s of BF16 weights through the round trip, 2*n / step time
+  compress  : GB/s of weights, and % of HBM peak on algorithmic bytes (4n + P)
+  decompress: GB/s of weights, and % of HBM peak on algorithmic bytes (2n + P + 2c)
+  roofline  : the compress call (the dominant kernel) against 8 TB/s
+  cpu_baseline : the CPU oracle on a bounded sample of the same workload
+
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "compress / decompress GB/s of BF16 weights (% of HBM peak); payload % of orig"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ensure_built():
+    from lossless_bf16_weight_xor_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def generate(workload: str, device, limit=None):
+    from lossless_bf16_weight_xor_amd import synth
+    if workload == "7b":
+        it = synth.config2(device, limit=limit)
+        desc = ("7B-shaped BF16 checkpoint pair (32 layers, hidden 4096, FFN 11008, vocab 32000, "
+                "291 tensors), both resident; 2% of elements changed per tensor, 95/4.5/0.5 "
+                "mantissa/exponent/sign, 70% of changes in 10% of rows")
+    elif workload == "70b-half":
+        it = synth.config5(device, limit=limit)
+        desc = ("one-GPU share of a 70B-shaped model: 40 of 80 layers (hidden 8192, FFN 28672, "
+                "GQA 64q/8kv, head_dim 128, 360 tensors); 1% uniform changes, 95/4.5/0.5")
+    else:
+        raise SystemExit(f"unknown workload {workload}")
+    names, pairs = [], []
+    for name, src, dst in it:
+        names.append(name)
+        pairs.append((src.reshape(-1), dst.reshape(-1)))
+    return names, pairs, desc
+
+
+def cpu_baseline(pairs, gpu_payloads, budget_s: float):
+    """The CPU oracle, single-threaded, timed on a bounded sample of the
+    workload's tensors, walking from the last tensor back.  Each oracle
+    payload is also compared byte for byte with the GPU's."""
+    import oracle
+    from lossless_bf16_weight_xor_amd import synth
+    t_c = t_d = 0.0
+    n_done = 0
+    names = []
+    mismatches = 0
+    for j in range(len(pairs) - 1, -1, -1):
+        src, dst = pairs[j]
+        a = synth.bits(src).cpu().numpy().astype(np.uint16)
+        b = synth.bits(dst).cpu().numpy().astype(np.uint16)
+        t0 = time.perf_counter()
+        payload, cs, _ = oracle.compress(a, b)
+        t1 = time.perf_counter()
+        w = a.copy()
+        st = oracle.decompress_inplace(w, payload, cs)
+        t2 = time.perf_counter()
+        assert st == oracle.OK and np.array_equal(w, b)
+        got = gpu_payloads[j]
+        if got is not None and not (got.size == payload.size and np.array_equal(got, payload)):
+            mismatches += 1
+        t_c += t1 - t0
+        t_d += t2 - t1
+        n_done += a.size
+        names.append(j)
+        if t_c + t_d > budget_s:
+            break
+    return {
+        "value": round(2 * n_done / (t_c + t_d) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(names)} of {len(pairs)} tensors ({2 * n_done / 1e9:.3f} GB of BF16 "
+                  f"weights), compress + decompress, single-threaded C oracle",
+        "compress_gbps": round(2 * n_done / t_c / 1e9, 4),
+        "decompress_gbps": round(2 * n_done / t_d / 1e9, 4),
+        "payload_mismatches_vs_gpu": mismatches,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="7b", choices=["7b", "70b-half"])
+    ap.add_argument("--limit", type=int, default=None, help="first N tensors only (debug)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for the baseline (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the delta path is "
+                          "per-GPU (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    ensure_built()
+    import lossless_bf16_weight_xor_amd as bd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    names, pairs, desc = generate(args.workload, dev, args.limit)
+    torch.cuda.synchronize()
+    n_total = sum(s.numel() for s, _ in pairs)
+    log(f"generated {len(pairs)} tensors, {n_total} elements in {time.time() - t0:.1f}s")
+
+    # payload capacity: framing + 1/8 of the weights, exact size on overflow
+    caps = [bd._first_capacity(s.numel()) for s, _ in pairs]
+    comp = bd.CompressBatch(pairs, caps)
+    comp.run()
+    res = comp.results()
+    if any(r["status"] != bd.OK for r in res):
+        caps = [r["payload_bytes"] for r in res]
+        comp = bd.CompressBatch(pairs, caps)
+        comp.run()
+        res = comp.results()
+    assert all(r["status"] == bd.OK for r in res), "compress failed"
+    cs_new = [r["checksum"] for r in res]
+    payload_total = sum(r["payload_bytes"] for r in res)
+    n_changed = sum(r["n_changed"] for r in res)
+    n_rare = sum(r["n_rare"] for r in res)
+    n_bitmap = sum(r["n_bitmap_blocks"] for r in res)
+    payloads = [comp.payload(j, r["payload_bytes"]) for j, r in enumerate(res)]
+
+    # checksums of old: compress the reverse direction (same payload bytes)
+    rev = bd.CompressBatch([(d, s) for s, d in pairs], caps)
+    rev.run()
+    rres = rev.results()
+    cs_old = [r["checksum"] for r in rres]
+    same = all(torch.equal(rev.payload(j, r["payload_bytes"]), payloads[j])
+               for j, r in enumerate(rres))
+    assert same, "reverse payload differs"
+    del rev
+
+    receiver = [s.clone() for s, _ in pairs]
+    dec = bd.DecompressBatch([(w, p, c) for w, p, c in zip(receiver, payloads, cs_new)])
+    torch.cuda.synchronize()
+    log(f"payload {payload_total} B ({100 * payload_total / (2 * n_total):.3f}% of orig), "
+        f"changed {n_changed}, rare {n_rare}, bitmap blocks {n_bitmap}")
+
+    direction = [0]   # 0: receiver holds old, 1: it holds new
+
+    def step(ev=None):
+        cs = cs_new if direction[0] == 0 else cs_old
+        for j in range(len(cs)):
+            dec.jobs[j].checksum = cs[j]
+        if ev: ev[0].record()
+        comp.run()
+        if ev: ev[1].record()
+        dec.run()
+        if ev: ev[2].record()
+        direction[0] ^= 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert all(r["status"] == bd.OK for r in dec.results()), "warm-up decompress failed"
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dres = dec.results()
+    assert all(r["status"] == bd.OK for r in dres), "decompress failed in the timed region"
+    assert all(r["status"] == bd.OK for r in comp.results()), "compress failed in the timed region"
+    expect_new = direction[0] == 1
+    for w, (s, d) in zip(receiver, pairs):
+        ref = d if expect_new else s
+        assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "receiver not bit-exact"
+
+    t_comp = [evs[i][0].elapsed_time(evs[i][1]) / 1e3 for i in range(args.steps)]
+    t_dec = [evs[i][1].elapsed_time(evs[i][2]) / 1e3 for i in range(args.steps)]
+    tc, td = float(np.mean(t_comp)), float(np.mean(t_dec))
+    ms_per_step = 1e3 * elapsed / args.steps
+    w_bytes = 2 * n_total
+    comp_alg = 4 * n_total + payload_total
+    dec_alg = 2 * n_total + payload_total + 2 * n_changed
+    value = w_bytes / (elapsed / args.steps) / 1e9
+
+    gpu_payloads = [None] * len(pairs)
+    cpu = None
+    if args.cpu_budget > 0:
+        for j in range(len(pairs) - 1, max(-1, len(pairs) - 40), -1):
+            gpu_payloads[j] = payloads[j].cpu().numpy()
+        cpu = cpu_baseline(pairs, gpu_payloads, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": desc, "tensors": len(pairs), "elements": n_total,
+                   "weights_bytes": w_bytes, "parallelism": "single GPU"},
+        "compress": {"gbps_weights": round(w_bytes / tc / 1e9, 2),
+                     "hbm_pct": round(100 * comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 2),
+                     "ms": round(1e3 * tc, 4), "algorithmic_bytes": comp_alg},
+        "decompress": {"gbps_weights": round(w_bytes / td / 1e9, 2),
+                       "hbm_pct": round(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS, 2),
+                       "ms": round(1e3 * td, 4), "algorithmic_bytes": dec_alg},
+        "payload_pct_of_orig": round(100 * payload_total / w_bytes, 4),
+        "payload_bytes": payload_total,
+        "n_changed": n_changed, "n_rare": n_rare, "bitmap_blocks": n_bitmap,
+        "roofline": {"bound": "hbm", "kernel": "bf16d_compress call",
+                     "achieved": round(comp_alg / tc / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

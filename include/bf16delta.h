@@ -1,0 +1,201 @@
+/*
+ * bf16delta.h -- C ABI of libbf16delta: lossless delta compression of BF16
+ * checkpoints on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Sources are cited by page title and section:
+ *  - "GPU-accelerated Weight Teleportation", section "Delta update algebra":
+ *    the delta between two checkpoints is the bitwise XOR of their bit
+ *    patterns, and the receiver rebuilds the new weights by XOR-ing that mask
+ *    onto the old ones.  The work is bitwise, with no floating point.
+ *  - "Every byte counts: ARCv3 and the case for cross-region RL", section
+ *    "Deep dive into ARCv3" and the figure "How ARCv3 encodes a block of
+ *    weights":
+ *    - each changed element is classified as mantissa-only or as an
+ *      exponent/sign change;
+ *    - unchanged elements cost nothing;
+ *    - mantissa-only changes carry only their mantissa bits;
+ *    - the rare exponent/sign changes are packed in a stream of their own;
+ *    - the receiver applies both streams to the previous checkpoint and
+ *      checks the result against a checksum of the trainer's weights.
+ *  - same page, section "Using ARCv3": compress(src, dst) returns the
+ *    compressed diff and a checksum; decompress(src, diff, checksum)
+ *    returns weights equal to dst bit for bit.
+ *  - "A strong baseline with Blackwell-native DE" (Weight Teleportation):
+ *    the XOR is applied in place in HBM by one launch that reads a plan
+ *    prepared on the CPU.  Here the plan is the job table passed to
+ *    bf16d_compress / bf16d_decompress.
+ *
+ * Wire format "bf16delta_v1".  The pages fix no format; this one is the
+ * project's own and is not ARCv3's.
+ *   - Elements are 16-bit patterns, in blocks of BF16D_BLOCK_ELEMS = 8192
+ *     (the last block may be shorter).
+ *   - Header, 64 bytes, little-endian:
+ *       magic "BF16DXOR", u32 version = 1, u32 block_elems = 8192, u64 n,
+ *       u64 n_changed, u64 n_rare, u64 pos_bytes, u64 mant_bytes,
+ *       u64 rare_bytes.
+ *   - Then one u32 descriptor per block:
+ *       c | r << 14 | code << 28
+ *     c counts changed elements, r counts exponent/sign ("rare") changes.
+ *     code 0..13 means a gap list of width `code`; 15 means a bitmap;
+ *     14 is invalid.
+ *   - Then one record per block, in block order, with no padding between
+ *     records:
+ *       position segment : either c gap fields of `code` bits or one bit per
+ *                          element, whichever is smaller (a tie goes to the
+ *                          gap list)
+ *       mantissa segment : c fields of 7 bits, each the mantissa XOR, or 0
+ *                          for an exponent/sign change
+ *       rare segment     : r u16 words, the full XOR of every exponent/sign
+ *                          change
+ *     Bit fields are packed LSB-first and each segment is zero-padded to a
+ *     byte.
+ *   - Checksum of the new weights:
+ *       checksum = mix64(S ^ n)
+ *       S        = sum over k of mix64(W_k ^ (k+1) * 0x9E3779B97F4A7C15)
+ *                  mod 2^64
+ *     W_k is the little-endian u64 of elements 4k..4k+3; missing elements
+ *     are 0.  mix64 is the SplitMix64 finaliser.
+ *
+ * Conventions shared by every entry point:
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no state between calls.
+ *   - src, dst, weights, payload and workspace are device pointers and must
+ *     be 16-byte aligned.
+ *   - `results` must be memory the device can write: device memory, or
+ *     pinned host memory.
+ *   - `stream` is a HIP stream; NULL means the null stream.  All device work
+ *     is enqueued on it, and results[] is valid once the stream has
+ *     completed.
+ *   - The return value reports only errors the host can detect before
+ *     enqueueing anything:
+ *       BF16D_EINVAL  bad pointer, alignment, size, overlap, or a workspace
+ *                     that is too small;
+ *       BF16D_EHIP    a HIP runtime call failed.
+ *     Errors found on the device land in results[i].status.
+ *   - Calls that share a workspace, payload or weight buffer must not
+ *     overlap in time (for example, on two streams).
+ */
+#ifndef BF16DELTA_H
+#define BF16DELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BF16D_OK        0  /* success */
+#define BF16D_EINVAL    1  /* invalid arguments (host-detected; nothing enqueued) */
+#define BF16D_ECAPACITY 2  /* compress: payload larger than capacity; required size reported */
+#define BF16D_EFORMAT   3  /* decompress: malformed or mismatched payload; weights end old */
+#define BF16D_ECHECKSUM 4  /* decompress: rebuilt weights fail the checksum; weights end old */
+#define BF16D_EHIP      5  /* a HIP runtime call failed */
+
+#define BF16D_BLOCK_ELEMS    8192
+#define BF16D_HEADER_BYTES   64
+#define BF16D_FORMAT_VERSION 1
+
+/* Per-job outcome, written by the device. 48 bytes. */
+typedef struct bf16d_result {
+    int32_t  status;          /* BF16D_OK, BF16D_ECAPACITY, BF16D_EFORMAT or BF16D_ECHECKSUM */
+    uint32_t reserved;
+    uint64_t payload_bytes;   /* compress: bytes written, or bytes required on ECAPACITY;
+                                 decompress: the payload length given */
+    uint64_t checksum;        /* compress: checksum of dst; decompress: checksum of the
+                                 weights after the apply pass (before any rollback), or 0
+                                 if the payload was rejected before applying */
+    uint64_t n_changed;       /* elements whose XOR is non-zero */
+    uint64_t n_rare;          /* elements whose XOR touches the exponent or the sign */
+    uint64_t n_bitmap_blocks; /* blocks whose position segment is a bitmap */
+} bf16d_result;
+
+/* One tensor to compress.
+ *   src, dst : device, 16-byte aligned, n elements each.  They are read only
+ *              and may be the same buffer; they may be NULL when n == 0.
+ *   payload  : device, 16-byte aligned, capacity bytes.  It must not overlap
+ *              src or dst.
+ *   capacity : room in payload.  bf16d_max_payload_bytes(n) always suffices.
+ *              If it is too small, the status is BF16D_ECAPACITY, the
+ *              required size is reported, nothing is written at or beyond
+ *              capacity, and the bytes below it are unspecified. */
+typedef struct bf16d_compress_job {
+    const uint16_t *src;
+    const uint16_t *dst;
+    uint64_t        n;
+    uint8_t        *payload;
+    uint64_t        capacity;
+} bf16d_compress_job;
+
+/* One tensor to rebuild in place.
+ *   weights       : device, 16-byte aligned, n elements.  It holds the old
+ *                   weights on entry, and the new ones on BF16D_OK.  On any
+ *                   other status it holds the old ones bit for bit (XOR is
+ *                   its own inverse, so the pass is undone).
+ *   payload       : device, 16-byte aligned, payload_bytes bytes.  It must
+ *                   not overlap weights.  It may be NULL only when
+ *                   payload_bytes is 0; such a payload is too short, and the
+ *                   status is BF16D_EFORMAT.
+ *   checksum      : the value returned by compress for this tensor. */
+typedef struct bf16d_decompress_job {
+    uint16_t      *weights;
+    uint64_t       n;
+    const uint8_t *payload;
+    uint64_t       payload_bytes;
+    uint64_t       checksum;
+} bf16d_decompress_job;
+
+/* Upper bound on the bytes of an n-element payload.  Per block it is:
+ * a bitmap-sized position segment, with every element changed and rare. */
+uint64_t bf16d_max_payload_bytes(uint64_t n);
+
+/* Workspace bytes that suffice for any batch of `count` jobs totalling
+ * total_n elements, in either direction. */
+size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count);
+
+/* Compress `count` tensors in one batched pass: old = src, new = dst.
+ * The job array is host memory.  It is copied into the workspace before
+ * the call returns, so it may be freed right after.  results[i] receives
+ * job i's outcome.  All jobs share one launch per kernel; each job gets its
+ * own payload and checksum. */
+int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count,
+                   void *workspace, size_t workspace_bytes,
+                   bf16d_result *results, hipStream_t stream);
+
+/* Apply `count` payloads in place in one batched pass.  Per job, one of:
+ *   - a bad header or descriptor table: BF16D_EFORMAT, weights untouched;
+ *   - a malformed block record: BF16D_EFORMAT, pass undone, weights old;
+ *   - a checksum mismatch: BF16D_ECHECKSUM, pass undone, weights old;
+ *   - BF16D_OK, weights new. */
+int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count,
+                     void *workspace, size_t workspace_bytes,
+                     bf16d_result *results, hipStream_t stream);
+
+/* Single-tensor forms of the two calls above, named after the pages'
+ * delta_compress(src, dst) -> (payload, checksum) and
+ * delta_decompress(src, payload, checksum) -> dst ("Every byte counts:
+ * ARCv3 and the case for cross-region RL", section "Using ARCv3").
+ * delta_decompress rebuilds dst in src_inout, in place. */
+int bf16d_delta_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
+                         uint8_t *payload, uint64_t capacity,
+                         void *workspace, size_t workspace_bytes,
+                         bf16d_result *result, hipStream_t stream);
+
+int bf16d_delta_decompress(uint16_t *src_inout, uint64_t n,
+                           const uint8_t *payload, uint64_t payload_bytes,
+                           uint64_t checksum,
+                           void *workspace, size_t workspace_bytes,
+                           bf16d_result *result, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *bf16d_status_string(int status);
+
+/* Wire-format version this library reads and writes (1). */
+int bf16d_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BF16DELTA_H */

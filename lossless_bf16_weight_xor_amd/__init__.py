@@ -1,0 +1,244 @@
+"""Lossless delta compression of BF16 checkpoints on AMD MI355X (gfx950).
+
+Python binding of libbf16delta (include/bf16delta.h).  It only marshals
+arguments: torch tensors supply device memory and streams, and every step of
+compression and decompression runs in the library's HIP kernels.  There is no
+CPU fallback; tensors must live on a HIP device.
+
+The call shapes follow "Every byte counts: ARCv3 and the case for
+cross-region RL", section "Using ARCv3":
+
+    payload, checksum = delta_compress(src, dst)
+    restored = delta_decompress(src, payload, checksum)   # src is rebuilt in place
+
+The wire format is this project's own "bf16delta_v1", not ARCv3's.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import torch
+
+from . import _native
+from ._native import (OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, BLOCK_ELEMS,
+                      HEADER_BYTES, CompressJob, DecompressJob, RESULT_BYTES)
+
+FORMAT = "bf16delta_v1"
+_ALIGN = 256   # payload slots inside an arena start on this boundary
+
+__all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_batch",
+           "CompressBatch", "DecompressBatch", "FormatError", "ChecksumError",
+           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
+
+
+class FormatError(ValueError):
+    """The payload is malformed or does not match the tensor (weights end old)."""
+
+
+class ChecksumError(RuntimeError):
+    """The rebuilt weights fail the checksum (weights end old)."""
+
+
+class CapacityError(RuntimeError):
+    """A payload buffer is too small."""
+
+
+def max_payload_bytes(n: int) -> int:
+    return int(_native.lib().bf16d_max_payload_bytes(n))
+
+
+def workspace_bytes(total_n: int, count: int) -> int:
+    return int(_native.lib().bf16d_workspace_bytes(total_n, count))
+
+
+def _check_format(compression_format: str) -> None:
+    if compression_format != FORMAT:
+        raise ValueError(f"unsupported compression_format {compression_format!r}: this "
+                         f"library reads and writes {FORMAT!r} only")
+
+
+def _weights_ptr(t: torch.Tensor, what: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{what} must be a tensor on a HIP device (got "
+                        f"{getattr(t, 'device', type(t))}); there is no CPU path")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what} must hold 16-bit patterns (bfloat16), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() and t.data_ptr() % 16:
+        raise ValueError(f"{what} must be 16-byte aligned")
+    return t.data_ptr() if t.numel() else 0
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_rc(rc: int, what: str) -> None:
+    if rc != OK:
+        raise RuntimeError(f"{what} failed: {_native.status_string(rc)}")
+
+
+def _results(buf: torch.Tensor, count: int) -> list[dict]:
+    host = buf[: count * RESULT_BYTES].cpu().numpy().tobytes()
+    out = []
+    for j in range(count):
+        r = _native.Result.from_buffer_copy(host, j * RESULT_BYTES)
+        out.append({k: int(getattr(r, k)) for k, _ in _native.Result._fields_ if k != "reserved"})
+    return out
+
+
+class CompressBatch:
+    """A prepared batched compress call over fixed (src, dst) pairs.
+
+    It owns one payload arena (a slot of `capacity[j]` bytes per job), the
+    workspace, and a device result buffer.  `run()` enqueues one batched call
+    on the current stream.  `results()` waits for it and returns one dict
+    per job."""
+
+    def __init__(self, pairs: Sequence[tuple[torch.Tensor, torch.Tensor]],
+                 capacities: Sequence[int] | None = None):
+        if not pairs:
+            raise ValueError("empty batch")
+        self.device = pairs[0][0].device
+        self.count = len(pairs)
+        self.n = [p[0].numel() for p in pairs]
+        if capacities is None:
+            capacities = [max_payload_bytes(n) for n in self.n]
+        self.capacity = [int(c) for c in capacities]
+        self.offset = []
+        at = 0
+        for cap in self.capacity:
+            self.offset.append(at)
+            at += (cap + _ALIGN - 1) // _ALIGN * _ALIGN
+        self.arena = torch.empty(max(at, _ALIGN), dtype=torch.uint8, device=self.device)
+        self.ws_bytes = workspace_bytes(sum(self.n), self.count)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
+                                      device=self.device)
+        self.jobs = (CompressJob * self.count)()
+        base = self.arena.data_ptr()
+        self.pairs = list(pairs)   # keep the tensors alive
+        for j, (src, dst) in enumerate(pairs):
+            if src.shape != dst.shape:
+                raise ValueError(f"job {j}: src and dst differ in shape")
+            if src.device != self.device or dst.device != self.device:
+                raise ValueError("all tensors of a batch must be on one device")
+            self.jobs[j] = CompressJob(_weights_ptr(src, "src"), _weights_ptr(dst, "dst"),
+                                       src.numel(), base + self.offset[j], self.capacity[j])
+
+    def run(self) -> None:
+        rc = _native.lib().bf16d_compress(self.jobs, self.count, self.workspace.data_ptr(),
+                                          self.ws_bytes, self.result_buf.data_ptr(),
+                                          _stream(self.device))
+        _check_rc(rc, "bf16d_compress")
+
+    def results(self) -> list[dict]:
+        return _results(self.result_buf, self.count)
+
+    def payload(self, j: int, nbytes: int) -> torch.Tensor:
+        return self.arena[self.offset[j]: self.offset[j] + nbytes]
+
+
+class DecompressBatch:
+    """A prepared batched in-place decompress call over fixed (weights, payload,
+    checksum) triples.  `run()` enqueues it on the current stream."""
+
+    def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]]):
+        if not items:
+            raise ValueError("empty batch")
+        self.device = items[0][0].device
+        self.count = len(items)
+        self.items = list(items)
+        n_total = sum(w.numel() for w, _, _ in items)
+        self.ws_bytes = workspace_bytes(n_total, self.count)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
+                                      device=self.device)
+        self.jobs = (DecompressJob * self.count)()
+        for j, (w, payload, checksum) in enumerate(items):
+            self._set(j, w, payload, checksum)
+
+    def _set(self, j, w, payload, checksum):
+        if payload.dtype != torch.uint8 or payload.device != self.device or \
+                not payload.is_contiguous():
+            raise TypeError("payload must be a contiguous uint8 tensor on the weights' device")
+        if payload.data_ptr() % 16:
+            raise ValueError("payload must be 16-byte aligned")
+        self.jobs[j] = DecompressJob(_weights_ptr(w, "weights"), w.numel(), payload.data_ptr(),
+                                     payload.numel(), int(checksum) & 0xFFFFFFFFFFFFFFFF)
+
+    def set_checksum(self, j: int, checksum: int) -> None:
+        self.jobs[j].checksum = int(checksum) & 0xFFFFFFFFFFFFFFFF
+
+    def run(self) -> None:
+        rc = _native.lib().bf16d_decompress(self.jobs, self.count, self.workspace.data_ptr(),
+                                            self.ws_bytes, self.result_buf.data_ptr(),
+                                            _stream(self.device))
+        _check_rc(rc, "bf16d_decompress")
+
+    def results(self) -> list[dict]:
+        return _results(self.result_buf, self.count)
+
+
+def _first_capacity(n: int) -> int:
+    """A first guess at the payload size: framing plus 1/8 of the weights.  A
+    denser delta reports its exact size and is encoded again."""
+    nb = -(-n // BLOCK_ELEMS)
+    return min(max_payload_bytes(n), HEADER_BYTES + 4 * nb + (2 * n) // 8 + 4096)
+
+
+def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]]):
+    """Compress several (src, dst) pairs in one batched call.
+
+    Returns a list of (payload uint8 tensor, checksum int, stats dict).  The
+    payloads are views into one device arena."""
+    caps = [_first_capacity(s.numel()) for s, _ in pairs]
+    batch = CompressBatch(pairs, caps)
+    batch.run()
+    res = batch.results()
+    short = [j for j, r in enumerate(res) if r["status"] == ECAPACITY]
+    if short:
+        caps = [res[j]["payload_bytes"] if j in short else caps[j] for j in range(len(pairs))]
+        batch = CompressBatch(pairs, caps)
+        batch.run()
+        res = batch.results()
+    out = []
+    for j, r in enumerate(res):
+        if r["status"] != OK:
+            raise RuntimeError(f"job {j}: {_native.status_string(r['status'])}")
+        out.append((batch.payload(j, r["payload_bytes"]), r["checksum"], r))
+    return out
+
+
+def decompress_batch(items: Sequence[tuple[torch.Tensor, torch.Tensor, int]]) -> list[dict]:
+    """Apply several payloads in place in one batched call.  Returns the
+    per-job result dicts, without raising on per-job failures."""
+    batch = DecompressBatch(items)
+    batch.run()
+    return batch.results()
+
+
+def delta_compress(src: torch.Tensor, dst: torch.Tensor, compression_format: str = FORMAT):
+    """(compressed_diff, checksum) of the update src -> dst.  Both are bf16
+    tensors of one shape on a HIP device; the payload is a uint8 device tensor."""
+    _check_format(compression_format)
+    payload, checksum, _ = compress_batch([(src, dst)])[0]
+    return payload.clone(), checksum
+
+
+def delta_decompress(src: torch.Tensor, compressed_diff: torch.Tensor, checksum: int,
+                     compression_format: str = FORMAT) -> torch.Tensor:
+    """Rebuild the new weights in place in `src` and return it.  Raises
+    FormatError or ChecksumError (with `src` holding the old weights exactly)
+    if the payload does not apply."""
+    _check_format(compression_format)
+    r = decompress_batch([(src, compressed_diff, checksum)])[0]
+    if r["status"] == EFORMAT:
+        raise FormatError("payload rejected (malformed or not for this tensor); weights unchanged")
+    if r["status"] == ECHECKSUM:
+        raise ChecksumError("rebuilt weights fail the checksum; weights restored to the old values")
+    if r["status"] != OK:
+        raise RuntimeError(_native.status_string(r["status"]))
+    return src

@@ -1,0 +1,84 @@
+"""ctypes declarations of libbf16delta (include/bf16delta.h), and nothing else.
+
+The library is loaded from this package directory.  torch is imported first so
+that the library binds to the HIP runtime torch already uses.  A missing
+library is an error: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library must share)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta.so")
+
+OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP = 0, 1, 2, 3, 4, 5
+BLOCK_ELEMS = 8192
+HEADER_BYTES = 64
+FORMAT_VERSION = 1
+
+EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress",
+            "bf16d_decompress", "bf16d_delta_compress", "bf16d_delta_decompress",
+            "bf16d_status_string", "bf16d_format_version")
+
+
+class Result(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("reserved", ctypes.c_uint32),
+                ("payload_bytes", ctypes.c_uint64), ("checksum", ctypes.c_uint64),
+                ("n_changed", ctypes.c_uint64), ("n_rare", ctypes.c_uint64),
+                ("n_bitmap_blocks", ctypes.c_uint64)]
+
+
+class CompressJob(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("n", ctypes.c_uint64),
+                ("payload", ctypes.c_void_p), ("capacity", ctypes.c_uint64)]
+
+
+class DecompressJob(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_void_p), ("n", ctypes.c_uint64),
+                ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64),
+                ("checksum", ctypes.c_uint64)]
+
+
+RESULT_BYTES = ctypes.sizeof(Result)
+assert RESULT_BYTES == 48
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library; raises LibraryMissing if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        u64, u32, vp, sz = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
+        L.bf16d_max_payload_bytes.argtypes = [u64]
+        L.bf16d_max_payload_bytes.restype = u64
+        L.bf16d_workspace_bytes.argtypes = [u64, u32]
+        L.bf16d_workspace_bytes.restype = sz
+        L.bf16d_compress.argtypes = [ctypes.POINTER(CompressJob), u32, vp, sz, vp, vp]
+        L.bf16d_compress.restype = ctypes.c_int
+        L.bf16d_decompress.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp, vp]
+        L.bf16d_decompress.restype = ctypes.c_int
+        L.bf16d_delta_compress.argtypes = [vp, vp, u64, vp, u64, vp, sz, vp, vp]
+        L.bf16d_delta_compress.restype = ctypes.c_int
+        L.bf16d_delta_decompress.argtypes = [vp, u64, vp, u64, u64, vp, sz, vp, vp]
+        L.bf16d_delta_decompress.restype = ctypes.c_int
+        L.bf16d_status_string.argtypes = [ctypes.c_int]
+        L.bf16d_status_string.restype = ctypes.c_char_p
+        L.bf16d_format_version.argtypes = []
+        L.bf16d_format_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().bf16d_status_string(code).decode()

@@ -1,0 +1,199 @@
+// api.hip -- host side of the libbf16delta C ABI (see include/bf16delta.h).
+//
+// Validates arguments, computes the workspace layout, copies the job table
+// (the CPU-prepared "plan") into the workspace, and enqueues the kernels.
+// Nothing here allocates device memory or keeps state between calls.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace bf16d;
+
+namespace {
+
+constexpr uint64_t kMaxTiles = 1ull << 24;   // grid limit: tiles * 256 threads < 2^32
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t blocks_of(uint64_t n) { return (n + kBlock - 1) / kBlock; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+    bool written;
+};
+
+// A written range may overlap no other range; read ranges may overlap each other.
+bool ranges_disjoint(std::vector<Range> &v) {
+    v.erase(std::remove_if(v.begin(), v.end(), [](const Range &r) { return r.hi <= r.lo; }),
+            v.end());
+    std::sort(v.begin(), v.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    // sweep: compare each range with the furthest-reaching earlier written range
+    // and the furthest-reaching earlier range of any kind
+    uintptr_t reach_any = 0, reach_written = 0;
+    for (const Range &r : v) {
+        if (r.lo < reach_written) return false;
+        if (r.written && r.lo < reach_any) return false;
+        reach_any = std::max(reach_any, r.hi);
+        if (r.written) reach_written = std::max(reach_written, r.hi);
+    }
+    return true;
+}
+
+int upload(void *ws, const std::vector<uint8_t> &host, size_t at, hipStream_t stream) {
+    if (host.empty()) return BF16D_OK;
+    // Pageable source: the runtime stages it before returning, so `host` may be freed.
+    hipError_t e = hipMemcpyAsync(static_cast<uint8_t *>(ws) + at, host.data(), host.size(),
+                                  hipMemcpyHostToDevice, stream);
+    return e == hipSuccess ? BF16D_OK : BF16D_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t bf16d_max_payload_bytes(uint64_t n) {
+    const uint64_t full = n / kBlock, tail = n % kBlock;
+    uint64_t total = kHeader + 4 * blocks_of(n) + full * (uint64_t)kMaxRecord;
+    if (tail) total += (tail + 7) / 8 + (7 * tail + 7) / 8 + 2 * tail;
+    return total;
+}
+
+size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
+    const uint64_t tiles = blocks_of(total_n) + count;
+    const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
+    return make_layout(tiles, dtiles, count).total;
+}
+
+int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
+                   size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
+    if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
+        return BF16D_EINVAL;
+    std::vector<uint64_t> start(size_t(count) + 1, 0);
+    std::vector<Range> ranges;
+    ranges.reserve(3 * size_t(count) + 1);
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_compress_job &J = jobs[j];
+        if (J.n > 0 && (!J.src || !J.dst || !aligned16(J.src) || !aligned16(J.dst)))
+            return BF16D_EINVAL;
+        if (J.capacity > 0 && (!J.payload || !aligned16(J.payload))) return BF16D_EINVAL;
+        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        start[j + 1] = start[j] + blocks_of(J.n);
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.src),
+                          reinterpret_cast<uintptr_t>(J.src) + 2 * J.n, false});
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.dst),
+                          reinterpret_cast<uintptr_t>(J.dst) + 2 * J.n, false});
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
+                          reinterpret_cast<uintptr_t>(J.payload) + J.capacity, true});
+    }
+    const uint64_t tiles = start[count];
+    if (tiles >= kMaxTiles) return BF16D_EINVAL;
+    const Layout l = make_layout(tiles, 0, count);
+    if (workspace_bytes < l.total) return BF16D_EINVAL;
+    ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
+                      reinterpret_cast<uintptr_t>(workspace) + l.total, true});
+    if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
+
+    // job table and block starts, laid out as in the workspace
+    std::vector<uint8_t> host(l.block_start + 8 * (size_t(count) + 1) - l.jobs, 0);
+    auto *dj = reinterpret_cast<CompressJob *>(host.data());
+    for (uint32_t j = 0; j < count; ++j) {
+        dj[j].src = jobs[j].src;
+        dj[j].dst = jobs[j].dst;
+        dj[j].n = jobs[j].n;
+        dj[j].payload = jobs[j].payload;
+        dj[j].capacity = jobs[j].capacity;
+        dj[j].block0 = start[j];
+        dj[j].nb = start[j + 1] - start[j];
+        dj[j].pad = 0;
+    }
+    std::memcpy(host.data() + (l.block_start - l.jobs), start.data(), 8 * start.size());
+    int rc = upload(workspace, host, l.jobs, stream);
+    if (rc != BF16D_OK) return rc;
+    return launch_compress(l, static_cast<uint8_t *>(workspace), count, tiles, results,
+                           stream) == hipSuccess
+               ? BF16D_OK
+               : BF16D_EHIP;
+}
+
+int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
+                     size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
+    if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
+        return BF16D_EINVAL;
+    std::vector<uint64_t> bstart(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
+    std::vector<Range> ranges;
+    ranges.reserve(2 * size_t(count) + 1);
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_decompress_job &J = jobs[j];
+        if (J.n > 0 && (!J.weights || !aligned16(J.weights))) return BF16D_EINVAL;
+        // an empty payload may be NULL; it is then rejected on the device as too short
+        if ((J.payload_bytes > 0 && !J.payload) || !aligned16(J.payload)) return BF16D_EINVAL;
+        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        const uint64_t nb = blocks_of(J.n);
+        bstart[j + 1] = bstart[j] + nb;
+        dstart[j + 1] = dstart[j] + (nb + kDescTile - 1) / kDescTile;
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.weights),
+                          reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
+                          reinterpret_cast<uintptr_t>(J.payload) + J.payload_bytes, false});
+    }
+    const uint64_t tiles = bstart[count], dtiles = dstart[count];
+    if (tiles >= kMaxTiles) return BF16D_EINVAL;
+    const Layout l = make_layout(tiles, dtiles, count);
+    if (workspace_bytes < l.total) return BF16D_EINVAL;
+    ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
+                      reinterpret_cast<uintptr_t>(workspace) + l.total, true});
+    if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
+
+    std::vector<uint8_t> host(l.dtile_start + 8 * (size_t(count) + 1) - l.jobs, 0);
+    auto *dj = reinterpret_cast<DecompressJob *>(host.data());
+    for (uint32_t j = 0; j < count; ++j) {
+        dj[j].weights = jobs[j].weights;
+        dj[j].n = jobs[j].n;
+        dj[j].payload = jobs[j].payload;
+        dj[j].payload_bytes = jobs[j].payload_bytes;
+        dj[j].checksum = jobs[j].checksum;
+        dj[j].block0 = bstart[j];
+        dj[j].nb = bstart[j + 1] - bstart[j];
+        dj[j].dtile0 = dstart[j];
+    }
+    std::memcpy(host.data() + (l.block_start - l.jobs), bstart.data(), 8 * bstart.size());
+    std::memcpy(host.data() + (l.dtile_start - l.jobs), dstart.data(), 8 * dstart.size());
+    int rc = upload(workspace, host, l.jobs, stream);
+    if (rc != BF16D_OK) return rc;
+    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
+                             stream) == hipSuccess
+               ? BF16D_OK
+               : BF16D_EHIP;
+}
+
+int bf16d_delta_compress(const uint16_t *src, const uint16_t *dst, uint64_t n, uint8_t *payload,
+                         uint64_t capacity, void *workspace, size_t workspace_bytes,
+                         bf16d_result *result, hipStream_t stream) {
+    const bf16d_compress_job job = {src, dst, n, payload, capacity};
+    return bf16d_compress(&job, 1, workspace, workspace_bytes, result, stream);
+}
+
+int bf16d_delta_decompress(uint16_t *src_inout, uint64_t n, const uint8_t *payload,
+                           uint64_t payload_bytes, uint64_t checksum, void *workspace,
+                           size_t workspace_bytes, bf16d_result *result, hipStream_t stream) {
+    const bf16d_decompress_job job = {src_inout, n, payload, payload_bytes, checksum};
+    return bf16d_decompress(&job, 1, workspace, workspace_bytes, result, stream);
+}
+
+const char *bf16d_status_string(int status) {
+    switch (status) {
+        case BF16D_OK: return "OK";
+        case BF16D_EINVAL: return "EINVAL: invalid arguments";
+        case BF16D_ECAPACITY: return "ECAPACITY: payload capacity too small";
+        case BF16D_EFORMAT: return "EFORMAT: malformed or mismatched payload";
+        case BF16D_ECHECKSUM: return "ECHECKSUM: rebuilt weights fail the checksum";
+        case BF16D_EHIP: return "EHIP: HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int bf16d_format_version(void) { return BF16D_FORMAT_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+// internal.hpp -- shared definitions of the libbf16delta HIP kernels and the
+// host code that launches them (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bf16delta.h"
+
+namespace bf16d {
+
+// ---- format constants (bf16delta_v1) ---------------------------------------
+constexpr uint32_t kBlock = BF16D_BLOCK_ELEMS;            // elements per block
+constexpr uint32_t kHeader = BF16D_HEADER_BYTES;          // header bytes
+constexpr uint32_t kCodeBitmap = 15;
+constexpr uint32_t kCodeInvalid = 14;
+constexpr uint32_t kExpSign = 0xFF80u;                   // sign + exponent bits of a bf16
+constexpr uint32_t kMant = 0x007Fu;                      // mantissa bits
+// largest record of one block: bitmap-sized position segment + 7 bits and a
+// rare word for every element
+constexpr uint32_t kMaxRecord = kBlock / 8 + (7 * kBlock) / 8 + 2 * kBlock;   // 24576
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint32_t kMagicLo = 0x36314642u;               // "BF16"
+constexpr uint32_t kMagicHi = 0x524F5844u;               // "DXOR"
+
+// ---- launch shape -------------------------------------------------------------
+constexpr uint32_t kThreads = 256;                       // 4 waves of 64
+constexpr uint32_t kWaves = kThreads / 64;
+constexpr uint32_t kChunks = kBlock / 8;                 // 16-byte chunks per block
+constexpr uint32_t kChunksPerThread = kChunks / kThreads;   // 4
+constexpr uint32_t kDescPerThread = 8;
+constexpr uint32_t kDescTile = kThreads * kDescPerThread;   // descriptors per scan tile
+
+// ---- decoupled look-back status words ---------------------------------------
+// bits 62..63: 0 = not yet published, 1 = tile aggregate, 2 = inclusive prefix
+constexpr uint64_t kFlagAggregate = 1ull << 62;
+constexpr uint64_t kFlagPrefix = 2ull << 62;
+constexpr uint64_t kValueMask = (1ull << 62) - 1;
+
+// ---- device-side job tables (copied into the workspace by the host) ---------
+struct alignas(64) CompressJob {
+    const uint16_t *src;
+    const uint16_t *dst;
+    uint64_t n;
+    uint8_t *payload;
+    uint64_t capacity;
+    uint64_t block0;   // first global tile index of this job
+    uint64_t nb;       // blocks of this job
+    uint64_t pad;
+};
+
+enum JobState : uint32_t { kStateReady = 1, kStateRejected = 2 };
+
+struct alignas(64) DecompressJob {
+    uint16_t *weights;
+    uint64_t n;
+    const uint8_t *payload;
+    uint64_t payload_bytes;
+    uint64_t checksum;
+    uint64_t block0;   // first global tile index
+    uint64_t nb;       // blocks
+    uint64_t dtile0;   // first global descriptor-scan tile index
+};
+
+// per-job device state of a decompress call (zeroed by the setup kernel)
+struct alignas(64) DecompressState {
+    unsigned long long sum_c, sum_r, sum_pos, sum_mant, sum_rare, n_bitmap;
+    uint32_t desc_bad;     // a descriptor failed its checks
+    uint32_t state;        // JobState, set by the prepare kernel
+    uint32_t block_bad;    // a block record failed its checks
+    uint32_t rollback;     // the apply pass must be undone
+};
+
+struct alignas(64) Control {
+    uint32_t ticket;       // dynamic tile ids for the compress look-back
+    uint32_t dticket;      // dynamic tile ids for the descriptor-scan look-back
+    uint32_t any_rollback;
+    uint32_t pad[13];
+};
+
+// Workspace layout, computed identically by every entry point.
+struct Layout {
+    size_t control, jobs, block_start, dtile_start, tile_job, status, partial, desc,
+        dtile_job, dstatus, state, total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count) {
+    Layout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    size_t job_bytes = sizeof(CompressJob) > sizeof(DecompressJob) ? sizeof(CompressJob)
+                                                                  : sizeof(DecompressJob);
+    l.control = take(sizeof(Control));
+    l.jobs = take(job_bytes * count);
+    l.block_start = take(8 * (size_t(count) + 1));
+    l.dtile_start = take(8 * (size_t(count) + 1));
+    l.tile_job = take(4 * tiles);
+    l.status = take(8 * tiles);     // compress: look-back words; decompress: record offsets
+    l.partial = take(8 * tiles);    // per-tile checksum partial sums
+    l.desc = take(4 * tiles);       // compress: descriptor copies
+    l.dtile_job = take(4 * dtiles);
+    l.dstatus = take(8 * dtiles);
+    l.state = take(sizeof(DecompressState) * size_t(count));
+    l.total = off;
+    return l;
+}
+
+// ---- device helpers ------------------------------------------------------------
+
+// SplitMix64 finaliser (Steele, Lea and Flood, OOPSLA 2014; Stafford's Mix13).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+__device__ __forceinline__ uint64_t ld_acquire_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        T o = __shfl_xor(v, d, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Block-wide sum over kThreads threads; every thread gets the total.
+// s_tmp needs kWaves entries.  Contains two barriers.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T *s_tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) s_tmp[wave] = v;
+    __syncthreads();
+    T t = 0;
+#pragma unroll
+    for (int w = 0; w < (int)kWaves; ++w) t += s_tmp[w];
+    __syncthreads();
+    return t;
+}
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T *s_tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) s_tmp[wave] = v;
+    __syncthreads();
+    T t = s_tmp[0];
+#pragma unroll
+    for (int w = 1; w < (int)kWaves; ++w) t = s_tmp[w] > t ? s_tmp[w] : t;
+    __syncthreads();
+    return t;
+}
+
+// Block-wide exclusive prefix sum in thread order; `total` receives the sum.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_sum(T v, T *s_tmp, T &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        T o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_tmp[wave] = inc;
+    __syncthreads();
+    T before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < (int)kWaves; ++w) {
+        if (w < wave) before += s_tmp[w];
+        all += s_tmp[w];
+    }
+    __syncthreads();
+    total = all;
+    return before + inc - v;
+}
+
+// Block-wide exclusive prefix max in thread order (identity `lowest`).
+__device__ __forceinline__ int block_exclusive_max(int v, int lowest, int *s_tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc = o > inc ? o : inc;
+    }
+    int excl = __shfl_up(inc, 1, 64);
+    if (lane == 0) excl = lowest;
+    if (lane == 63) s_tmp[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) excl = s_tmp[w] > excl ? s_tmp[w] : excl;
+    __syncthreads();
+    return excl;
+}
+
+__device__ __forceinline__ uint32_t bit_length(uint32_t v) { return v ? 32u - __clz(v) : 0u; }
+
+// OR `width` (<= 16) bits of `value` into an LDS bit stream at `bitpos`.
+__device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t bitpos, uint32_t value,
+                                            uint32_t width) {
+    if (value == 0) return;
+    const uint32_t d = bitpos >> 5, sh = bitpos & 31;
+    atomicOr(&s[d], value << sh);
+    if (sh + width > 32) atomicOr(&s[d + 1], value >> (32 - sh));
+}
+
+// Read `width` (<= 32) bits at `bitpos` of an LDS bit stream.
+__device__ __forceinline__ uint32_t lds_get_bits(const uint32_t *s, uint32_t bitpos,
+                                                 uint32_t width) {
+    const uint32_t d = bitpos >> 5, sh = bitpos & 31;
+    const uint64_t v = (uint64_t)s[d] | ((uint64_t)s[d + 1] << 32);
+    const uint64_t mask = (width >= 32) ? 0xFFFFFFFFull : ((1ull << width) - 1);
+    return (uint32_t)((v >> sh) & mask);
+}
+
+// Element s (0..7) of a 16-byte chunk held as uint4.
+__device__ __forceinline__ uint32_t chunk_elem(const uint4 &v, int s) {
+    uint32_t w = (s < 2) ? v.x : (s < 4) ? v.y : (s < 6) ? v.z : v.w;
+    return (s & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Load 8 bf16 patterns at p, of which the first `valid` (<= 8) exist.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t *p, uint32_t valid) {
+    if (valid >= 8) return *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (uint32_t s = 0; s < valid; ++s) w[s >> 1] |= (uint32_t)p[s] << (16 * (s & 1));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Checksum terms of one chunk of new weights starting at element index e
+// (a multiple of 8) of which `valid` exist: words k = e/4 and e/4+1.
+__device__ __forceinline__ uint64_t chunk_checksum(const uint4 &v, uint64_t e, uint32_t valid) {
+    uint64_t acc = 0;
+    const uint64_t k = e >> 2;
+    if (valid > 0) acc += mix64(((uint64_t)v.y << 32 | v.x) ^ ((k + 1) * kGamma));
+    if (valid > 4) acc += mix64(((uint64_t)v.w << 32 | v.z) ^ ((k + 2) * kGamma));
+    return acc;
+}
+
+}  // namespace bf16d
+
+// ---- kernel launchers (defined in the .hip files) ------------------------------
+namespace bf16d {
+void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
+                      uint64_t tiles, hipStream_t stream);
+void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
+hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
+                           bf16d_result *results, hipStream_t stream);
+hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
+                             uint64_t dtiles, bf16d_result *results, hipStream_t stream);
+}  // namespace bf16d

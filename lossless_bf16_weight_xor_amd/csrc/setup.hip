@@ -1,0 +1,46 @@
+// setup.hip -- small kernels that prepare a batched call: the tile -> job map
+// (the "plan" that lets one launch cover every tensor of a checkpoint, as the
+// single-launch XOR apply of "GPU-accelerated Weight Teleportation", section
+// "A strong baseline with Blackwell-native DE", reads a CPU-prepared plan),
+// and zero fills of look-back words and per-job state.
+#include "internal.hpp"
+
+namespace bf16d {
+
+// map[t] = j with start[j] <= t < start[j+1]; optionally clears status[t]
+__global__ void map_tiles_kernel(const uint64_t *__restrict__ start, uint32_t count,
+                                 uint32_t *__restrict__ map, uint64_t *__restrict__ status,
+                                 uint64_t tiles) {
+    for (uint64_t t = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; t < tiles;
+         t += (uint64_t)gridDim.x * blockDim.x) {
+        uint32_t lo = 0, hi = count;   // invariant: start[lo] <= t < start[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (start[mid] <= t) lo = mid; else hi = mid;
+        }
+        map[t] = lo;
+        if (status) status[t] = 0;
+    }
+}
+
+__global__ void zero_words_kernel(uint32_t *__restrict__ p, uint64_t words) {
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+static uint32_t grid_for(uint64_t items) {
+    const uint64_t g = (items + kThreads - 1) / kThreads;
+    return (uint32_t)(g < 4096 ? (g ? g : 1) : 4096);
+}
+
+void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
+                      uint64_t tiles, hipStream_t stream) {
+    map_tiles_kernel<<<grid_for(tiles), kThreads, 0, stream>>>(start, count, map, status, tiles);
+}
+
+void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream) {
+    zero_words_kernel<<<grid_for(words), kThreads, 0, stream>>>(p, words);
+}
+
+}  // namespace bf16d

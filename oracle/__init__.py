@@ -117,9 +117,7 @@ def decompress_inplace(weights: np.ndarray, payload, checksum_value: int) -> int
     if weights.dtype != np.uint16 or not weights.flags["C_CONTIGUOUS"]:
         raise TypeError("weights must be a C-contiguous uint16 array")
     pay = np.ascontiguousarray(payload, dtype=np.uint8).reshape(-1)
-    n_bytes = pay.size
-    if n_bytes == 0:
-        pay = np.zeros(1, np.uint8)  # a valid pointer; the length passed stays 0
+    ptr = pay.ctypes.data if pay.size else None
     return int(_load().bf16d_ref_decompress(weights.ctypes.data, weights.size,
-                                            pay.ctypes.data, n_bytes,
+                                            ptr, pay.size,
                                             checksum_value & 0xFFFFFFFFFFFFFFFF))

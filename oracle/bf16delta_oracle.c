@@ -379,7 +379,7 @@ static uint64_t apply_pass(uint16_t *weights, uint64_t n, const uint8_t *payload
 
 int bf16d_ref_decompress(uint16_t *weights, uint64_t n, const uint8_t *payload,
                          uint64_t payload_bytes, uint64_t checksum) {
-    if (payload == NULL || (n > 0 && weights == NULL)) return REF_EINVAL;
+    if ((payload == NULL && payload_bytes > 0) || (n > 0 && weights == NULL)) return REF_EINVAL;
 
     /* header */
     if (payload_bytes < HEADER_BYTES) return REF_EFORMAT;

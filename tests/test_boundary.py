@@ -1,0 +1,105 @@
+"""CPU checks of the C-ABI library.
+
+These tests load libbf16delta and check that it exports every function that
+include/bf16delta.h declares.  They also exercise the entry points that run
+on the host only.  Nothing here launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bf16delta.h")
+
+
+@pytest.fixture(scope="module")
+def native():
+    from lossless_bf16_weight_xor_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _native
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bf16d_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert "bf16d_compress" in names and "bf16d_decompress" in names
+    assert "bf16d_delta_compress" in names and "bf16d_delta_decompress" in names
+
+
+def test_every_declared_symbol_is_exported(native):
+    lib = ctypes.CDLL(native.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(native.EXPORTED) == set(_declared_functions())
+
+
+def test_struct_sizes_match_the_header(native):
+    assert ctypes.sizeof(native.Result) == 48
+    assert ctypes.sizeof(native.CompressJob) == 40
+    assert ctypes.sizeof(native.DecompressJob) == 40
+
+
+def test_host_only_entry_points(native):
+    lib = native.lib()
+    assert lib.bf16d_format_version() == 1
+    assert native.status_string(native.ECHECKSUM).startswith("ECHECKSUM")
+    for n in (0, 1, 7, 8191, 8192, 8193, 3 * 8192 + 5, 10 ** 7 + 3):
+        assert lib.bf16d_max_payload_bytes(n) == oracle.max_payload_bytes(n)
+    assert lib.bf16d_workspace_bytes(10 ** 9, 300) > lib.bf16d_workspace_bytes(10 ** 6, 3)
+
+
+def test_invalid_arguments_are_rejected_before_any_gpu_work(native):
+    lib = native.lib()
+    res = (native.Result * 1)()
+    ws = ctypes.create_string_buffer(1 << 16)
+    ws_ptr = (ctypes.addressof(ws) + 15) // 16 * 16
+    job = native.CompressJob(None, None, 5, None, 0)
+    # count == 0, null jobs, null results, null workspace, null src with n > 0
+    assert lib.bf16d_compress(ctypes.byref(job), 0, ws_ptr, 1 << 15, ctypes.addressof(res), None) \
+        == native.EINVAL
+    assert lib.bf16d_compress(None, 1, ws_ptr, 1 << 15, ctypes.addressof(res), None) == native.EINVAL
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr, 1 << 15, None, None) == native.EINVAL
+    assert lib.bf16d_compress(ctypes.byref(job), 1, None, 1 << 15, ctypes.addressof(res), None) \
+        == native.EINVAL
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr, 1 << 15, ctypes.addressof(res), None) \
+        == native.EINVAL
+    # misaligned src
+    job = native.CompressJob(ws_ptr + 2, ws_ptr + 64, 4, ws_ptr + 4096, 128)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, 1 << 14,
+                              ctypes.addressof(res), None) == native.EINVAL
+    # payload overlapping dst
+    job = native.CompressJob(ws_ptr, ws_ptr + 64, 16, ws_ptr + 80, 128)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, 1 << 14,
+                              ctypes.addressof(res), None) == native.EINVAL
+    # workspace too small
+    job = native.CompressJob(ws_ptr, ws_ptr + 64, 16, ws_ptr + 128, 128)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, 16,
+                              ctypes.addressof(res), None) == native.EINVAL
+    # decompress: null payload, weights overlapping payload
+    djob = native.DecompressJob(ws_ptr, 16, None, 64, 0)
+    assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, 1 << 14,
+                                ctypes.addressof(res), None) == native.EINVAL
+    djob = native.DecompressJob(ws_ptr, 64, ws_ptr + 64, 64, 0)
+    assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, 1 << 14,
+                                ctypes.addressof(res), None) == native.EINVAL
+
+
+def test_python_api_refuses_cpu_tensors(native):
+    import torch
+    from lossless_bf16_weight_xor_amd import delta_compress
+    src = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        delta_compress(src, src.clone())
+    with pytest.raises(ValueError):
+        delta_compress(src, src.clone(), compression_format="arc_v3")
