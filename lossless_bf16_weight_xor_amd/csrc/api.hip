@@ -63,14 +63,16 @@ uint64_t bf16d_max_payload_bytes(uint64_t n) {
 size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
     const uint64_t tiles = blocks_of(total_n) + count;
     const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
-    return make_layout(tiles, dtiles, count).total;
+    const size_t c = make_layout(tiles, dtiles, count, true).total;
+    const size_t d = make_layout(tiles, dtiles, count, false).total;
+    return c > d ? c : d;
 }
 
 int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
                    size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
-    std::vector<uint64_t> start(size_t(count) + 1, 0);
+    std::vector<uint64_t> start(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
     std::vector<Range> ranges;
     ranges.reserve(3 * size_t(count) + 1);
     for (uint32_t j = 0; j < count; ++j) {
@@ -80,6 +82,7 @@ int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspa
         if (J.capacity > 0 && (!J.payload || !aligned16(J.payload))) return BF16D_EINVAL;
         if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
         start[j + 1] = start[j] + blocks_of(J.n);
+        dstart[j + 1] = dstart[j] + (blocks_of(J.n) + kDescTile - 1) / kDescTile;
         ranges.push_back({reinterpret_cast<uintptr_t>(J.src),
                           reinterpret_cast<uintptr_t>(J.src) + 2 * J.n, false});
         ranges.push_back({reinterpret_cast<uintptr_t>(J.dst),
@@ -87,16 +90,16 @@ int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspa
         ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
                           reinterpret_cast<uintptr_t>(J.payload) + J.capacity, true});
     }
-    const uint64_t tiles = start[count];
+    const uint64_t tiles = start[count], dtiles = dstart[count];
     if (tiles >= kMaxTiles) return BF16D_EINVAL;
-    const Layout l = make_layout(tiles, 0, count);
+    const Layout l = make_layout(tiles, dtiles, count, true);
     if (workspace_bytes < l.total) return BF16D_EINVAL;
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + l.total, true});
     if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
 
-    // job table and block starts, laid out as in the workspace
-    std::vector<uint8_t> host(l.block_start + 8 * (size_t(count) + 1) - l.jobs, 0);
+    // job table, block starts and scan-tile starts, laid out as in the workspace
+    std::vector<uint8_t> host(l.dtile_start + 8 * (size_t(count) + 1) - l.jobs, 0);
     auto *dj = reinterpret_cast<CompressJob *>(host.data());
     for (uint32_t j = 0; j < count; ++j) {
         dj[j].src = jobs[j].src;
@@ -109,9 +112,10 @@ int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspa
         dj[j].pad = 0;
     }
     std::memcpy(host.data() + (l.block_start - l.jobs), start.data(), 8 * start.size());
+    std::memcpy(host.data() + (l.dtile_start - l.jobs), dstart.data(), 8 * dstart.size());
     int rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
-    return launch_compress(l, static_cast<uint8_t *>(workspace), count, tiles, results,
+    return launch_compress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
                            stream) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
@@ -140,7 +144,7 @@ int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *wor
     }
     const uint64_t tiles = bstart[count], dtiles = dstart[count];
     if (tiles >= kMaxTiles) return BF16D_EINVAL;
-    const Layout l = make_layout(tiles, dtiles, count);
+    const Layout l = make_layout(tiles, dtiles, count, false);
     if (workspace_bytes < l.total) return BF16D_EINVAL;
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + l.total, true});

@@ -1,246 +1,480 @@
-// compress.hip -- single-pass BF16 delta encoder for gfx950.
+// compress.hip -- BF16 delta encoder for gfx950.
 //
-// One workgroup (256 threads = 4 waves of 64) encodes one 8192-element block
-// of one job.  A batch of tensors is one grid: the tile-to-job map built by
-// the setup kernel turns a tile index into (job, block).
+// A batch of tensors ("jobs") is one sequence of kernels; a tile is one
+// 8192-element block of one job, and the tile-to-job map built by the setup
+// kernel turns a tile index into (job, block).
 //
-// Per block, in one pass over HBM (old and new are each read once, the
-// payload is written once):
-//   1. 16-byte coalesced loads of old and new; x = old XOR new.  The XOR mask
-//      of "GPU-accelerated Weight Teleportation", section "Delta update
-//      algebra", lives only in registers and is never stored.
-//   2. Classify each element: x == 0 is unchanged, (x & 0xFF80) == 0 is
-//      mantissa-only, anything else is an exponent/sign change ("Every byte
-//      counts: ARCv3 and the case for cross-region RL", section "Deep dive
-//      into ARCv3").  The checksum terms of the new weights are accumulated
-//      in the same pass.
-//   3. Per-chunk counts, an LDS scan in element order, and compaction of the
-//      changed positions into LDS.
-//   4. Largest gap -> field width; the cheaper of gap list and bitmap.
-//   5. Decoupled look-back (Merrill and Garland, "Single-pass Parallel
-//      Prefix Scan with Decoupled Look-back", 2016) over the record sizes of
-//      the job's blocks gives this record's byte offset.  The aggregate is
-//      published before packing, so the look-back rarely waits.
-//   6. The record (position | mantissa | rare segments) is built in LDS with
-//      atomic ORs, one owner per field, so the bytes do not depend on
-//      timing.  It is then stored with dword stores, plus byte stores at the
-//      two ends it may share with neighbouring records.
-// A finalize kernel then reduces the per-block statistics of each job into
-// its header, its checksum and its result.
+// Per tile the encoder:
+//   1. loads old and new with 16-byte coalesced loads and forms x = old XOR
+//      new.  This is the mask of "GPU-accelerated Weight Teleportation",
+//      section "Delta update algebra"; it lives only in registers and LDS
+//      and is never stored.
+//   2. classifies each element ("Every byte counts: ARCv3 and the case for
+//      cross-region RL", section "Deep dive into ARCv3"):
+//        x == 0                unchanged
+//        (x & 0xFF80) == 0     mantissa-only
+//        otherwise             exponent/sign change
+//      The checksum terms of the new weights are summed in the same pass.
+//   3. scans the changed/rare counts in element order with wave64 DPP
+//      scans, and finds the widest gap, which gives the gap-field width and
+//      the cheaper position encoding (gap list or bitmap).
+//   4. builds the record (position | mantissa | rare segments) in LDS with
+//      atomic ORs.  Each field has one owner, so the bytes do not depend on
+//      timing.
+//
+// Placing records needs each record's byte offset: the exclusive sum of the
+// sizes of the job's earlier records.  Computing that inside the streaming
+// pass would stall it on a cross-workgroup look-back.  So the work is split:
+//   encode   : persistent, prefetching, no inter-workgroup waits.  Reads old
+//              and new once.  Writes each record (if <= kSlot bytes) to a
+//              fixed per-tile slot in the workspace, plus its descriptor and
+//              checksum partials; larger records are listed for re-encoding.
+//   offsets  : a decoupled look-back scan (Merrill and Garland, "Single-pass
+//              Parallel Prefix Scan with Decoupled Look-back", 2016) over the
+//              record sizes of each job: the stream offsets.
+//   place    : one wave per tile copies its slot to the record's offset and
+//              writes the descriptor.
+//   reencode : for tiles whose record did not fit a slot (dense blocks),
+//              encodes again straight into the payload.
+//   finalize : one workgroup per job; header, checksum and result.
+// The slots cost 2 * (record bytes) of extra traffic, about 2% at a 2%
+// change rate.
 #include "internal.hpp"
 
 namespace bf16d {
 
-// Look-back by one wave: returns the exclusive prefix of tile `tile` over the
-// tiles [first, tile) of its job.
-__device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint64_t first) {
-    const int lane = threadIdx.x & 63;
-    uint64_t excl = 0;
-    int64_t pred = (int64_t)tile - 1;
-    for (;;) {
-        const int64_t idx = pred - lane;
-        uint64_t v = kFlagPrefix;   // below the job's first tile: an empty inclusive prefix
-        if (idx >= (int64_t)first) {
-            v = ld_acquire_agent(&status[idx]);
-            while ((v >> 62) == 0) {
-                __builtin_amdgcn_s_sleep(1);
-                v = ld_acquire_agent(&status[idx]);
-            }
+constexpr uint32_t kPosMantMax = kBlock / 8 + (7 * kBlock) / 8;   // 8192 bytes
+
+// Uniform (per-workgroup) description of one tile.
+struct TileRef {
+    const uint16_t *src, *dst;   // first element of the tile
+    uint64_t b;                  // block index within the job
+    uint32_t L;                  // elements in this block
+};
+
+__device__ __forceinline__ TileRef tile_ref(const CompressJob &job, uint64_t t) {
+    TileRef r;
+    r.b = t - job.block0;
+    const uint64_t base = r.b * kBlock;
+    const uint64_t left = job.n - base;
+    r.L = left < kBlock ? (uint32_t)left : kBlock;
+    r.src = job.src + base;
+    r.dst = job.dst + base;
+    return r;
+}
+
+__device__ __forceinline__ void load_tile(const TileRef &t, uint4 (&o)[kChunksPerThread],
+                                          uint4 (&nw)[kChunksPerThread]) {
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
+        o[i] = make_uint4(0, 0, 0, 0);
+        nw[i] = make_uint4(0, 0, 0, 0);
+        if (e0 < t.L) {
+            o[i] = load_chunk(t.src + e0, t.L - e0);
+            nw[i] = load_chunk(t.dst + e0, t.L - e0);
         }
-        const uint64_t pmask = __ballot((v >> 62) == 2);
-        const int stop = pmask ? __ffsll((unsigned long long)pmask) - 1 : 63;
-        const uint64_t mine = (lane <= stop) ? (v & kValueMask) : 0;
-        excl += wave_sum(mine);
-        if (pmask) return excl;
-        pred -= 64;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void compress_kernel(
-    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
-    uint64_t *__restrict__ status, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ desc_out, Control *__restrict__ ctrl) {
-    __shared__ uint32_t s_pre[kChunks];                 // chunk counts, then prefixes
-    __shared__ uint16_t s_pos[kBlock];                  // compacted changed positions
-    __shared__ uint32_t s_rec[kMaxRecord / 4 + 4];      // record under construction
-    __shared__ uint32_t s_tmp32[kWaves];
-    __shared__ uint64_t s_tmp64[kWaves];
-    __shared__ uint32_t s_tile;
-    __shared__ uint64_t s_excl;
+// LDS shared by the encoding steps.
+struct EncodeShared {
+    uint32_t cnt[kChunksPerThread][kWaves];    // per round and wave: changed | rare << 16
+    uint32_t last[kChunksPerThread][kWaves];   // per round and wave: last changed position + 1
+    uint32_t gmax[kWaves];
+};
 
+// Result of classifying and scanning one tile (per thread, except the
+// uniform fields c, r, w, code, pb, mb, len, desc).
+struct TileCode {
+    uint32_t M, R;           // changed / rare flags of this thread: bit 8i+s = slot s of round i
+    uint64_t Jb, Kb, Pb;     // per-round bases (16 bits per round): changed rank, rare rank,
+                             // previous changed position + 1
+    uint64_t acc;            // checksum partial of this thread
+    uint32_t c, r, w, code, pb, mb, len, desc;
+};
+
+// Per-thread results of classifying a tile, before the scans.
+struct TileFlags {
+    uint32_t M, R;                          // changed / rare flags, bit 8i+s = slot s of round i
+    uint32_t cnt[kChunksPerThread];         // changed | rare << 16 per round
+    uint32_t last[kChunksPerThread];        // last changed position + 1 per round (0 = none)
+    uint64_t acc;                           // checksum partial
+};
+
+// Steps 1-2 for one tile, in registers only: writes x to s_x (each thread
+// touches only its own chunks).  After it returns, o/nw are free.
+__device__ __forceinline__ void classify(const TileRef &t, const uint4 (&o)[kChunksPerThread],
+                                         const uint4 (&nw)[kChunksPerThread], uint16_t *s_x,
+                                         TileFlags &f) {
     const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63, wave = tid >> 6;
-
-    // dynamic tile id: every smaller id belongs to a workgroup already running
-    if (tid == 0)
-        s_tile = __hip_atomic_fetch_add(&ctrl->ticket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint64_t tile = s_tile;
-    const CompressJob job = jobs[tile_job[tile]];
-    const uint64_t b = tile - job.block0;
-    const uint64_t base = b * kBlock;
-    const uint64_t left = job.n - base;
-    const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
-
-    // 1-2: load, XOR, classify, checksum terms
-    uint4 x[kChunksPerThread];
-    uint32_t ch8[kChunksPerThread], rr8[kChunksPerThread];
+    uint32_t M = 0, R = 0;
     uint64_t acc = 0;
+    // (k+1)*G of this thread's first word: word index = tile word + 2*tid + 512*i
+    const uint64_t kg0 = ((t.b * kBlock >> 2) + 1 + 2 * tid) * kGamma;
+    constexpr uint64_t kRoundKg = (uint64_t)(2 * kThreads) * kGamma;
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
         const uint32_t q = tid + kThreads * i;
         const uint32_t e0 = 8 * q;
-        uint4 o = make_uint4(0, 0, 0, 0), nw = make_uint4(0, 0, 0, 0);
-        uint32_t valid = 0;
-        if (e0 < L) {
-            valid = L - e0 < 8 ? L - e0 : 8;
-            o = load_chunk(job.src + base + e0, valid);
-            nw = load_chunk(job.dst + base + e0, valid);
-        }
-        x[i] = make_uint4(o.x ^ nw.x, o.y ^ nw.y, o.z ^ nw.z, o.w ^ nw.w);
-        acc += chunk_checksum(nw, base + e0, valid);
-        uint32_t c8 = 0, r8 = 0;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t xs = chunk_elem(x[i], s);
-            c8 |= (xs != 0 ? 1u : 0u) << s;
-            r8 |= ((xs & kExpSign) != 0 ? 1u : 0u) << s;
-        }
-        ch8[i] = c8;
-        rr8[i] = r8;
-        s_pre[q] = __popc(c8) | (__popc(r8) << 16);
+        const uint32_t valid = e0 < t.L ? (t.L - e0 < 8 ? t.L - e0 : 8) : 0;
+        const uint4 x = make_uint4(o[i].x ^ nw[i].x, o[i].y ^ nw[i].y, o[i].z ^ nw[i].z,
+                                   o[i].w ^ nw[i].w);
+        reinterpret_cast<uint4 *>(s_x)[q] = x;
+        const uint64_t kg = kg0 + i * kRoundKg;
+        if (valid > 0) acc += mix64(((uint64_t)nw[i].y << 32 | nw[i].x) ^ kg);
+        if (valid > 4) acc += mix64(((uint64_t)nw[i].w << 32 | nw[i].z) ^ (kg + kGamma));
+        const uint32_t c8 = nonzero_halves(x), r8 = nonzero_halves(and4(x, 0xFF80FF80u));
+        M |= c8 << (8 * i);
+        R |= r8 << (8 * i);
+        f.cnt[i] = __popc(c8) | (__popc(r8) << 16);
+        f.last[i] = c8 ? e0 + 32 - __clz(c8) : 0;
     }
-    __syncthreads();
+    f.M = M;
+    f.R = R;
+    f.acc = acc;
+}
 
-    // 3: exclusive scan of (changed, rare) counts over chunks in element order
-    uint32_t total;
-    {
-        uint32_t v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = s_pre[4 * tid + k];
-        const uint32_t mine = v[0] + v[1] + v[2] + v[3];
-        uint32_t excl = block_exclusive_sum(mine, s_tmp32, total);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            s_pre[4 * tid + k] = excl;
-            excl += v[k];
-        }
-    }
-    __syncthreads();
-    const uint32_t c = total & 0xFFFFu;
-    const uint32_t r = total >> 16;
-
-    uint32_t pre[kChunksPerThread];
+// Step 3: scans in element order (round i, then thread, then slot), the
+// widest gap and the record layout.  Contains two barriers.
+__device__ __forceinline__ void scan(const TileRef &t, const TileFlags &f, EncodeShared &sh,
+                                     TileCode &out) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t M = f.M;
+    const uint32_t(&cnt)[kChunksPerThread] = f.cnt;
+    const uint32_t(&last)[kChunksPerThread] = f.last;
+    uint32_t inc_cnt[kChunksPerThread], inc_last[kChunksPerThread];
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-        const uint32_t q = tid + kThreads * i;
-        pre[i] = s_pre[q];
-        uint32_t bits = ch8[i], j = pre[i] & 0xFFFFu;
-        while (bits) {
-            s_pos[j++] = (uint16_t)(8 * q + __ffs(bits) - 1);
-            bits &= bits - 1;
+        inc_cnt[i] = wave_incl_add(cnt[i]);
+        inc_last[i] = wave_incl_max(last[i]);
+        const uint32_t tot = lane63(inc_cnt[i]), mx = lane63(inc_last[i]);
+        if (lane == 0) {
+            sh.cnt[i][wave] = tot;
+            sh.last[i][wave] = mx;
         }
     }
     __syncthreads();
-
-    // 4: widest gap -> field width -> cheaper position encoding
-    uint32_t maxgap = 0;
-    for (uint32_t j = tid; j < c; j += kThreads) {
-        const uint32_t g = j ? (uint32_t)s_pos[j] - s_pos[j - 1] - 1 : s_pos[0];
-        maxgap = g > maxgap ? g : maxgap;
+    uint64_t Jb = 0, Kb = 0, Pb = 0;
+    uint32_t run = 0, runmax = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        uint32_t before = run, bmax = runmax;
+#pragma unroll
+        for (uint32_t w = 0; w < kWaves; ++w) {
+            const uint32_t v = sh.cnt[i][w], m = sh.last[i][w];
+            if (w < wave) {
+                before += v;
+                bmax = umax32(bmax, m);
+            }
+            run += v;
+            runmax = umax32(runmax, m);
+        }
+        const uint32_t ex = before + inc_cnt[i] - cnt[i];
+        Jb |= (uint64_t)(ex & 0xFFFFu) << (16 * i);
+        Kb |= (uint64_t)(ex >> 16) << (16 * i);
+        Pb |= (uint64_t)umax32(bmax, wave_shr1(inc_last[i])) << (16 * i);
     }
-    maxgap = block_max(maxgap, s_tmp32);
-    const uint32_t w = bit_length(maxgap);
-    const uint32_t delta_bytes = (c * w + 7) / 8;
-    const uint32_t bitmap_bytes = (L + 7) / 8;
-    const uint32_t code = bitmap_bytes < delta_bytes ? kCodeBitmap : w;
-    const uint32_t pb = code == kCodeBitmap ? bitmap_bytes : delta_bytes;
-    const uint32_t mb = (7 * c + 7) / 8;
-    const uint32_t len = pb + mb + 2 * r;
-    const uint32_t desc = c | (r << 14) | (code << 28);
+    const uint32_t c = run & 0xFFFFu, r = run >> 16;
 
-    // 5a: publish this tile's aggregate (or, for a job's first tile, its prefix)
-    if (tid == 0) st_agent(&status[tile], (b == 0 ? kFlagPrefix : kFlagAggregate) | len);
-
-    // 6a: build the record in LDS
-    const uint32_t rec_words = (len + 3) / 4 + 1;
-    for (uint32_t u = tid; u < rec_words; u += kThreads) s_rec[u] = 0;
+    // widest gap -> field width -> the cheaper position encoding
+    uint32_t maxgap = 0;
+    for (uint32_t bits = M; bits; bits &= bits - 1) {
+        const uint32_t idx = __ffs(bits) - 1, i = idx >> 3, s = idx & 7;
+        const uint32_t below = (M >> (8 * i)) & ((1u << s) - 1);
+        const uint32_t q = tid + kThreads * i;
+        const uint32_t p1 =
+            below ? 8 * q + 32 - __clz(below) : (uint32_t)(Pb >> (16 * i)) & 0xFFFFu;
+        maxgap = umax32(maxgap, 8 * q + s - p1);
+    }
+    maxgap = lane63(wave_incl_max(maxgap));
+    if (lane == 0) sh.gmax[wave] = maxgap;
     __syncthreads();
-    if (code == kCodeBitmap) {
+    maxgap = umax32(umax32(sh.gmax[0], sh.gmax[1]), umax32(sh.gmax[2], sh.gmax[3]));
+
+    out.M = M;
+    out.R = f.R;
+    out.Jb = Jb;
+    out.Kb = Kb;
+    out.Pb = Pb;
+    out.acc = f.acc;
+    out.c = c;
+    out.r = r;
+    out.w = bit_length(maxgap);
+    const uint32_t delta_bytes = (c * out.w + 7) / 8;
+    const uint32_t bitmap_bytes = (t.L + 7) / 8;
+    out.code = bitmap_bytes < delta_bytes ? kCodeBitmap : out.w;
+    out.pb = out.code == kCodeBitmap ? bitmap_bytes : delta_bytes;
+    out.mb = (7 * c + 7) / 8;
+    out.len = out.pb + out.mb + 2 * r;
+    out.desc = c | (r << 14) | (out.code << 28);
+}
+
+// Step 4: OR this thread's fields into a zeroed LDS record.  The rare words
+// go in too when kWithRare; otherwise the caller stores them directly.
+template <bool kWithRare>
+__device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
+                                          const TileCode &k) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t mant_bit = 8 * k.pb, rare_bit = 8 * (k.pb + k.mb);
+    if (k.code == kCodeBitmap) {
 #pragma unroll
         for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-            const uint32_t q = tid + kThreads * i;
-            if (ch8[i]) atomicOr(&s_rec[q >> 2], ch8[i] << (8 * (q & 3)));
-        }
-    } else if (w > 0) {
-        for (uint32_t j = tid; j < c; j += kThreads) {
-            const uint32_t g = j ? (uint32_t)s_pos[j] - s_pos[j - 1] - 1 : s_pos[0];
-            lds_or_bits(s_rec, j * w, g, w);
+            const uint32_t q = tid + kThreads * i, c8 = (k.M >> (8 * i)) & 0xFFu;
+            if (c8) atomicOr(&s_rec[q >> 2], c8 << (8 * (q & 3)));
         }
     }
-    const uint32_t mant_bit = 8 * pb, rare_bit = 8 * (pb + mb);
-#pragma unroll
-    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-        uint32_t bits = ch8[i];
-        uint32_t j = pre[i] & 0xFFFFu, k = pre[i] >> 16;
-        while (bits) {
-            const int s = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const uint32_t xs = chunk_elem(x[i], s);
-            if (xs & kExpSign) {
-                lds_or_bits(s_rec, rare_bit + 16 * k, xs, 16);
-                ++k;
-            } else {
-                lds_or_bits(s_rec, mant_bit + 7 * j, xs & kMant, 7);
-            }
-            ++j;
+    for (uint32_t bits = k.M; bits; bits &= bits - 1) {
+        const uint32_t idx = __ffs(bits) - 1, i = idx >> 3, s = idx & 7;
+        const uint32_t below = (k.M >> (8 * i)) & ((1u << s) - 1);
+        const uint32_t q = tid + kThreads * i;
+        const uint32_t j = ((uint32_t)(k.Jb >> (16 * i)) & 0xFFFFu) + __popc(below);
+        if (k.code != kCodeBitmap) {
+            const uint32_t p1 = below ? 8 * q + 32 - __clz(below)
+                                      : (uint32_t)(k.Pb >> (16 * i)) & 0xFFFFu;
+            lds_or_bits(s_rec, j * k.w, 8 * q + s - p1, k.w);
+        }
+        const uint32_t xs = s_x[8 * q + s];
+        if (!(xs & kExpSign)) {
+            lds_or_bits(s_rec, mant_bit + 7 * j, xs & kMant, 7);
+        } else if (kWithRare) {
+            const uint32_t kk = ((uint32_t)(k.Kb >> (16 * i)) & 0xFFFFu) +
+                                __popc((k.R >> (8 * i)) & ((1u << s) - 1));
+            lds_or_bits(s_rec, rare_bit + 16 * kk, xs, 16);
         }
     }
+}
 
-    // 5b: look back for the record's offset within the job's data region
+// ------------------------------------------------------------------ encode ---
+// Persistent: workgroup g encodes tiles g, g + G, g + 2G, ... and keeps the
+// next tile's loads in flight while it encodes the current one.
+__global__ __launch_bounds__(kThreads) void encode_kernel(
+    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
+    uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out, uint64_t *__restrict__ partial,
+    uint32_t *__restrict__ overflow, Control *__restrict__ ctrl, uint64_t tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
+    __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];   // kept zero
+    __shared__ EncodeShared sh;
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (uint32_t u = tid; u < kSlot / 4 + 4; u += kThreads) s_rec[u] = 0;
+    uint64_t t = blockIdx.x;
+    if (t >= tiles) return;
+    uint4 o[kChunksPerThread], nw[kChunksPerThread];
+    load_tile(tile_ref(jobs[tile_job[t]], t), o, nw);
+    __syncthreads();   // s_rec cleared
+
+    while (true) {
+        const TileRef tr = tile_ref(jobs[tile_job[t]], t);
+        TileFlags f;
+        classify(tr, o, nw, s_x, f);
+        // o/nw are free: the next tile's loads go out before the scans
+        const uint64_t next = t + gridDim.x;
+        if (next < tiles) load_tile(tile_ref(jobs[tile_job[next]], next), o, nw);
+        TileCode k;
+        scan(tr, f, sh, k);
+
+        const bool fits = k.len <= kSlot;
+        if (fits) or_fields<true>(s_rec, s_x, k);
+        const uint64_t acc = wave_sum(k.acc);
+        __syncthreads();
+
+        if (fits) {
+            uint4 *slot = reinterpret_cast<uint4 *>(slots + t * kSlot);
+            uint4 *rec = reinterpret_cast<uint4 *>(s_rec);
+            for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) {
+                slot[u] = rec[u];
+                rec[u] = make_uint4(0, 0, 0, 0);   // only this thread touches dwords 4u..4u+3
+            }
+        } else if (tid == 0) {
+            overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
+        }
+        if (lane == 0) partial[kWaves * t + wave] = acc;
+        if (tid == 0) desc_out[t] = k.desc;
+
+        if (next >= tiles) break;
+        t = next;
+    }
+}
+
+// ----------------------------------------------------------------- offsets ---
+// Record offsets within each job: exclusive sum of record sizes over the
+// job's tiles, by tiles of kDescTile descriptors with a decoupled look-back.
+__global__ __launch_bounds__(kThreads) void record_offsets_kernel(
+    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
+    const uint64_t *__restrict__ dstart, const uint32_t *__restrict__ desc,
+    uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets, Control *__restrict__ ctrl) {
+    __shared__ uint32_t s_tmp[kWaves];
+    __shared__ uint32_t s_dt;
+    __shared__ uint64_t s_excl;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0)
+        s_dt = __hip_atomic_fetch_add(&ctrl->dticket, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint64_t dt = s_dt;
+    const uint32_t j = dtile_job[dt];
+    const CompressJob job = jobs[j];
+    const uint64_t first = dstart[j];
+    const uint64_t ld = dt - first;
+
+    uint32_t lens[kDescPerThread];
+    uint32_t mine = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kDescPerThread; ++k) {
+        const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
+        lens[k] = 0;
+        if (b >= job.nb) continue;
+        const uint32_t d = desc[job.block0 + b];
+        const uint64_t left = job.n - b * kBlock;
+        const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
+        const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
+        const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
+        lens[k] = pb + (7 * c + 7) / 8 + 2 * r;
+        mine += lens[k];
+    }
+    uint32_t total;
+    uint32_t excl = block_exclusive_sum(mine, s_tmp, total);
+    if (tid == 0) st_agent(&dstatus[dt], (ld == 0 ? kFlagPrefix : kFlagAggregate) | total);
     if (wave == 0) {
-        const uint64_t excl = (b == 0) ? 0 : look_back(status, tile, job.block0);
+        const uint64_t e = (ld == 0) ? 0 : look_back(dstatus, dt, first);
         if (lane == 0) {
-            if (b != 0) st_agent(&status[tile], kFlagPrefix | (excl + len));
-            s_excl = excl;
+            if (ld != 0) st_agent(&dstatus[dt], kFlagPrefix | (e + total));
+            s_excl = e;
         }
     }
     __syncthreads();
+    uint64_t off = s_excl + excl;
+#pragma unroll
+    for (uint32_t k = 0; k < kDescPerThread; ++k) {
+        const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
+        if (b < job.nb) offsets[job.block0 + b] = off;
+        off += lens[k];
+    }
+}
 
-    // 6b: store descriptor and record, never at or beyond capacity
+// ------------------------------------------------------------------- place ---
+// One wave per tile: descriptor into the table, slot into the data region.
+// Every byte of a record belongs to one tile, and stores never reach
+// `capacity`; the dwords a record shares with its neighbours are written
+// byte by byte.
+__global__ __launch_bounds__(kThreads) void place_kernel(
+    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
+    const uint8_t *__restrict__ slots, const uint32_t *__restrict__ desc,
+    const uint64_t *__restrict__ offsets, uint64_t tiles) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t t = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (t >= tiles) return;
+    const CompressJob job = jobs[tile_job[t]];
+    const uint64_t b = t - job.block0;
+    const uint64_t left = job.n - b * kBlock;
+    const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
+    const uint32_t d = desc[t];
+    const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
+    const uint32_t len = (code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8) +
+                         (7 * c + 7) / 8 + 2 * r;
     uint8_t *const pay = job.payload;
     const uint64_t cap = job.capacity;
-    if (tid == 0) {
-        const uint64_t at = kHeader + 4 * b;
-        if (at + 4 <= cap) *reinterpret_cast<uint32_t *>(pay + at) = desc;
-        desc_out[tile] = desc;
-    }
-    const uint64_t D = kHeader + 4 * job.nb + s_excl;   // record start in the payload
+    if (lane == 0 && kHeader + 4 * b + 4 <= cap)
+        *reinterpret_cast<uint32_t *>(pay + kHeader + 4 * b) = d;
+    if (len > kSlot || len == 0) return;   // re-encoded elsewhere / nothing to copy
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + t * kSlot);
+    const uint64_t D = kHeader + 4 * job.nb + offsets[t];
     const uint32_t sh = (uint32_t)(D & 3);
     const uint64_t a0 = D - sh;
     const uint32_t words = (sh + len + 3) / 4;
-    for (uint32_t u = tid; u < words; u += kThreads) {
-        const uint32_t hi = s_rec[u];
-        const uint32_t lo = u ? s_rec[u - 1] : 0u;
+    const uint32_t src_words = (len + 3) / 4;
+    for (uint32_t u = lane; u < words; u += 64) {
+        const uint32_t hi = u < src_words ? src[u] : 0u;
+        const uint32_t lo = (u && u - 1 < src_words) ? src[u - 1] : 0u;
         const uint32_t v = sh ? ((hi << (8 * sh)) | (lo >> (32 - 8 * sh))) : hi;
         const uint64_t A = a0 + 4ull * u;
         if (A >= D && A + 4 <= D + len && A + 4 <= cap) {
             *reinterpret_cast<uint32_t *>(pay + A) = v;
         } else {
 #pragma unroll
-            for (uint32_t t = 0; t < 4; ++t) {
-                const uint64_t at = A + t;
-                if (at >= D && at < D + len && at < cap) pay[at] = (uint8_t)(v >> (8 * t));
+            for (uint32_t k = 0; k < 4; ++k) {
+                const uint64_t at = A + k;
+                if (at >= D && at < D + len && at < cap) pay[at] = (uint8_t)(v >> (8 * k));
             }
         }
     }
-
-    // per-tile checksum partial sum (mod 2^64)
-    acc = block_sum(acc, s_tmp64);
-    if (tid == 0) partial[tile] = acc;
 }
 
+// ---------------------------------------------------------------- reencode ---
+// Tiles whose record exceeded a slot, encoded again straight into the
+// payload now that their offsets are known.  The position and mantissa
+// segments are built in LDS (<= 8192 bytes); the rare words, whole 16-bit
+// words on byte boundaries, are stored directly.
+__global__ __launch_bounds__(kThreads) void reencode_kernel(
+    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
+    const uint32_t *__restrict__ overflow, const uint64_t *__restrict__ offsets,
+    const Control *__restrict__ ctrl) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
+    __shared__ uint32_t s_rec[kPosMantMax / 4 + 4];
+    __shared__ EncodeShared sh;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t count = ctrl->overflow_count;
+    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+        const uint64_t t = overflow[i];
+        const CompressJob job = jobs[tile_job[t]];
+        const TileRef tr = tile_ref(job, t);
+        uint4 o[kChunksPerThread], nw[kChunksPerThread];
+        load_tile(tr, o, nw);
+        for (uint32_t u = tid; u < kPosMantMax / 4 + 4; u += kThreads) s_rec[u] = 0;
+        TileFlags f;
+        classify(tr, o, nw, s_x, f);
+        TileCode k;
+        scan(tr, f, sh, k);   // its barriers also order the clearing of s_rec
+        or_fields<false>(s_rec, s_x, k);
+        __syncthreads();
+
+        uint8_t *const pay = job.payload;
+        const uint64_t cap = job.capacity;
+        const uint64_t D = kHeader + 4 * job.nb + offsets[t];
+        const uint32_t pm = k.pb + k.mb;
+        const uint32_t sh4 = (uint32_t)(D & 3);
+        const uint64_t a0 = D - sh4;
+        const uint32_t words = (sh4 + pm + 3) / 4;
+        for (uint32_t u = tid; u < words; u += kThreads) {
+            const uint32_t hi = s_rec[u];
+            const uint32_t lo = u ? s_rec[u - 1] : 0u;
+            const uint32_t v = sh4 ? ((hi << (8 * sh4)) | (lo >> (32 - 8 * sh4))) : hi;
+            const uint64_t A = a0 + 4ull * u;
+            if (A >= D && A + 4 <= D + pm && A + 4 <= cap) {
+                *reinterpret_cast<uint32_t *>(pay + A) = v;
+            } else {
+#pragma unroll
+                for (uint32_t q = 0; q < 4; ++q) {
+                    const uint64_t at = A + q;
+                    if (at >= D && at < D + pm && at < cap) pay[at] = (uint8_t)(v >> (8 * q));
+                }
+            }
+        }
+        const uint64_t rare0 = D + pm;
+        for (uint32_t bits = k.R; bits; bits &= bits - 1) {
+            const uint32_t idx = __ffs(bits) - 1, ii = idx >> 3, s = idx & 7;
+            const uint32_t q = tid + kThreads * ii;
+            const uint32_t kk = ((uint32_t)(k.Kb >> (16 * ii)) & 0xFFFFu) +
+                                __popc((k.R >> (8 * ii)) & ((1u << s) - 1));
+            const uint32_t xs = s_x[8 * q + s];
+            const uint64_t at = rare0 + 2 * kk;
+            if (at + 2 <= cap) {
+                if ((at & 1) == 0) {
+                    *reinterpret_cast<uint16_t *>(pay + at) = (uint16_t)xs;
+                } else {
+                    pay[at] = (uint8_t)xs;
+                    pay[at + 1] = (uint8_t)(xs >> 8);
+                }
+            } else if (at < cap) {
+                pay[at] = (uint8_t)xs;
+            }
+        }
+        __syncthreads();   // s_x and s_rec are reused by the next tile
+    }
+}
+
+// ---------------------------------------------------------------- finalize ---
 // One workgroup per job: header, checksum and result.
 __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ desc,
@@ -249,11 +483,12 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     const CompressJob job = jobs[blockIdx.x];
     unsigned long long S = 0, c = 0, r = 0, pos = 0, mant = 0, nbm = 0;
     for (uint64_t b = threadIdx.x; b < job.nb; b += kThreads) {
-        const uint32_t d = desc[job.block0 + b];
+        const uint64_t t = job.block0 + b;
+        const uint32_t d = desc[t];
         const uint64_t left = job.n - b * kBlock;
         const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
         const uint32_t cb = d & 0x3FFFu, rb = (d >> 14) & 0x3FFFu, code = d >> 28;
-        S += partial[job.block0 + b];
+        for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * t + w];
         c += cb;
         r += rb;
         pos += code == kCodeBitmap ? (L + 7) / 8 : (cb * code + 7) / 8;
@@ -296,20 +531,32 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
 }
 
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                           bf16d_result *results, hipStream_t stream) {
+                           uint64_t dtiles, bf16d_result *results, hipStream_t stream) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const CompressJob *>(ws + l.jobs);
-    auto *start = reinterpret_cast<const uint64_t *>(ws + l.block_start);
+    auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
+    auto *dstart = reinterpret_cast<const uint64_t *>(ws + l.dtile_start);
     auto *map = reinterpret_cast<uint32_t *>(ws + l.tile_job);
-    auto *status = reinterpret_cast<uint64_t *>(ws + l.status);
+    auto *offsets = reinterpret_cast<uint64_t *>(ws + l.status);
     auto *partial = reinterpret_cast<uint64_t *>(ws + l.partial);
     auto *desc = reinterpret_cast<uint32_t *>(ws + l.desc);
+    auto *dmap = reinterpret_cast<uint32_t *>(ws + l.dtile_job);
+    auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
+    auto *slots = ws + l.slots;
+    auto *overflow = reinterpret_cast<uint32_t *>(ws + l.overflow);
 
     launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
     if (tiles) {
-        launch_map_tiles(start, count, map, status, tiles, stream);
-        compress_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, status, partial,
-                                                                  desc, ctrl);
+        launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
+        launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
+        encode_kernel<<<persistent_grid((const void *)encode_kernel, tiles), kThreads, 0,
+                        stream>>>(jobs, map, slots, desc, partial, overflow, ctrl, tiles);
+        record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
+            jobs, dmap, dstart, desc, dstatus, offsets, ctrl);
+        place_kernel<<<(uint32_t)((tiles + kWaves - 1) / kWaves), kThreads, 0, stream>>>(
+            jobs, map, slots, desc, offsets, tiles);
+        reencode_kernel<<<persistent_grid((const void *)reencode_kernel, tiles), kThreads, 0,
+                          stream>>>(jobs, map, overflow, offsets, ctrl);
     }
     compress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, desc, partial, results);
     return hipGetLastError();

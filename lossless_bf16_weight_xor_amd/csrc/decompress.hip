@@ -29,28 +29,6 @@
 
 namespace bf16d {
 
-__device__ uint64_t look_back_d(uint64_t *status, uint64_t tile, uint64_t first) {
-    const int lane = threadIdx.x & 63;
-    uint64_t excl = 0;
-    int64_t pred = (int64_t)tile - 1;
-    for (;;) {
-        const int64_t idx = pred - lane;
-        uint64_t v = kFlagPrefix;
-        if (idx >= (int64_t)first) {
-            v = ld_acquire_agent(&status[idx]);
-            while ((v >> 62) == 0) {
-                __builtin_amdgcn_s_sleep(1);
-                v = ld_acquire_agent(&status[idx]);
-            }
-        }
-        const uint64_t pmask = __ballot((v >> 62) == 2);
-        const int stop = pmask ? __ffsll((unsigned long long)pmask) - 1 : 63;
-        const uint64_t mine = (lane <= stop) ? (v & kValueMask) : 0;
-        excl += wave_sum(mine);
-        if (pmask) return excl;
-        pred -= 64;
-    }
-}
 
 __device__ __forceinline__ uint32_t block_length(uint64_t n, uint64_t b) {
     const uint64_t left = n - b * kBlock;
@@ -113,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
     uint32_t excl = block_exclusive_sum(mine, s_tmp32, tile_total);
     if (tid == 0) st_agent(&dstatus[dt], (ld == 0 ? kFlagPrefix : kFlagAggregate) | tile_total);
     if (wave == 0) {
-        const uint64_t e = (ld == 0) ? 0 : look_back_d(dstatus, dt, job.dtile0);
+        const uint64_t e = (ld == 0) ? 0 : look_back(dstatus, dt, job.dtile0);
         if (lane == 0) {
             if (ld != 0) st_agent(&dstatus[dt], kFlagPrefix | (e + tile_total));
             s_excl = e;
@@ -168,110 +146,199 @@ __global__ void prepare_kernel(const DecompressJob *__restrict__ jobs,
 }
 
 // -------------------------------------------------------------------- apply ---
+// Records up to kStage bytes are staged in LDS; fields beyond are read from
+// HBM (only dense blocks have larger records).
+constexpr uint32_t kStage = 6144;
+constexpr uint32_t kStageWords = kStage / 4;
+
+// Bit reader over a record: bits [0, 8*kStage - 32) of the window come from
+// LDS; later bits come from the payload in global memory.
+struct RecordBits {
+    const uint32_t *lds;        // staged dwords; window bit 0 = payload byte `a0`
+    const uint8_t *payload;
+    uint64_t a0;                // 4-aligned payload offset of the window
+    uint64_t payload_bytes;
+    uint32_t rb0;               // window bit of record bit 0
+
+    __device__ __forceinline__ uint32_t get(uint32_t bitpos, uint32_t width) const {
+        const uint32_t wb = rb0 + bitpos;
+        const uint32_t d = wb >> 5, sh = wb & 31;
+        uint64_t v;
+        if (d + 1 < kStageWords) {
+            v = (uint64_t)lds[d] | ((uint64_t)lds[d + 1] << 32);
+        } else {
+            v = 0;
+            const uint64_t at = a0 + 4ull * d;
+            for (uint32_t t = 0; t < 8; ++t)
+                if (at + t < payload_bytes) v |= (uint64_t)payload[at + t] << (8 * t);
+        }
+        const uint64_t mask = (width >= 32) ? 0xFFFFFFFFull : ((1ull << width) - 1);
+        return (uint32_t)((v >> sh) & mask);
+    }
+};
+
+// Per-tile metadata, read one tile ahead.
+struct ApplyMeta {
+    uint32_t job;
+    uint32_t desc;
+    uint64_t offset;
+};
+
 template <bool kRollback>
 __global__ __launch_bounds__(kThreads) void apply_kernel(
     const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
     const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
     uint64_t *__restrict__ partial, const Control *__restrict__ ctrl, uint64_t tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];   // dense XOR tile
-    __shared__ uint32_t s_raw[kMaxRecord / 4 + 4];                    // staged record
-    __shared__ uint32_t s_tmp32[kWaves];
-    __shared__ int s_tmpi[kWaves];
-    __shared__ unsigned long long s_tmp64[kWaves];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];   // dense XOR tile (kept zero)
+    __shared__ uint32_t s_raw[kStageWords + 4];                       // staged record
+    __shared__ uint32_t s_a[kWaves], s_b[kWaves], s_c[kWaves];
 
     if (kRollback && ctrl->any_rollback == 0) return;
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
+        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
 
-    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const uint32_t j = tile_job[tile];
-        if (kRollback ? state[j].rollback == 0 : state[j].state != kStateReady) continue;
+    // tiles of this workgroup: blockIdx.x, blockIdx.x + gridDim.x, ... of
+    // the jobs that take part (ready, or marked for rollback)
+    auto wanted = [&](uint32_t j) {
+        return kRollback ? state[j].rollback != 0 : state[j].state == kStateReady;
+    };
+    uint64_t tile = blockIdx.x;
+    uint4 o[kChunksPerThread];
+    ApplyMeta meta{};
+    auto fetch = [&](uint64_t t, ApplyMeta &m, uint4 (&old)[kChunksPerThread]) {
+        m.job = tile_job[t];
+        const DecompressJob &J = jobs[m.job];
+        const uint64_t b = t - J.block0;
+        const uint32_t L = block_length(J.n, b);
+#pragma unroll
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+            const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
+            old[i] = make_uint4(0, 0, 0, 0);
+            if (e0 < L) old[i] = load_chunk(J.weights + b * kBlock + e0, L - e0);
+        }
+        m.desc = *reinterpret_cast<const uint32_t *>(J.payload + kHeader + 4 * b);
+        m.offset = offsets[t];
+    };
+    while (tile < tiles && !wanted(tile_job[tile])) tile += gridDim.x;
+    if (tile >= tiles) return;
+    fetch(tile, meta, o);
+    __syncthreads();   // s_x cleared
+
+    while (true) {
+        const uint32_t j = meta.job;
         const DecompressJob job = jobs[j];
         const uint64_t b = tile - job.block0;
         const uint64_t base = b * kBlock;
         const uint32_t L = block_length(job.n, b);
-
-        // old weights first: their latency overlaps the decode below
-        uint4 o[kChunksPerThread];
-#pragma unroll
-        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-            const uint32_t e0 = 8 * (tid + kThreads * i);
-            o[i] = make_uint4(0, 0, 0, 0);
-            if (e0 < L) o[i] = load_chunk(job.weights + base + e0, L - e0);
-        }
-
-        const uint32_t desc = *reinterpret_cast<const uint32_t *>(job.payload + kHeader + 4 * b);
+        const uint32_t desc = meta.desc;
         const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
         const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
         const uint32_t mb = (7 * c + 7) / 8;
         const uint32_t len = pb + mb + 2 * r;
-        const uint64_t D = kHeader + 4 * job.nb + offsets[tile];
-        const uint32_t sh = (uint32_t)(D & 3);
-        const uint64_t a0 = D - sh;
-        const uint32_t nraw = (sh + len + 3) / 4;
-        for (uint32_t u = tid; u <= nraw; u += kThreads) {
-            const uint64_t A = a0 + 4ull * u;
-            uint32_t v = 0;
-            if (A + 4 <= job.payload_bytes) {
-                v = *reinterpret_cast<const uint32_t *>(job.payload + A);
-            } else {
-                for (uint32_t t = 0; t < 4; ++t)
-                    if (A + t < job.payload_bytes) v |= (uint32_t)job.payload[A + t] << (8 * t);
+        const uint64_t D = kHeader + 4 * job.nb + meta.offset;
+
+        // stage the first kStage bytes of the record window
+        RecordBits rb;
+        rb.lds = s_raw;
+        rb.payload = job.payload;
+        rb.payload_bytes = job.payload_bytes;
+        rb.rb0 = 8 * (uint32_t)(D & 3);
+        rb.a0 = D & ~3ull;
+        {
+            const uint32_t nraw = (uint32_t)((D & 3) + len + 3) / 4 + 1;
+            const uint32_t n_stage = nraw < kStageWords + 4 ? nraw : kStageWords + 4;
+            for (uint32_t u = tid; u < n_stage; u += kThreads) {
+                const uint64_t A = rb.a0 + 4ull * u;
+                uint32_t v = 0;
+                if (A + 4 <= job.payload_bytes) {
+                    v = *reinterpret_cast<const uint32_t *>(job.payload + A);
+                } else {
+                    for (uint32_t t = 0; t < 4; ++t)
+                        if (A + t < job.payload_bytes)
+                            v |= (uint32_t)job.payload[A + t] << (8 * t);
+                }
+                s_raw[u] = v;
             }
-            s_raw[u] = v;
         }
-        for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
-            reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
-        __syncthreads();
+
+        // prefetch the next wanted tile
+        uint64_t next = tile + gridDim.x;
+        while (next < tiles && !wanted(tile_job[next])) next += gridDim.x;
+        uint4 o2[kChunksPerThread];
+        ApplyMeta meta2{};
+        if (next < tiles) fetch(next, meta2, o2);
+        __syncthreads();   // barrier A: record staged
 
         // ---- decode the record into s_x, checking that it is canonical ----
-        const uint32_t rb0 = 8 * sh;                      // record bit 0 within s_raw
-        const uint32_t mant0 = rb0 + 8 * pb;              // first mantissa field
-        const uint32_t rare0 = rb0 + 8 * (pb + mb);       // first rare word
+        const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
         uint32_t bad = 0;
         if (code == kCodeBitmap) {
             // thread t owns bitmap bits [32t, 32t + 32) = elements 32t .. 32t+31
             const uint32_t lo = 32 * tid, seg_end = 8 * pb;
             uint32_t word = 0;
             if (lo < seg_end) {
-                word = lds_get_bits(s_raw, rb0 + lo, 32);
+                word = rb.get(lo, 32);
                 if (lo + 32 > seg_end) word &= (1u << (seg_end - lo)) - 1;
             }
             const uint32_t valid_mask =
                 lo + 32 <= L ? 0xFFFFFFFFu : (lo >= L ? 0u : (1u << (L - lo)) - 1);
             bad |= (word & ~valid_mask) != 0;               // pad bits must be zero
             word &= valid_mask;
-            uint32_t total;
-            const uint32_t rank0 = block_exclusive_sum((uint32_t)__popc(word), s_tmp32, total);
+            const uint32_t pop = __popc(word);
+            const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
+            const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
+            if (lane == 0) {
+                s_a[wave] = lane63(inc_pop);
+                s_b[wave] = lane63(inc_last);
+            }
+            __syncthreads();   // barrier B1
+            uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) {
+                    rank0 += s_a[w2];
+                    prev1 = umax32(prev1, s_b[w2]);
+                }
+                total += s_a[w2];
+            }
             bad |= total != c;
-            // the gap before each set bit -> the minimal gap-list width
-            const int my_last = word ? (int)(lo + 31 - __clz(word)) : -1;
-            int prev = block_exclusive_max(my_last, -1, s_tmpi);
+            // gaps before each set bit, and the escapes among this thread's fields
             uint32_t maxg = 0, esc = 0;
             {
-                uint32_t bits = word, jj = rank0;
+                uint32_t bits = word, jj = rank0, p1 = prev1;
                 while (bits) {
-                    const int p = (int)lo + __ffs(bits) - 1;
+                    const uint32_t p = lo + __ffs(bits) - 1;
                     bits &= bits - 1;
-                    const uint32_t g = (uint32_t)(p - prev - 1);
-                    maxg = g > maxg ? g : maxg;
-                    prev = p;
-                    esc += lds_get_bits(s_raw, mant0 + 7 * jj, 7) == 0;
+                    maxg = umax32(maxg, p - p1);
+                    p1 = p + 1;
+                    esc += rb.get(mant0 + 7 * jj, 7) == 0;
                     ++jj;
                 }
             }
-            maxg = block_max(maxg, s_tmp32);
-            bad |= !(pb < (c * bit_length(maxg) + 7) / 8);
-            uint32_t esc_total;
-            uint32_t e = block_exclusive_sum(esc, s_tmp32, esc_total);
+            const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
+            __syncthreads();   // barrier B2 (s_a / s_b reads done)
+            if (lane == 0) {
+                s_a[wave] = lane63(inc_esc);
+                s_c[wave] = wmax;
+            }
+            __syncthreads();   // barrier B3
+            uint32_t e = inc_esc - esc, esc_total = 0;
+            maxg = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) e += s_a[w2];
+                esc_total += s_a[w2];
+                maxg = umax32(maxg, s_c[w2]);
+            }
             bad |= esc_total != r;
+            bad |= !(pb < (c * bit_length(maxg) + 7) / 8);   // a bitmap only when smaller
             uint32_t bits = word, jj = rank0;
             while (bits) {
                 const uint32_t p = lo + __ffs(bits) - 1;
                 bits &= bits - 1;
-                uint32_t x = lds_get_bits(s_raw, mant0 + 7 * jj, 7);
+                uint32_t x = rb.get(mant0 + 7 * jj, 7);
                 if (x == 0) {
                     if (e < r) {
-                        x = lds_get_bits(s_raw, rare0 + 16 * e, 16);
+                        x = rb.get(rare0 + 16 * e, 16);
                         bad |= (x & kExpSign) == 0;
                     } else {
                         bad = 1;
@@ -289,28 +356,42 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(
             const uint32_t je = jb + F < c ? jb + F : c;
             uint32_t sum_g1 = 0, esc = 0, maxg = 0;
             for (uint32_t jj = jb; jj < je; ++jj) {
-                const uint32_t g = w ? lds_get_bits(s_raw, rb0 + jj * w, w) : 0;
+                const uint32_t g = w ? rb.get(jj * w, w) : 0;
                 sum_g1 += g + 1;
-                maxg = g > maxg ? g : maxg;
-                esc += lds_get_bits(s_raw, mant0 + 7 * jj, 7) == 0;
+                maxg = umax32(maxg, g);
+                esc += rb.get(mant0 + 7 * jj, 7) == 0;
             }
-            unsigned long long total;
-            const unsigned long long ex = block_exclusive_sum(
-                (unsigned long long)sum_g1 | ((unsigned long long)esc << 32), s_tmp64, total);
-            const uint32_t total_g1 = (uint32_t)total, esc_total = (uint32_t)(total >> 32);
-            bad |= (c > 0) && (total_g1 - 1 >= L);         // last position inside the block
+            const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
+            const uint32_t wmax = lane63(wave_incl_max(maxg));
+            if (lane == 0) {
+                s_a[wave] = lane63(inc_g);
+                s_b[wave] = lane63(inc_e);
+                s_c[wave] = wmax;
+            }
+            __syncthreads();   // barrier B1
+            uint32_t run = inc_g - sum_g1, e = inc_e - esc;
+            uint32_t total_g1 = 0, esc_total = 0;
+            maxg = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) {
+                    run += s_a[w2];
+                    e += s_b[w2];
+                }
+                total_g1 += s_a[w2];
+                esc_total += s_b[w2];
+                maxg = umax32(maxg, s_c[w2]);
+            }
+            bad |= (c > 0) && (total_g1 - 1 >= L);          // last position inside the block
             bad |= esc_total != r;
-            maxg = block_max(maxg, s_tmp32);
-            bad |= bit_length(maxg) != w;
-            uint32_t run = (uint32_t)ex, e = (uint32_t)(ex >> 32);
+            bad |= bit_length(maxg) != w;                    // width is minimal
             for (uint32_t jj = jb; jj < je; ++jj) {
-                const uint32_t g = w ? lds_get_bits(s_raw, rb0 + jj * w, w) : 0;
+                const uint32_t g = w ? rb.get(jj * w, w) : 0;
                 run += g + 1;
                 const uint32_t p = run - 1;
-                uint32_t x = lds_get_bits(s_raw, mant0 + 7 * jj, 7);
+                uint32_t x = rb.get(mant0 + 7 * jj, 7);
                 if (x == 0) {
                     if (e < r) {
-                        x = lds_get_bits(s_raw, rare0 + 16 * e, 16);
+                        x = rb.get(rare0 + 16 * e, 16);
                         bad |= (x & kExpSign) == 0;
                     } else {
                         bad = 1;
@@ -320,24 +401,27 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(
                 if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
             }
             if (tid == 0 && 8 * pb > c * w)                  // position padding
-                bad |= lds_get_bits(s_raw, rb0 + c * w, 8 * pb - c * w) != 0;
+                bad |= rb.get(c * w, 8 * pb - c * w) != 0;
         }
         if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
-            bad |= lds_get_bits(s_raw, mant0 + 7 * c, 8 * mb - 7 * c) != 0;
-        bad = __syncthreads_or(bad);
+            bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
+        bad = __syncthreads_or(bad);   // barrier C: s_x complete
 
-        // ---- new = old ^ tile; store only the chunks that changed ----
-        unsigned long long acc = 0;
-        if (!bad) {
+        // ---- new = old ^ tile; store only changed chunks; clear the tile ----
+        uint64_t acc = 0;
+        const uint64_t thread_kg = (uint64_t)(2 * tid) * kGamma;
+        const uint64_t tile_kg = ((base >> 2) + 1) * kGamma + thread_kg;
 #pragma unroll
-            for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-                const uint32_t q = tid + kThreads * i;
-                const uint32_t e0 = 8 * q;
-                if (e0 >= L) continue;
-                const uint32_t valid = L - e0 < 8 ? L - e0 : 8;
-                const uint4 t = reinterpret_cast<const uint4 *>(s_x)[q];
-                uint4 nw = o[i];
-                if ((t.x | t.y | t.z | t.w) != 0) {
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+            const uint32_t q = tid + kThreads * i;
+            const uint32_t e0 = 8 * q;
+            const uint32_t valid = e0 < L ? (L - e0 < 8 ? L - e0 : 8) : 0;
+            const uint4 t = reinterpret_cast<const uint4 *>(s_x)[q];
+            const bool dirty = (t.x | t.y | t.z | t.w) != 0;
+            uint4 nw = o[i];
+            if (dirty) {
+                reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
+                if (!bad) {
                     nw = make_uint4(o[i].x ^ t.x, o[i].y ^ t.y, o[i].z ^ t.z, o[i].w ^ t.w);
                     uint16_t *dstp = job.weights + base + e0;
                     if (valid == 8) {
@@ -346,17 +430,25 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(
                         for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
                     }
                 }
-                if (!kRollback) acc += chunk_checksum(nw, base + e0, valid);
+            }
+            if (!kRollback) {
+                const uint64_t kg = tile_kg + (uint64_t)i * ((uint64_t)(2 * kThreads) * kGamma);
+                if (valid > 0) acc += mix64(((uint64_t)nw.y << 32 | nw.x) ^ kg);
+                if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + kGamma));
             }
         }
         if (!kRollback) {
-            acc = block_sum(acc, s_tmp64);
-            if (tid == 0) {
-                partial[tile] = acc;
-                if (bad) atomicOr(&state[j].block_bad, 1u);
-            }
+            acc = wave_sum(acc);
+            if (lane == 0) partial[kWaves * tile + wave] = acc;
+            if (tid == 0 && bad) atomicOr(&state[j].block_bad, 1u);
         }
-        __syncthreads();   // LDS is reused by the next tile of this workgroup
+
+        if (next >= tiles) break;
+        tile = next;
+        meta = meta2;
+#pragma unroll
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) o[i] = o2[i];
+        __syncthreads();   // barrier D: s_x cleared, s_raw and s_a..s_c free again
     }
 }
 
@@ -372,7 +464,8 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
     const bool ready = st->state == kStateReady;
     unsigned long long S = 0;
     if (ready)
-        for (uint64_t b = threadIdx.x; b < job.nb; b += kThreads) S += partial[job.block0 + b];
+        for (uint64_t b = threadIdx.x; b < job.nb; b += kThreads)
+            for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * (job.block0 + b) + w];
     S = block_sum(S, s_tmp);
     if (threadIdx.x != 0) return;
     bf16d_result res;
@@ -423,15 +516,14 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
                                                                                count);
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
-        apply_kernel<false><<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, state, map, offsets,
-                                                                      partial, ctrl, tiles);
+        apply_kernel<false><<<persistent_grid((const void *)apply_kernel<false>, tiles), kThreads,
+                              0, stream>>>(jobs, state, map, offsets, partial, ctrl, tiles);
     }
     decompress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, state, partial, ctrl,
                                                                results);
     if (tiles) {
-        const uint32_t grid = (uint32_t)(tiles < 2048 ? tiles : 2048);
-        apply_kernel<true><<<grid, kThreads, 0, stream>>>(jobs, state, map, offsets, partial,
-                                                          ctrl, tiles);
+        apply_kernel<true><<<persistent_grid((const void *)apply_kernel<true>, tiles), kThreads, 0,
+                             stream>>>(jobs, state, map, offsets, partial, ctrl, tiles);
     }
     return hipGetLastError();
 }

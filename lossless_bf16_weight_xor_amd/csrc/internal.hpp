@@ -31,6 +31,9 @@ constexpr uint32_t kChunks = kBlock / 8;                 // 16-byte chunks per b
 constexpr uint32_t kChunksPerThread = kChunks / kThreads;   // 4
 constexpr uint32_t kDescPerThread = 8;
 constexpr uint32_t kDescTile = kThreads * kDescPerThread;   // descriptors per scan tile
+// compress: workspace slot per tile for its record; larger records are
+// encoded a second time straight into the payload
+constexpr uint32_t kSlot = 2048;
 
 // ---- decoupled look-back status words ---------------------------------------
 // bits 62..63: 0 = not yet published, 1 = tile aggregate, 2 = inclusive prefix
@@ -73,21 +76,22 @@ struct alignas(64) DecompressState {
 };
 
 struct alignas(64) Control {
-    uint32_t ticket;       // dynamic tile ids for the compress look-back
-    uint32_t dticket;      // dynamic tile ids for the descriptor-scan look-back
-    uint32_t any_rollback;
-    uint32_t pad[13];
+    uint32_t ticket;          // (unused) dynamic tile ids
+    uint32_t dticket;         // dynamic tile ids for the descriptor-scan look-back
+    uint32_t any_rollback;    // decompress: some job must be rolled back
+    uint32_t overflow_count;  // compress: tiles whose record exceeded a slot
+    uint32_t pad[12];
 };
 
 // Workspace layout, computed identically by every entry point.
 struct Layout {
     size_t control, jobs, block_start, dtile_start, tile_job, status, partial, desc,
-        dtile_job, dstatus, state, total;
+        dtile_job, dstatus, state, slots, overflow, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count) {
+inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool compress) {
     Layout l{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -102,12 +106,14 @@ inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count) {
     l.block_start = take(8 * (size_t(count) + 1));
     l.dtile_start = take(8 * (size_t(count) + 1));
     l.tile_job = take(4 * tiles);
-    l.status = take(8 * tiles);     // compress: look-back words; decompress: record offsets
-    l.partial = take(8 * tiles);    // per-tile checksum partial sums
+    l.status = take(8 * tiles);     // record offsets
+    l.partial = take(8 * kWaves * tiles);   // per-wave checksum partial sums of each tile
     l.desc = take(4 * tiles);       // compress: descriptor copies
     l.dtile_job = take(4 * dtiles);
     l.dstatus = take(8 * dtiles);
     l.state = take(sizeof(DecompressState) * size_t(count));
+    l.slots = take(compress ? size_t(kSlot) * tiles : 0);     // compress: record slots
+    l.overflow = take(compress ? 4 * tiles : 0);              // compress: overflowing tiles
     l.total = off;
     return l;
 }
@@ -215,6 +221,95 @@ __device__ __forceinline__ int block_exclusive_max(int v, int lowest, int *s_tmp
     return excl;
 }
 
+// ---- wave64 DPP scans (GFX9 row_shr / row_bcast / wave_shr) -------------------
+// Inclusive scans over the 64 lanes of a wave in 6 DPP-fused ALU ops.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+    // lanes without a source (or outside row_mask) read 0, the identity of add and unsigned max
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+    v += dpp_src<0x111>(v);          // row_shr:1
+    v += dpp_src<0x112>(v);          // row_shr:2
+    v += dpp_src<0x114>(v);          // row_shr:4
+    v += dpp_src<0x118>(v);          // row_shr:8
+    v += dpp_src<0x142, 0xa>(v);     // row_bcast:15 into rows 1 and 3
+    v += dpp_src<0x143, 0xc>(v);     // row_bcast:31 into rows 2 and 3
+    return v;
+}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+    v = umax32(v, dpp_src<0x111>(v));
+    v = umax32(v, dpp_src<0x112>(v));
+    v = umax32(v, dpp_src<0x114>(v));
+    v = umax32(v, dpp_src<0x118>(v));
+    v = umax32(v, dpp_src<0x142, 0xa>(v));
+    v = umax32(v, dpp_src<0x143, 0xc>(v));
+    return v;
+}
+// value of the previous lane (0 for lane 0)
+__device__ __forceinline__ uint32_t wave_shr1(uint32_t v) { return dpp_src<0x138>(v); }
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Decoupled look-back by one wave over the status words of tiles
+// [first, tile): returns the sum of their values (the exclusive prefix of
+// `tile`).  Each lane reads kLookDepth words per round, so one round trip
+// covers 64 * kLookDepth predecessors.  A tile publishes its aggregate
+// before it looks back, and a workgroup only waits on tiles claimed before
+// its own, whose holders are running; so every wait ends.  Tiles below
+// `first` read as an empty inclusive prefix.
+constexpr int kLookDepth = 4;
+
+__device__ __forceinline__ uint64_t look_back(uint64_t *status, uint64_t tile, uint64_t first) {
+    const int lane = threadIdx.x & 63;
+    uint64_t excl = 0;
+    int64_t pred = (int64_t)tile - 1;
+    for (;;) {
+        uint64_t v[kLookDepth];
+#pragma unroll
+        for (int k = 0; k < kLookDepth; ++k) {
+            const int64_t idx = pred - lane - 64 * k;   // distance 1 + lane + 64k
+            v[k] = idx >= (int64_t)first ? ld_acquire_agent(&status[idx]) : kFlagPrefix;
+        }
+        // wait only for the entries nearer than the nearest inclusive prefix
+        // seen so far; re-pick that prefix after every reload
+        int stop_k, stop_lane;
+        for (;;) {
+            stop_k = kLookDepth;
+            stop_lane = 63;
+#pragma unroll
+            for (int k = kLookDepth - 1; k >= 0; --k) {
+                const uint64_t m = __ballot((v[k] >> 62) == 2);
+                if (m) {
+                    stop_k = k;
+                    stop_lane = __ffsll((unsigned long long)m) - 1;
+                }
+            }
+            bool pending = false;
+#pragma unroll
+            for (int k = 0; k < kLookDepth; ++k)
+                pending |= (k < stop_k || (k == stop_k && lane < stop_lane)) && (v[k] >> 62) == 0;
+            if (__ballot(pending) == 0) break;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int k = 0; k < kLookDepth; ++k) {
+                const int64_t idx = pred - lane - 64 * k;
+                if ((k < stop_k || (k == stop_k && lane < stop_lane)) && (v[k] >> 62) == 0)
+                    v[k] = ld_acquire_agent(&status[idx]);
+            }
+        }
+        uint64_t mine = 0;
+#pragma unroll
+        for (int k = 0; k < kLookDepth; ++k)
+            if (k < stop_k || (k == stop_k && lane <= stop_lane)) mine += v[k] & kValueMask;
+        excl += wave_sum(mine);
+        if (stop_k < kLookDepth) return excl;
+        pred -= 64 * kLookDepth;
+    }
+}
+
 __device__ __forceinline__ uint32_t bit_length(uint32_t v) { return v ? 32u - __clz(v) : 0u; }
 
 // OR `width` (<= 16) bits of `value` into an LDS bit stream at `bitpos`.
@@ -233,6 +328,22 @@ __device__ __forceinline__ uint32_t lds_get_bits(const uint32_t *s, uint32_t bit
     const uint64_t v = (uint64_t)s[d] | ((uint64_t)s[d + 1] << 32);
     const uint64_t mask = (width >= 32) ? 0xFFFFFFFFull : ((1ull << width) - 1);
     return (uint32_t)((v >> sh) & mask);
+}
+
+// 8-bit mask of the non-zero 16-bit halves of a 16-byte chunk: bit s is set
+// iff element s (low half of dword s/2 for even s, high half for odd s) != 0.
+__device__ __forceinline__ uint32_t nz2(uint32_t w) {
+    // bit 15 of each half: its low 15 bits are non-zero, or bit 15 itself is set
+    return (((w & 0x7FFF7FFFu) + 0x7FFF7FFFu) | w) & 0x80008000u;
+}
+__device__ __forceinline__ uint32_t nonzero_halves(const uint4 &v) {
+    // halves of dword d land on bits 2d (low) and 2d+16 (high) ...
+    const uint32_t m = (nz2(v.x) >> 15) | (nz2(v.y) >> 13) | (nz2(v.z) >> 11) | (nz2(v.w) >> 9);
+    // ... then bits 16..22 move down next to their even partners
+    return (m & 0x55u) | ((m >> 15) & 0xAAu);
+}
+__device__ __forceinline__ uint4 and4(const uint4 &v, uint32_t m) {
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
 // Element s (0..7) of a 16-byte chunk held as uint4.
@@ -263,11 +374,13 @@ __device__ __forceinline__ uint64_t chunk_checksum(const uint4 &v, uint64_t e, u
 
 // ---- kernel launchers (defined in the .hip files) ------------------------------
 namespace bf16d {
+// workgroups of a persistent kernel: as many as fit on the device at once
+uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds = 0);
 void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
                       uint64_t tiles, hipStream_t stream);
 void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                           bf16d_result *results, hipStream_t stream);
+                           uint64_t dtiles, bf16d_result *results, hipStream_t stream);
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream);
 }  // namespace bf16d

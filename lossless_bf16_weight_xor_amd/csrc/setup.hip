@@ -34,6 +34,20 @@ static uint32_t grid_for(uint64_t items) {
     return (uint32_t)(g < 4096 ? (g ? g : 1) : 4096);
 }
 
+uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, dynamic_lds) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        cus = 256;
+        per_cu = 2;
+    }
+    const uint64_t g = (uint64_t)cus * (uint64_t)per_cu;
+    return (uint32_t)(tiles < g ? (tiles ? tiles : 1) : g);
+}
+
 void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
                       uint64_t tiles, hipStream_t stream) {
     map_tiles_kernel<<<grid_for(tiles), kThreads, 0, stream>>>(start, count, map, status, tiles);
