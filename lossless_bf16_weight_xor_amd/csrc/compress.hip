@@ -25,7 +25,7 @@
 // Placing records needs each record's byte offset: the exclusive sum of the
 // sizes of the job's earlier records.  Computing that inside the streaming
 // pass would stall it on a cross-workgroup look-back.  So the work is split:
-//   encode   : persistent, prefetching, no inter-workgroup waits.  Reads old
+//   encode   : one workgroup per tile, no inter-workgroup waits.  Reads old
 //              and new once.  Writes each record (if <= kSlot bytes) to a
 //              fixed per-tile slot in the workspace, plus its descriptor and
 //              checksum partials; larger records are listed for re-encoding.
@@ -79,10 +79,25 @@ __device__ __forceinline__ void load_tile(const TileRef &t, uint4 (&o)[kChunksPe
 
 // LDS shared by the encoding steps.
 struct EncodeShared {
-    uint32_t cnt[kChunksPerThread][kWaves];    // per round and wave: changed | rare << 16
-    uint32_t last[kChunksPerThread][kWaves];   // per round and wave: last changed position + 1
+    uint32_t cnt[kChunksPerThread * kWaves];    // [round][wave]: changed | rare << 16
+    uint32_t last[kChunksPerThread * kWaves];   // [round][wave]: last changed position + 1
     uint32_t gmax[kWaves];
+    uint8_t gap8[256];   // widest gap between set bits of an 8-bit mask (0 if < 2 bits)
 };
+
+// Fill sh.gap8 (once per workgroup; the caller synchronises).
+__device__ __forceinline__ void init_gap_table(EncodeShared &sh) {
+    const uint32_t m = threadIdx.x;   // kThreads == 256
+    uint32_t best = 0;
+    int prev = -1;
+    for (int b = 0; b < 8; ++b) {
+        if ((m >> b) & 1) {
+            if (prev >= 0) best = umax32(best, (uint32_t)(b - prev - 1));
+            prev = b;
+        }
+    }
+    sh.gap8[m] = (uint8_t)best;
+}
 
 // Result of classifying and scanning one tile (per thread, except the
 // uniform fields c, r, w, code, pb, mb, len, desc).
@@ -124,7 +139,7 @@ __device__ __forceinline__ void classify(const TileRef &t, const uint4 (&o)[kChu
         const uint64_t kg = kg0 + i * kRoundKg;
         if (valid > 0) acc += mix64(((uint64_t)nw[i].y << 32 | nw[i].x) ^ kg);
         if (valid > 4) acc += mix64(((uint64_t)nw[i].w << 32 | nw[i].z) ^ (kg + kGamma));
-        const uint32_t c8 = nonzero_halves(x), r8 = nonzero_halves(and4(x, 0xFF80FF80u));
+        const uint32_t c8 = nonzero8(x, 0xFFFFFFFFu), r8 = nonzero8(x, 0xFF80FF80u);
         M |= c8 << (8 * i);
         R |= r8 << (8 * i);
         f.cnt[i] = __popc(c8) | (__popc(r8) << 16);
@@ -150,42 +165,40 @@ __device__ __forceinline__ void scan(const TileRef &t, const TileFlags &f, Encod
         inc_last[i] = wave_incl_max(last[i]);
         const uint32_t tot = lane63(inc_cnt[i]), mx = lane63(inc_last[i]);
         if (lane == 0) {
-            sh.cnt[i][wave] = tot;
-            sh.last[i][wave] = mx;
+            sh.cnt[kWaves * i + wave] = tot;
+            sh.last[kWaves * i + wave] = mx;
         }
     }
     __syncthreads();
+    // the 16 (round, wave) totals in element order, scanned by lanes 0..15 of
+    // every wave (one DPP row): exclusive sums and exclusive maxima
+    const uint32_t v16 = lane < 16 ? sh.cnt[lane] : 0u, m16 = lane < 16 ? sh.last[lane] : 0u;
+    const uint32_t inc16 = row_incl_add(v16), max16 = row_incl_max(m16);
+    const uint32_t ex16 = inc16 - v16, exm16 = wave_shr1(max16);   // lane 0 reads 0
     uint64_t Jb = 0, Kb = 0, Pb = 0;
-    uint32_t run = 0, runmax = 0;
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-        uint32_t before = run, bmax = runmax;
-#pragma unroll
-        for (uint32_t w = 0; w < kWaves; ++w) {
-            const uint32_t v = sh.cnt[i][w], m = sh.last[i][w];
-            if (w < wave) {
-                before += v;
-                bmax = umax32(bmax, m);
-            }
-            run += v;
-            runmax = umax32(runmax, m);
-        }
-        const uint32_t ex = before + inc_cnt[i] - cnt[i];
+        const uint32_t base = readlane_u32(ex16, kWaves * i + wave);
+        const uint32_t pbase = readlane_u32(exm16, kWaves * i + wave);
+        const uint32_t ex = base + inc_cnt[i] - cnt[i];
         Jb |= (uint64_t)(ex & 0xFFFFu) << (16 * i);
         Kb |= (uint64_t)(ex >> 16) << (16 * i);
-        Pb |= (uint64_t)umax32(bmax, wave_shr1(inc_last[i])) << (16 * i);
+        Pb |= (uint64_t)umax32(pbase, wave_shr1(inc_last[i])) << (16 * i);
     }
+    const uint32_t run = readlane_u32(inc16, 15);
     const uint32_t c = run & 0xFFFFu, r = run >> 16;
 
-    // widest gap -> field width -> the cheaper position encoding
+    // widest gap: the gap before each chunk's first change, and the widest
+    // gap inside each chunk (table) -> field width -> cheaper encoding
     uint32_t maxgap = 0;
-    for (uint32_t bits = M; bits; bits &= bits - 1) {
-        const uint32_t idx = __ffs(bits) - 1, i = idx >> 3, s = idx & 7;
-        const uint32_t below = (M >> (8 * i)) & ((1u << s) - 1);
-        const uint32_t q = tid + kThreads * i;
-        const uint32_t p1 =
-            below ? 8 * q + 32 - __clz(below) : (uint32_t)(Pb >> (16 * i)) & 0xFFFFu;
-        maxgap = umax32(maxgap, 8 * q + s - p1);
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t c8 = (M >> (8 * i)) & 0xFFu;
+        if (c8) {
+            const uint32_t p1 = (uint32_t)(Pb >> (16 * i)) & 0xFFFFu;   // previous change + 1
+            const uint32_t first = 8 * (tid + kThreads * i) + __ffs(c8) - 1;
+            maxgap = umax32(maxgap, umax32(first - p1, sh.gap8[c8]));
+        }
     }
     maxgap = lane63(wave_incl_max(maxgap));
     if (lane == 0) sh.gmax[wave] = maxgap;
@@ -246,55 +259,47 @@ __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
 }
 
 // ------------------------------------------------------------------ encode ---
-// Persistent: workgroup g encodes tiles g, g + G, g + 2G, ... and keeps the
-// next tile's loads in flight while it encodes the current one.
-__global__ __launch_bounds__(kThreads) void encode_kernel(
-    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
-    uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ overflow, Control *__restrict__ ctrl, uint64_t tiles) {
+// One workgroup per tile, no inter-workgroup waits.  Occupancy hides the
+// load latency: with 53 VGPRs and 18.8 KiB of LDS, eight workgroups fit on a
+// CU.  That measured faster than a persistent loop that keeps the next
+// tile's loads in registers at half the occupancy.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
+void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
+                   uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out,
+                   uint64_t *__restrict__ partial, uint32_t *__restrict__ overflow,
+                   Control *__restrict__ ctrl) {
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
-    __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];   // kept zero
+    __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
     __shared__ EncodeShared sh;
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (uint32_t u = tid; u < kSlot / 4 + 4; u += kThreads) s_rec[u] = 0;
-    uint64_t t = blockIdx.x;
-    if (t >= tiles) return;
+    const uint64_t t = blockIdx.x;
+    const TileRef tr = tile_ref(jobs[tile_job[t]], t);
     uint4 o[kChunksPerThread], nw[kChunksPerThread];
-    load_tile(tile_ref(jobs[tile_job[t]], t), o, nw);
-    __syncthreads();   // s_rec cleared
+    load_tile(tr, o, nw);
+    // while the loads are in flight: clear the record, build the gap table
+    for (uint32_t u = tid; u < kSlot / 4 + 4; u += kThreads) s_rec[u] = 0;
+    init_gap_table(sh);
 
-    while (true) {
-        const TileRef tr = tile_ref(jobs[tile_job[t]], t);
-        TileFlags f;
-        classify(tr, o, nw, s_x, f);
-        // o/nw are free: the next tile's loads go out before the scans
-        const uint64_t next = t + gridDim.x;
-        if (next < tiles) load_tile(tile_ref(jobs[tile_job[next]], next), o, nw);
-        TileCode k;
-        scan(tr, f, sh, k);
+    TileFlags f;
+    classify(tr, o, nw, s_x, f);
+    TileCode k;
+    scan(tr, f, sh, k);   // its barriers also order the clearing above
 
-        const bool fits = k.len <= kSlot;
-        if (fits) or_fields<true>(s_rec, s_x, k);
-        const uint64_t acc = wave_sum(k.acc);
-        __syncthreads();
+    const bool fits = k.len <= kSlot;
+    if (fits) or_fields<true>(s_rec, s_x, k);
+    const uint64_t acc = wave_sum(k.acc);
+    __syncthreads();
 
-        if (fits) {
-            uint4 *slot = reinterpret_cast<uint4 *>(slots + t * kSlot);
-            uint4 *rec = reinterpret_cast<uint4 *>(s_rec);
-            for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) {
-                slot[u] = rec[u];
-                rec[u] = make_uint4(0, 0, 0, 0);   // only this thread touches dwords 4u..4u+3
-            }
-        } else if (tid == 0) {
-            overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
-        }
-        if (lane == 0) partial[kWaves * t + wave] = acc;
-        if (tid == 0) desc_out[t] = k.desc;
-
-        if (next >= tiles) break;
-        t = next;
+    if (fits) {
+        uint4 *slot = reinterpret_cast<uint4 *>(slots + t * kSlot);
+        const uint4 *rec = reinterpret_cast<const uint4 *>(s_rec);
+        for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) slot[u] = rec[u];
+    } else if (tid == 0) {
+        overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
     }
+    if (lane == 0) partial[kWaves * t + wave] = acc;
+    if (tid == 0) desc_out[t] = k.desc;
 }
 
 // ----------------------------------------------------------------- offsets ---
@@ -415,6 +420,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
     __shared__ EncodeShared sh;
     const uint32_t tid = threadIdx.x;
     const uint32_t count = ctrl->overflow_count;
+    init_gap_table(sh);   // ordered before use by the barriers in scan()
     for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
         const uint64_t t = overflow[i];
         const CompressJob job = jobs[tile_job[t]];
@@ -549,8 +555,8 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
         launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
-        encode_kernel<<<persistent_grid((const void *)encode_kernel, tiles), kThreads, 0,
-                        stream>>>(jobs, map, slots, desc, partial, overflow, ctrl, tiles);
+        encode_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, slots, desc, partial,
+                                                                overflow, ctrl);
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
             jobs, dmap, dstart, desc, dstatus, offsets, ctrl);
         place_kernel<<<(uint32_t)((tiles + kWaves - 1) / kWaves), kThreads, 0, stream>>>(

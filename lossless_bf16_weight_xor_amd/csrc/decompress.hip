@@ -16,7 +16,8 @@
 //               rejected before any weight is touched.
 //   apply     : one workgroup per 8192-element block.  The block's old
 //               weights are loaded into registers first, so HBM latency
-//               overlaps the decode.  The record is staged in LDS and
+//               overlaps the decode; occupancy (up to 6 workgroups per CU)
+//               hides the rest.  The record is staged in LDS and
 //               decoded into a dense 16 KiB XOR tile in LDS, checking that it
 //               is canonical.  Then old ^ tile is formed, only the changed
 //               16-byte chunks are written back, and the checksum terms of
@@ -177,278 +178,272 @@ struct RecordBits {
     }
 };
 
-// Per-tile metadata, read one tile ahead.
-struct ApplyMeta {
-    uint32_t job;
-    uint32_t desc;
-    uint64_t offset;
+struct ApplyShared {
+    uint32_t a[kWaves], b[kWaves], c[kWaves];
 };
 
+// Decode tile `tile` of job `j` and XOR it onto the weights.  s_x must be
+// all zero on entry; it is all zero again on return.  kRollback: undo a
+// previous pass (same decode, no checksum).
 template <bool kRollback>
-__global__ __launch_bounds__(kThreads) void apply_kernel(
-    const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
-    const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
-    uint64_t *__restrict__ partial, const Control *__restrict__ ctrl, uint64_t tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];   // dense XOR tile (kept zero)
-    __shared__ uint32_t s_raw[kStageWords + 4];                       // staged record
-    __shared__ uint32_t s_a[kWaves], s_b[kWaves], s_c[kWaves];
-
-    if (kRollback && ctrl->any_rollback == 0) return;
+__device__ __forceinline__ void apply_tile(const DecompressJob &job, uint32_t j, uint64_t tile,
+                                           DecompressState *__restrict__ state,
+                                           const uint64_t *__restrict__ offsets,
+                                           uint64_t *__restrict__ partial, uint16_t *s_x,
+                                           uint32_t *s_raw, ApplyShared &sa) {
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
-        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+    const uint64_t b = tile - job.block0;
+    const uint64_t base = b * kBlock;
+    const uint32_t L = block_length(job.n, b);
 
-    // tiles of this workgroup: blockIdx.x, blockIdx.x + gridDim.x, ... of
-    // the jobs that take part (ready, or marked for rollback)
-    auto wanted = [&](uint32_t j) {
-        return kRollback ? state[j].rollback != 0 : state[j].state == kStateReady;
-    };
-    uint64_t tile = blockIdx.x;
+    // old weights first: their latency overlaps the decode
     uint4 o[kChunksPerThread];
-    ApplyMeta meta{};
-    auto fetch = [&](uint64_t t, ApplyMeta &m, uint4 (&old)[kChunksPerThread]) {
-        m.job = tile_job[t];
-        const DecompressJob &J = jobs[m.job];
-        const uint64_t b = t - J.block0;
-        const uint32_t L = block_length(J.n, b);
 #pragma unroll
-        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-            const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
-            old[i] = make_uint4(0, 0, 0, 0);
-            if (e0 < L) old[i] = load_chunk(J.weights + b * kBlock + e0, L - e0);
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t e0 = 8 * (tid + kThreads * i);
+        o[i] = make_uint4(0, 0, 0, 0);
+        if (e0 < L) o[i] = load_chunk(job.weights + base + e0, L - e0);
+    }
+    const uint32_t desc = *reinterpret_cast<const uint32_t *>(job.payload + kHeader + 4 * b);
+    const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
+    const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
+    const uint32_t mb = (7 * c + 7) / 8;
+    const uint32_t len = pb + mb + 2 * r;
+    const uint64_t D = kHeader + 4 * job.nb + offsets[tile];
+
+    // stage the first kStage bytes of the record window
+    RecordBits rb;
+    rb.lds = s_raw;
+    rb.payload = job.payload;
+    rb.payload_bytes = job.payload_bytes;
+    rb.rb0 = 8 * (uint32_t)(D & 3);
+    rb.a0 = D & ~3ull;
+    {
+        const uint32_t nraw = (uint32_t)((D & 3) + len + 3) / 4 + 1;
+        const uint32_t n_stage = nraw < kStageWords + 4 ? nraw : kStageWords + 4;
+        for (uint32_t u = tid; u < n_stage; u += kThreads) {
+            const uint64_t A = rb.a0 + 4ull * u;
+            uint32_t v = 0;
+            if (A + 4 <= job.payload_bytes) {
+                v = *reinterpret_cast<const uint32_t *>(job.payload + A);
+            } else {
+                for (uint32_t t = 0; t < 4; ++t)
+                    if (A + t < job.payload_bytes) v |= (uint32_t)job.payload[A + t] << (8 * t);
+            }
+            s_raw[u] = v;
         }
-        m.desc = *reinterpret_cast<const uint32_t *>(J.payload + kHeader + 4 * b);
-        m.offset = offsets[t];
-    };
-    while (tile < tiles && !wanted(tile_job[tile])) tile += gridDim.x;
-    if (tile >= tiles) return;
-    fetch(tile, meta, o);
-    __syncthreads();   // s_x cleared
+    }
+    __syncthreads();   // record staged
 
-    while (true) {
-        const uint32_t j = meta.job;
-        const DecompressJob job = jobs[j];
-        const uint64_t b = tile - job.block0;
-        const uint64_t base = b * kBlock;
-        const uint32_t L = block_length(job.n, b);
-        const uint32_t desc = meta.desc;
-        const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
-        const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
-        const uint32_t mb = (7 * c + 7) / 8;
-        const uint32_t len = pb + mb + 2 * r;
-        const uint64_t D = kHeader + 4 * job.nb + meta.offset;
-
-        // stage the first kStage bytes of the record window
-        RecordBits rb;
-        rb.lds = s_raw;
-        rb.payload = job.payload;
-        rb.payload_bytes = job.payload_bytes;
-        rb.rb0 = 8 * (uint32_t)(D & 3);
-        rb.a0 = D & ~3ull;
+    // ---- decode the record into s_x, checking that it is canonical ----
+    const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
+    uint32_t bad = 0;
+    if (code == kCodeBitmap) {
+        // thread t owns bitmap bits [32t, 32t + 32) = elements 32t .. 32t+31
+        const uint32_t lo = 32 * tid, seg_end = 8 * pb;
+        uint32_t word = 0;
+        if (lo < seg_end) {
+            word = rb.get(lo, 32);
+            if (lo + 32 > seg_end) word &= (1u << (seg_end - lo)) - 1;
+        }
+        const uint32_t valid_mask =
+            lo + 32 <= L ? 0xFFFFFFFFu : (lo >= L ? 0u : (1u << (L - lo)) - 1);
+        bad |= (word & ~valid_mask) != 0;               // pad bits must be zero
+        word &= valid_mask;
+        const uint32_t pop = __popc(word);
+        const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
+        const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
+        if (lane == 0) {
+            sa.a[wave] = lane63(inc_pop);
+            sa.b[wave] = lane63(inc_last);
+        }
+        __syncthreads();
+        uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
+        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+            if (w2 < wave) {
+                rank0 += sa.a[w2];
+                prev1 = umax32(prev1, sa.b[w2]);
+            }
+            total += sa.a[w2];
+        }
+        bad |= total != c;
+        // gaps before each set bit, and the escapes among this thread's fields
+        uint32_t maxg = 0, esc = 0;
         {
-            const uint32_t nraw = (uint32_t)((D & 3) + len + 3) / 4 + 1;
-            const uint32_t n_stage = nraw < kStageWords + 4 ? nraw : kStageWords + 4;
-            for (uint32_t u = tid; u < n_stage; u += kThreads) {
-                const uint64_t A = rb.a0 + 4ull * u;
-                uint32_t v = 0;
-                if (A + 4 <= job.payload_bytes) {
-                    v = *reinterpret_cast<const uint32_t *>(job.payload + A);
-                } else {
-                    for (uint32_t t = 0; t < 4; ++t)
-                        if (A + t < job.payload_bytes)
-                            v |= (uint32_t)job.payload[A + t] << (8 * t);
-                }
-                s_raw[u] = v;
-            }
-        }
-
-        // prefetch the next wanted tile
-        uint64_t next = tile + gridDim.x;
-        while (next < tiles && !wanted(tile_job[next])) next += gridDim.x;
-        uint4 o2[kChunksPerThread];
-        ApplyMeta meta2{};
-        if (next < tiles) fetch(next, meta2, o2);
-        __syncthreads();   // barrier A: record staged
-
-        // ---- decode the record into s_x, checking that it is canonical ----
-        const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
-        uint32_t bad = 0;
-        if (code == kCodeBitmap) {
-            // thread t owns bitmap bits [32t, 32t + 32) = elements 32t .. 32t+31
-            const uint32_t lo = 32 * tid, seg_end = 8 * pb;
-            uint32_t word = 0;
-            if (lo < seg_end) {
-                word = rb.get(lo, 32);
-                if (lo + 32 > seg_end) word &= (1u << (seg_end - lo)) - 1;
-            }
-            const uint32_t valid_mask =
-                lo + 32 <= L ? 0xFFFFFFFFu : (lo >= L ? 0u : (1u << (L - lo)) - 1);
-            bad |= (word & ~valid_mask) != 0;               // pad bits must be zero
-            word &= valid_mask;
-            const uint32_t pop = __popc(word);
-            const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
-            const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
-            if (lane == 0) {
-                s_a[wave] = lane63(inc_pop);
-                s_b[wave] = lane63(inc_last);
-            }
-            __syncthreads();   // barrier B1
-            uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
-            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-                if (w2 < wave) {
-                    rank0 += s_a[w2];
-                    prev1 = umax32(prev1, s_b[w2]);
-                }
-                total += s_a[w2];
-            }
-            bad |= total != c;
-            // gaps before each set bit, and the escapes among this thread's fields
-            uint32_t maxg = 0, esc = 0;
-            {
-                uint32_t bits = word, jj = rank0, p1 = prev1;
-                while (bits) {
-                    const uint32_t p = lo + __ffs(bits) - 1;
-                    bits &= bits - 1;
-                    maxg = umax32(maxg, p - p1);
-                    p1 = p + 1;
-                    esc += rb.get(mant0 + 7 * jj, 7) == 0;
-                    ++jj;
-                }
-            }
-            const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
-            __syncthreads();   // barrier B2 (s_a / s_b reads done)
-            if (lane == 0) {
-                s_a[wave] = lane63(inc_esc);
-                s_c[wave] = wmax;
-            }
-            __syncthreads();   // barrier B3
-            uint32_t e = inc_esc - esc, esc_total = 0;
-            maxg = 0;
-            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-                if (w2 < wave) e += s_a[w2];
-                esc_total += s_a[w2];
-                maxg = umax32(maxg, s_c[w2]);
-            }
-            bad |= esc_total != r;
-            bad |= !(pb < (c * bit_length(maxg) + 7) / 8);   // a bitmap only when smaller
-            uint32_t bits = word, jj = rank0;
+            uint32_t bits = word, jj = rank0, p1 = prev1;
             while (bits) {
                 const uint32_t p = lo + __ffs(bits) - 1;
                 bits &= bits - 1;
-                uint32_t x = rb.get(mant0 + 7 * jj, 7);
-                if (x == 0) {
-                    if (e < r) {
-                        x = rb.get(rare0 + 16 * e, 16);
-                        bad |= (x & kExpSign) == 0;
-                    } else {
-                        bad = 1;
-                    }
-                    ++e;
-                }
-                s_x[p] = (uint16_t)x;
+                maxg = umax32(maxg, p - p1);
+                p1 = p + 1;
+                esc += rb.get(mant0 + 7 * jj, 7) == 0;
                 ++jj;
             }
-        } else {
-            // gap list of width w: thread t owns fields [t*F, t*F + F)
-            const uint32_t w = code;
-            const uint32_t F = (c + kThreads - 1) / kThreads;
-            const uint32_t jb = tid * F < c ? tid * F : c;
-            const uint32_t je = jb + F < c ? jb + F : c;
-            uint32_t sum_g1 = 0, esc = 0, maxg = 0;
-            for (uint32_t jj = jb; jj < je; ++jj) {
-                const uint32_t g = w ? rb.get(jj * w, w) : 0;
-                sum_g1 += g + 1;
-                maxg = umax32(maxg, g);
-                esc += rb.get(mant0 + 7 * jj, 7) == 0;
-            }
-            const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
-            const uint32_t wmax = lane63(wave_incl_max(maxg));
-            if (lane == 0) {
-                s_a[wave] = lane63(inc_g);
-                s_b[wave] = lane63(inc_e);
-                s_c[wave] = wmax;
-            }
-            __syncthreads();   // barrier B1
-            uint32_t run = inc_g - sum_g1, e = inc_e - esc;
-            uint32_t total_g1 = 0, esc_total = 0;
-            maxg = 0;
-            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-                if (w2 < wave) {
-                    run += s_a[w2];
-                    e += s_b[w2];
-                }
-                total_g1 += s_a[w2];
-                esc_total += s_b[w2];
-                maxg = umax32(maxg, s_c[w2]);
-            }
-            bad |= (c > 0) && (total_g1 - 1 >= L);          // last position inside the block
-            bad |= esc_total != r;
-            bad |= bit_length(maxg) != w;                    // width is minimal
-            for (uint32_t jj = jb; jj < je; ++jj) {
-                const uint32_t g = w ? rb.get(jj * w, w) : 0;
-                run += g + 1;
-                const uint32_t p = run - 1;
-                uint32_t x = rb.get(mant0 + 7 * jj, 7);
-                if (x == 0) {
-                    if (e < r) {
-                        x = rb.get(rare0 + 16 * e, 16);
-                        bad |= (x & kExpSign) == 0;
-                    } else {
-                        bad = 1;
-                    }
-                    ++e;
-                }
-                if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
-            }
-            if (tid == 0 && 8 * pb > c * w)                  // position padding
-                bad |= rb.get(c * w, 8 * pb - c * w) != 0;
         }
-        if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
-            bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
-        bad = __syncthreads_or(bad);   // barrier C: s_x complete
-
-        // ---- new = old ^ tile; store only changed chunks; clear the tile ----
-        uint64_t acc = 0;
-        const uint64_t thread_kg = (uint64_t)(2 * tid) * kGamma;
-        const uint64_t tile_kg = ((base >> 2) + 1) * kGamma + thread_kg;
-#pragma unroll
-        for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-            const uint32_t q = tid + kThreads * i;
-            const uint32_t e0 = 8 * q;
-            const uint32_t valid = e0 < L ? (L - e0 < 8 ? L - e0 : 8) : 0;
-            const uint4 t = reinterpret_cast<const uint4 *>(s_x)[q];
-            const bool dirty = (t.x | t.y | t.z | t.w) != 0;
-            uint4 nw = o[i];
-            if (dirty) {
-                reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
-                if (!bad) {
-                    nw = make_uint4(o[i].x ^ t.x, o[i].y ^ t.y, o[i].z ^ t.z, o[i].w ^ t.w);
-                    uint16_t *dstp = job.weights + base + e0;
-                    if (valid == 8) {
-                        *reinterpret_cast<uint4 *>(dstp) = nw;
-                    } else {
-                        for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
-                    }
+        const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
+        __syncthreads();   // sa.a / sa.b reads done
+        if (lane == 0) {
+            sa.a[wave] = lane63(inc_esc);
+            sa.c[wave] = wmax;
+        }
+        __syncthreads();
+        uint32_t e = inc_esc - esc, esc_total = 0;
+        maxg = 0;
+        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+            if (w2 < wave) e += sa.a[w2];
+            esc_total += sa.a[w2];
+            maxg = umax32(maxg, sa.c[w2]);
+        }
+        bad |= esc_total != r;
+        bad |= !(pb < (c * bit_length(maxg) + 7) / 8);   // a bitmap only when smaller
+        uint32_t bits = word, jj = rank0;
+        while (bits) {
+            const uint32_t p = lo + __ffs(bits) - 1;
+            bits &= bits - 1;
+            uint32_t x = rb.get(mant0 + 7 * jj, 7);
+            if (x == 0) {
+                if (e < r) {
+                    x = rb.get(rare0 + 16 * e, 16);
+                    bad |= (x & kExpSign) == 0;
+                } else {
+                    bad = 1;
                 }
+                ++e;
             }
-            if (!kRollback) {
-                const uint64_t kg = tile_kg + (uint64_t)i * ((uint64_t)(2 * kThreads) * kGamma);
-                if (valid > 0) acc += mix64(((uint64_t)nw.y << 32 | nw.x) ^ kg);
-                if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + kGamma));
+            s_x[p] = (uint16_t)x;
+            ++jj;
+        }
+    } else {
+        // gap list of width w: thread t owns fields [t*F, t*F + F)
+        const uint32_t w = code;
+        const uint32_t F = (c + kThreads - 1) / kThreads;
+        const uint32_t jb = tid * F < c ? tid * F : c;
+        const uint32_t je = jb + F < c ? jb + F : c;
+        uint32_t sum_g1 = 0, esc = 0, maxg = 0;
+        for (uint32_t jj = jb; jj < je; ++jj) {
+            const uint32_t g = w ? rb.get(jj * w, w) : 0;
+            sum_g1 += g + 1;
+            maxg = umax32(maxg, g);
+            esc += rb.get(mant0 + 7 * jj, 7) == 0;
+        }
+        const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
+        const uint32_t wmax = lane63(wave_incl_max(maxg));
+        if (lane == 0) {
+            sa.a[wave] = lane63(inc_g);
+            sa.b[wave] = lane63(inc_e);
+            sa.c[wave] = wmax;
+        }
+        __syncthreads();
+        uint32_t run = inc_g - sum_g1, e = inc_e - esc;
+        uint32_t total_g1 = 0, esc_total = 0;
+        maxg = 0;
+        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+            if (w2 < wave) {
+                run += sa.a[w2];
+                e += sa.b[w2];
+            }
+            total_g1 += sa.a[w2];
+            esc_total += sa.b[w2];
+            maxg = umax32(maxg, sa.c[w2]);
+        }
+        bad |= (c > 0) && (total_g1 - 1 >= L);          // last position inside the block
+        bad |= esc_total != r;
+        bad |= bit_length(maxg) != w;                    // width is minimal
+        for (uint32_t jj = jb; jj < je; ++jj) {
+            const uint32_t g = w ? rb.get(jj * w, w) : 0;
+            run += g + 1;
+            const uint32_t p = run - 1;
+            uint32_t x = rb.get(mant0 + 7 * jj, 7);
+            if (x == 0) {
+                if (e < r) {
+                    x = rb.get(rare0 + 16 * e, 16);
+                    bad |= (x & kExpSign) == 0;
+                } else {
+                    bad = 1;
+                }
+                ++e;
+            }
+            if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
+        }
+        if (tid == 0 && 8 * pb > c * w)                  // position padding
+            bad |= rb.get(c * w, 8 * pb - c * w) != 0;
+    }
+    if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
+        bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
+    bad = __syncthreads_or(bad);   // s_x complete
+
+    // ---- new = old ^ tile; store only changed chunks; clear the tile ----
+    uint64_t acc = 0;
+    const uint64_t kg0 = ((base >> 2) + 1 + 2 * tid) * kGamma;
+    constexpr uint64_t kRoundKg = (uint64_t)(2 * kThreads) * kGamma;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t q = tid + kThreads * i;
+        const uint32_t e0 = 8 * q;
+        const uint32_t valid = e0 < L ? (L - e0 < 8 ? L - e0 : 8) : 0;
+        const uint4 t = reinterpret_cast<const uint4 *>(s_x)[q];
+        const bool dirty = (t.x | t.y | t.z | t.w) != 0;
+        uint4 nw = o[i];
+        if (dirty) {
+            reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
+            if (!bad) {
+                nw = make_uint4(o[i].x ^ t.x, o[i].y ^ t.y, o[i].z ^ t.z, o[i].w ^ t.w);
+                uint16_t *dstp = job.weights + base + e0;
+                if (valid == 8) {
+                    *reinterpret_cast<uint4 *>(dstp) = nw;
+                } else {
+                    for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
+                }
             }
         }
         if (!kRollback) {
-            acc = wave_sum(acc);
-            if (lane == 0) partial[kWaves * tile + wave] = acc;
-            if (tid == 0 && bad) atomicOr(&state[j].block_bad, 1u);
+            const uint64_t kg = kg0 + i * kRoundKg;
+            if (valid > 0) acc += mix64(((uint64_t)nw.y << 32 | nw.x) ^ kg);
+            if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + kGamma));
         }
+    }
+    if (!kRollback) {
+        acc = wave_sum(acc);
+        if (lane == 0) partial[kWaves * tile + wave] = acc;
+        if (tid == 0 && bad) atomicOr(&state[j].block_bad, 1u);
+    }
+}
 
-        if (next >= tiles) break;
-        tile = next;
-        meta = meta2;
-#pragma unroll
-        for (uint32_t i = 0; i < kChunksPerThread; ++i) o[i] = o2[i];
-        __syncthreads();   // barrier D: s_x cleared, s_raw and s_a..s_c free again
+// The apply pass: one workgroup per tile of the jobs that passed the
+// header and descriptor checks.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
+void apply_kernel(const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
+                  const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
+                  uint64_t *__restrict__ partial) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];   // dense XOR tile
+    __shared__ uint32_t s_raw[kStageWords + 4];                       // staged record
+    __shared__ ApplyShared sa;
+    const uint64_t tile = blockIdx.x;
+    const uint32_t j = tile_job[tile];
+    if (state[j].state != kStateReady) return;
+    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
+        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+    // (the barrier after staging orders this clearing before the decode)
+    apply_tile<false>(jobs[j], j, tile, state, offsets, partial, s_x, s_raw, sa);
+}
+
+// The undo pass, for failed jobs only: a persistent grid that exits at once
+// when nothing failed.
+__global__ __launch_bounds__(kThreads) void rollback_kernel(
+    const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
+    const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
+    const Control *__restrict__ ctrl, uint64_t tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
+    __shared__ uint32_t s_raw[kStageWords + 4];
+    __shared__ ApplyShared sa;
+    if (ctrl->any_rollback == 0) return;
+    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
+        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const uint32_t j = tile_job[tile];
+        if (state[j].rollback == 0) continue;   // uniform across the workgroup
+        apply_tile<true>(jobs[j], j, tile, state, offsets, nullptr, s_x, s_raw, sa);
+        __syncthreads();   // LDS reused by the next tile
     }
 }
 
@@ -516,14 +511,13 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
                                                                                count);
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
-        apply_kernel<false><<<persistent_grid((const void *)apply_kernel<false>, tiles), kThreads,
-                              0, stream>>>(jobs, state, map, offsets, partial, ctrl, tiles);
+        apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, state, map, offsets, partial);
     }
     decompress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, state, partial, ctrl,
                                                                results);
     if (tiles) {
-        apply_kernel<true><<<persistent_grid((const void *)apply_kernel<true>, tiles), kThreads, 0,
-                             stream>>>(jobs, state, map, offsets, partial, ctrl, tiles);
+        rollback_kernel<<<persistent_grid((const void *)rollback_kernel, tiles), kThreads, 0,
+                          stream>>>(jobs, state, map, offsets, ctrl, tiles);
     }
     return hipGetLastError();
 }

@@ -247,6 +247,24 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
     v = umax32(v, dpp_src<0x143, 0xc>(v));
     return v;
 }
+// inclusive scans within each row of 16 lanes
+__device__ __forceinline__ uint32_t row_incl_add(uint32_t v) {
+    v += dpp_src<0x111>(v);
+    v += dpp_src<0x112>(v);
+    v += dpp_src<0x114>(v);
+    v += dpp_src<0x118>(v);
+    return v;
+}
+__device__ __forceinline__ uint32_t row_incl_max(uint32_t v) {
+    v = umax32(v, dpp_src<0x111>(v));
+    v = umax32(v, dpp_src<0x112>(v));
+    v = umax32(v, dpp_src<0x114>(v));
+    v = umax32(v, dpp_src<0x118>(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, uint32_t lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
+}
 // value of the previous lane (0 for lane 0)
 __device__ __forceinline__ uint32_t wave_shr1(uint32_t v) { return dpp_src<0x138>(v); }
 __device__ __forceinline__ uint32_t lane63(uint32_t v) {
@@ -341,6 +359,22 @@ __device__ __forceinline__ uint32_t nonzero_halves(const uint4 &v) {
     const uint32_t m = (nz2(v.x) >> 15) | (nz2(v.y) >> 13) | (nz2(v.z) >> 11) | (nz2(v.w) >> 9);
     // ... then bits 16..22 move down next to their even partners
     return (m & 0x55u) | ((m >> 15) & 0xAAu);
+}
+// Per 16-bit half: min(half, 1), i.e. 1 where the half is non-zero.  Written
+// as the packed-integer instruction itself: the compiler would otherwise turn
+// the min into two compares and two selects per dword.
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t w, uint32_t ones) {
+    uint32_t r;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(w), "v"(ones));
+    return r;
+}
+// 8-bit element-order mask of the non-zero halves of (v & mask).
+__device__ __forceinline__ uint32_t nonzero8(const uint4 &v, uint32_t mask) {
+    const uint32_t ones = 0x00010001u;
+    // low halves (elements 0,2,4,6) land on bits 0,2,4,6; high halves on 16,18,20,22
+    const uint32_t s = pk_min_u16(v.x & mask, ones) | (pk_min_u16(v.y & mask, ones) << 2) |
+                       (pk_min_u16(v.z & mask, ones) << 4) | (pk_min_u16(v.w & mask, ones) << 6);
+    return (s & 0x55u) | ((s >> 15) & 0xAAu);
 }
 __device__ __forceinline__ uint4 and4(const uint4 &v, uint32_t m) {
     return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
