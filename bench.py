@@ -19,7 +19,8 @@ Reported:
   value     : GB/s of BF16 weights through the round trip, 2*n / step time
   compress  : GB/s of weights, and % of HBM peak on algorithmic bytes (4n + P)
   decompress: GB/s of weights, and % of HBM peak on algorithmic bytes (2n + P + 2c)
-  roofline  : the compress call (the dominant kernel) against 8 TB/s
+  roofline  : the encode kernel (the dominant kernel of a step) against 8 TB/s,
+              timed with events recorded around it on its stream
   cpu_baseline : the CPU oracle on a bounded sample of the same workload
 
 Only one GPU is used; --gpus above 1 is refused.
@@ -40,6 +41,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "compress / decompress GB/s of BF16 weights (% of HBM peak); payload % of orig"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "encode_kernel_7b_traffic.txt")
+KERNEL_SOURCES = ("lossless_bf16_weight_xor_amd/csrc/compress.hip",
+                  "lossless_bf16_weight_xor_amd/csrc/internal.hpp")
 
 
 def log(msg):
@@ -71,6 +75,34 @@ def generate(workload: str, device, limit=None):
         names.append(name)
         pairs.append((src.reshape(-1), dst.reshape(-1)))
     return names, pairs, desc
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per encode launch from the committed counter summary, or None
+    if there is none or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(pairs, gpu_payloads, budget_s: float):
@@ -125,6 +157,8 @@ def main():
     ap.add_argument("--limit", type=int, default=None, help="first N tensors only (debug)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the delta path is "
@@ -183,10 +217,10 @@ def main():
         for j in range(len(cs)):
             dec.jobs[j].checksum = cs[j]
         if ev: ev[0].record()
-        comp.run()
-        if ev: ev[1].record()
-        dec.run()
-        if ev: ev[2].record()
+        comp.run(events=(ev[1], ev[2]) if ev else None)
+        if ev: ev[3].record()
+        dec.run(events=(ev[4], ev[5]) if ev else None)
+        if ev: ev[6].record()
         direction[0] ^= 1
 
     for _ in range(args.warmup):
@@ -195,7 +229,10 @@ def main():
     if args.warmup:
         assert all(r["status"] == bd.OK for r in dec.results()), "warm-up decompress failed"
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    for e in evs:                      # create the HIP events outside the timed region
+        for x in e:
+            x.record()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -210,14 +247,24 @@ def main():
         ref = d if expect_new else s
         assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "receiver not bit-exact"
 
-    t_comp = [evs[i][0].elapsed_time(evs[i][1]) / 1e3 for i in range(args.steps)]
-    t_dec = [evs[i][1].elapsed_time(evs[i][2]) / 1e3 for i in range(args.steps)]
-    tc, td = float(np.mean(t_comp)), float(np.mean(t_dec))
+    def avg(a, b):
+        return float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)])) / 1e3
+
+    tc, td = avg(0, 3), avg(3, 6)            # whole calls
+    t_enc, t_app = avg(1, 2), avg(4, 5)      # their main kernels
     ms_per_step = 1e3 * elapsed / args.steps
     w_bytes = 2 * n_total
     comp_alg = 4 * n_total + payload_total
     dec_alg = 2 * n_total + payload_total + 2 * n_changed
     value = w_bytes / (elapsed / args.steps) / 1e9
+
+    if args.with_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     gpu_payloads = [None] * len(pairs)
     cpu = None
@@ -243,17 +290,23 @@ def main():
                    "weights_bytes": w_bytes, "parallelism": "single GPU"},
         "compress": {"gbps_weights": round(w_bytes / tc / 1e9, 2),
                      "hbm_pct": round(100 * comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 2),
-                     "ms": round(1e3 * tc, 4), "algorithmic_bytes": comp_alg},
+                     "ms": round(1e3 * tc, 4), "encode_kernel_ms": round(1e3 * t_enc, 4),
+                     "algorithmic_bytes": comp_alg},
         "decompress": {"gbps_weights": round(w_bytes / td / 1e9, 2),
                        "hbm_pct": round(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS, 2),
-                       "ms": round(1e3 * td, 4), "algorithmic_bytes": dec_alg},
+                       "ms": round(1e3 * td, 4), "apply_kernel_ms": round(1e3 * t_app, 4),
+                       "algorithmic_bytes": dec_alg},
         "payload_pct_of_orig": round(100 * payload_total / w_bytes, 4),
         "payload_bytes": payload_total,
         "n_changed": n_changed, "n_rare": n_rare, "bitmap_blocks": n_bitmap,
-        "roofline": {"bound": "hbm", "kernel": "bf16d_compress call",
-                     "achieved": round(comp_alg / tc / 1e9, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "encode_kernel",
+                     "achieved": round(comp_alg / t_enc / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(comp_alg / t_enc / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic()},
+        "roofline_decompress": {"bound": "hbm", "kernel": "apply_kernel",
+                                "achieved": round(dec_alg / t_app / 1e9, 2),
+                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

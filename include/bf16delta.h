@@ -173,6 +173,27 @@ int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count,
                      void *workspace, size_t workspace_bytes,
                      bf16d_result *results, hipStream_t stream);
 
+/* Events recorded on the call's stream immediately before and after the main
+ * kernel of a call (compress: the encode kernel, which reads both
+ * checkpoints; decompress: the apply kernel, which rewrites the weights).
+ * They let a caller time that kernel alone.  The caller owns the events,
+ * which must be created with timing enabled; either may be NULL. */
+typedef struct bf16d_events {
+    hipEvent_t before;
+    hipEvent_t after;
+} bf16d_events;
+
+/* bf16d_compress / bf16d_decompress plus kernel events (`events` may be
+ * NULL, which is exactly the plain call). */
+int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count,
+                      void *workspace, size_t workspace_bytes,
+                      bf16d_result *results, hipStream_t stream,
+                      const bf16d_events *events);
+int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count,
+                        void *workspace, size_t workspace_bytes,
+                        bf16d_result *results, hipStream_t stream,
+                        const bf16d_events *events);
+
 /* Single-tensor forms of the two calls above, named after the pages'
  * delta_compress(src, dst) -> (payload, checksum) and
  * delta_decompress(src, payload, checksum) -> dst ("Every byte counts:

@@ -80,6 +80,17 @@ def _check_rc(rc: int, what: str) -> None:
         raise RuntimeError(f"{what} failed: {_native.status_string(rc)}")
 
 
+def _events(events):
+    """(before, after) timing-enabled torch.cuda.Event pair -> bf16d_events*, or None."""
+    if events is None:
+        return None
+    before, after = events
+    for e in (before, after):
+        if e.cuda_event == 0:       # torch creates the HIP event on first use
+            e.record()
+    return ctypes.byref(_native.Events(before.cuda_event, after.cuda_event))
+
+
 def _results(buf: torch.Tensor, count: int) -> list[dict]:
     host = buf[: count * RESULT_BYTES].cpu().numpy().tobytes()
     out = []
@@ -128,10 +139,13 @@ class CompressBatch:
             self.jobs[j] = CompressJob(_weights_ptr(src, "src"), _weights_ptr(dst, "dst"),
                                        src.numel(), base + self.offset[j], self.capacity[j])
 
-    def run(self) -> None:
-        rc = _native.lib().bf16d_compress(self.jobs, self.count, self.workspace.data_ptr(),
-                                          self.ws_bytes, self.result_buf.data_ptr(),
-                                          _stream(self.device))
+    def run(self, events=None) -> None:
+        """Enqueue the call.  `events`: optional (before, after) torch.cuda.Event
+        pair, recorded around the encode kernel."""
+        ev = _events(events)
+        rc = _native.lib().bf16d_compress_ex(self.jobs, self.count, self.workspace.data_ptr(),
+                                             self.ws_bytes, self.result_buf.data_ptr(),
+                                             _stream(self.device), ev)
         _check_rc(rc, "bf16d_compress")
 
     def results(self) -> list[dict]:
@@ -172,10 +186,13 @@ class DecompressBatch:
     def set_checksum(self, j: int, checksum: int) -> None:
         self.jobs[j].checksum = int(checksum) & 0xFFFFFFFFFFFFFFFF
 
-    def run(self) -> None:
-        rc = _native.lib().bf16d_decompress(self.jobs, self.count, self.workspace.data_ptr(),
-                                            self.ws_bytes, self.result_buf.data_ptr(),
-                                            _stream(self.device))
+    def run(self, events=None) -> None:
+        """Enqueue the call.  `events`: optional (before, after) torch.cuda.Event
+        pair, recorded around the apply kernel."""
+        ev = _events(events)
+        rc = _native.lib().bf16d_decompress_ex(self.jobs, self.count, self.workspace.data_ptr(),
+                                               self.ws_bytes, self.result_buf.data_ptr(),
+                                               _stream(self.device), ev)
         _check_rc(rc, "bf16d_decompress")
 
     def results(self) -> list[dict]:

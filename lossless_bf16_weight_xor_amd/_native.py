@@ -19,8 +19,9 @@ HEADER_BYTES = 64
 FORMAT_VERSION = 1
 
 EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress",
-            "bf16d_decompress", "bf16d_delta_compress", "bf16d_delta_decompress",
-            "bf16d_status_string", "bf16d_format_version")
+            "bf16d_decompress", "bf16d_compress_ex", "bf16d_decompress_ex",
+            "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_status_string",
+            "bf16d_format_version")
 
 
 class Result(ctypes.Structure):
@@ -39,6 +40,10 @@ class DecompressJob(ctypes.Structure):
     _fields_ = [("weights", ctypes.c_void_p), ("n", ctypes.c_uint64),
                 ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64),
                 ("checksum", ctypes.c_uint64)]
+
+
+class Events(ctypes.Structure):
+    _fields_ = [("before", ctypes.c_void_p), ("after", ctypes.c_void_p)]
 
 
 RESULT_BYTES = ctypes.sizeof(Result)
@@ -68,6 +73,12 @@ def lib():
         L.bf16d_compress.restype = ctypes.c_int
         L.bf16d_decompress.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp, vp]
         L.bf16d_decompress.restype = ctypes.c_int
+        L.bf16d_compress_ex.argtypes = [ctypes.POINTER(CompressJob), u32, vp, sz, vp, vp,
+                                        ctypes.POINTER(Events)]
+        L.bf16d_compress_ex.restype = ctypes.c_int
+        L.bf16d_decompress_ex.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp, vp,
+                                          ctypes.POINTER(Events)]
+        L.bf16d_decompress_ex.restype = ctypes.c_int
         L.bf16d_delta_compress.argtypes = [vp, vp, u64, vp, u64, vp, sz, vp, vp]
         L.bf16d_delta_compress.restype = ctypes.c_int
         L.bf16d_delta_decompress.argtypes = [vp, u64, vp, u64, u64, vp, sz, vp, vp]

@@ -70,6 +70,12 @@ size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
 
 int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
                    size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
+    return bf16d_compress_ex(jobs, count, workspace, workspace_bytes, results, stream, nullptr);
+}
+
+int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
+                      size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
+                      const bf16d_events *events) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
     std::vector<uint64_t> start(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
@@ -116,13 +122,19 @@ int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspa
     int rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
     return launch_compress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
-                           stream) == hipSuccess
+                           stream, events) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
 }
 
 int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
                      size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
+    return bf16d_decompress_ex(jobs, count, workspace, workspace_bytes, results, stream, nullptr);
+}
+
+int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
+                        size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
+                        const bf16d_events *events) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
     std::vector<uint64_t> bstart(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
@@ -167,7 +179,7 @@ int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *wor
     int rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
     return launch_decompress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
-                             stream) == hipSuccess
+                             stream, events) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
 }

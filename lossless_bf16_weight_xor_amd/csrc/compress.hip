@@ -537,7 +537,8 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
 }
 
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                           uint64_t dtiles, bf16d_result *results, hipStream_t stream) {
+                           uint64_t dtiles, bf16d_result *results, hipStream_t stream,
+                           const bf16d_events *events) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const CompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
@@ -555,8 +556,12 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
         launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
+        if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
+            return hipErrorInvalidValue;
         encode_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, slots, desc, partial,
                                                                 overflow, ctrl);
+        if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
+            return hipErrorInvalidValue;
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
             jobs, dmap, dstart, desc, dstatus, offsets, ctrl);
         place_kernel<<<(uint32_t)((tiles + kWaves - 1) / kWaves), kThreads, 0, stream>>>(

@@ -487,7 +487,8 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
 }
 
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                             uint64_t dtiles, bf16d_result *results, hipStream_t stream) {
+                             uint64_t dtiles, bf16d_result *results, hipStream_t stream,
+                             const bf16d_events *events) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const DecompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
@@ -511,7 +512,11 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
                                                                                count);
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
+        if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
+            return hipErrorInvalidValue;
         apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, state, map, offsets, partial);
+        if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
+            return hipErrorInvalidValue;
     }
     decompress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, state, partial, ctrl,
                                                                results);

@@ -414,7 +414,9 @@ void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint
                       uint64_t tiles, hipStream_t stream);
 void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                           uint64_t dtiles, bf16d_result *results, hipStream_t stream);
+                           uint64_t dtiles, bf16d_result *results, hipStream_t stream,
+                           const bf16d_events *events);
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
-                             uint64_t dtiles, bf16d_result *results, hipStream_t stream);
+                             uint64_t dtiles, bf16d_result *results, hipStream_t stream,
+                             const bf16d_events *events);
 }  // namespace bf16d
