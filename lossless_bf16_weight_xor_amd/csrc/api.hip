@@ -108,10 +108,10 @@ int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count, void *work
     std::vector<uint8_t> host(l.dtile_start + 8 * (size_t(count) + 1) - l.jobs, 0);
     auto *dj = reinterpret_cast<CompressJob *>(host.data());
     for (uint32_t j = 0; j < count; ++j) {
-        dj[j].src = jobs[j].src;
-        dj[j].dst = jobs[j].dst;
+        dj[j].src = (BF16D_GMEM const uint16_t *)jobs[j].src;
+        dj[j].dst = (BF16D_GMEM const uint16_t *)jobs[j].dst;
         dj[j].n = jobs[j].n;
-        dj[j].payload = jobs[j].payload;
+        dj[j].payload = (BF16D_GMEM uint8_t *)jobs[j].payload;
         dj[j].capacity = jobs[j].capacity;
         dj[j].block0 = start[j];
         dj[j].nb = start[j + 1] - start[j];
@@ -165,9 +165,9 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *
     std::vector<uint8_t> host(l.dtile_start + 8 * (size_t(count) + 1) - l.jobs, 0);
     auto *dj = reinterpret_cast<DecompressJob *>(host.data());
     for (uint32_t j = 0; j < count; ++j) {
-        dj[j].weights = jobs[j].weights;
+        dj[j].weights = (BF16D_GMEM uint16_t *)jobs[j].weights;
         dj[j].n = jobs[j].n;
-        dj[j].payload = jobs[j].payload;
+        dj[j].payload = (BF16D_GMEM const uint8_t *)jobs[j].payload;
         dj[j].payload_bytes = jobs[j].payload_bytes;
         dj[j].checksum = jobs[j].checksum;
         dj[j].block0 = bstart[j];

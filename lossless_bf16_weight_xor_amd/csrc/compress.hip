@@ -47,7 +47,7 @@ constexpr uint32_t kPosMantMax = kBlock / 8 + (7 * kBlock) / 8;   // 8192 bytes
 
 // Uniform (per-workgroup) description of one tile.
 struct TileRef {
-    const uint16_t *src, *dst;   // first element of the tile
+    BF16D_GMEM const uint16_t *src, *dst;   // first element of the tile
     uint64_t b;                  // block index within the job
     uint32_t L;                  // elements in this block
 };
@@ -63,16 +63,25 @@ __device__ __forceinline__ TileRef tile_ref(const CompressJob &job, uint64_t t) 
     return r;
 }
 
+// kFull (a whole block): eight unconditional 16-byte loads, all in flight
+// at once.  Otherwise (the short last block of a tensor) element by element
+// up to L, zero beyond.
+template <bool kFull>
 __device__ __forceinline__ void load_tile(const TileRef &t, uint4 (&o)[kChunksPerThread],
                                           uint4 (&nw)[kChunksPerThread]) {
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
         const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
-        o[i] = make_uint4(0, 0, 0, 0);
-        nw[i] = make_uint4(0, 0, 0, 0);
-        if (e0 < t.L) {
-            o[i] = load_chunk(t.src + e0, t.L - e0);
-            nw[i] = load_chunk(t.dst + e0, t.L - e0);
+        if (kFull) {
+            o[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(t.src + e0);
+            nw[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(t.dst + e0);
+        } else {
+            o[i] = make_uint4(0, 0, 0, 0);
+            nw[i] = make_uint4(0, 0, 0, 0);
+            if (e0 < t.L) {
+                o[i] = load_chunk(t.src + e0, t.L - e0);
+                nw[i] = load_chunk(t.dst + e0, t.L - e0);
+            }
         }
     }
 }
@@ -259,24 +268,20 @@ __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
 }
 
 // ------------------------------------------------------------------ encode ---
-// One workgroup per tile, no inter-workgroup waits.  Occupancy hides the
-// load latency: with 53 VGPRs and 18.8 KiB of LDS, eight workgroups fit on a
-// CU.  That measured faster than a persistent loop that keeps the next
-// tile's loads in registers at half the occupancy.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
-void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
-                   uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out,
-                   uint64_t *__restrict__ partial, uint32_t *__restrict__ overflow,
-                   Control *__restrict__ ctrl) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
-    __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
-    __shared__ EncodeShared sh;
-
+// One tile, from its loads to its slot.  Whole blocks and the short last
+// block of a tensor are compiled separately, so that all of a whole block's
+// loads are in flight together.
+template <bool kFull>
+__device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16_t *s_x,
+                                           uint32_t *s_rec, EncodeShared &sh,
+                                           uint8_t *__restrict__ slots,
+                                           uint32_t *__restrict__ desc_out,
+                                           uint64_t *__restrict__ partial,
+                                           uint32_t *__restrict__ overflow,
+                                           Control *__restrict__ ctrl) {
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t t = blockIdx.x;
-    const TileRef tr = tile_ref(jobs[tile_job[t]], t);
     uint4 o[kChunksPerThread], nw[kChunksPerThread];
-    load_tile(tr, o, nw);
+    load_tile<kFull>(tr, o, nw);
     // while the loads are in flight: clear the record, build the gap table
     for (uint32_t u = tid; u < kSlot / 4 + 4; u += kThreads) s_rec[u] = 0;
     init_gap_table(sh);
@@ -300,6 +305,26 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
     }
     if (lane == 0) partial[kWaves * t + wave] = acc;
     if (tid == 0) desc_out[t] = k.desc;
+}
+
+// One workgroup per tile, no inter-workgroup waits.  Occupancy hides the
+// load latency: with 53 VGPRs and 18.8 KiB of LDS, eight workgroups fit on a
+// CU.  That measured faster than a persistent loop that keeps the next
+// tile's loads in registers at half the occupancy.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
+void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
+                   uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out,
+                   uint64_t *__restrict__ partial, uint32_t *__restrict__ overflow,
+                   Control *__restrict__ ctrl) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
+    __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
+    __shared__ EncodeShared sh;
+    const uint64_t t = blockIdx.x;
+    const TileRef tr = tile_ref(jobs[tile_job[t]], t);
+    if (tr.L == kBlock)
+        encode_one<true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+    else
+        encode_one<false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
 }
 
 // ----------------------------------------------------------------- offsets ---
@@ -378,10 +403,10 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
     const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
     const uint32_t len = (code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8) +
                          (7 * c + 7) / 8 + 2 * r;
-    uint8_t *const pay = job.payload;
+    BF16D_GMEM uint8_t *const pay = job.payload;
     const uint64_t cap = job.capacity;
     if (lane == 0 && kHeader + 4 * b + 4 <= cap)
-        *reinterpret_cast<uint32_t *>(pay + kHeader + 4 * b) = d;
+        *reinterpret_cast<BF16D_GMEM uint32_t *>(pay + kHeader + 4 * b) = d;
     if (len > kSlot || len == 0) return;   // re-encoded elsewhere / nothing to copy
     const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + t * kSlot);
     const uint64_t D = kHeader + 4 * job.nb + offsets[t];
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
         const uint32_t v = sh ? ((hi << (8 * sh)) | (lo >> (32 - 8 * sh))) : hi;
         const uint64_t A = a0 + 4ull * u;
         if (A >= D && A + 4 <= D + len && A + 4 <= cap) {
-            *reinterpret_cast<uint32_t *>(pay + A) = v;
+            *reinterpret_cast<BF16D_GMEM uint32_t *>(pay + A) = v;
         } else {
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
@@ -426,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
         const CompressJob job = jobs[tile_job[t]];
         const TileRef tr = tile_ref(job, t);
         uint4 o[kChunksPerThread], nw[kChunksPerThread];
-        load_tile(tr, o, nw);
+        load_tile<false>(tr, o, nw);
         for (uint32_t u = tid; u < kPosMantMax / 4 + 4; u += kThreads) s_rec[u] = 0;
         TileFlags f;
         classify(tr, o, nw, s_x, f);
@@ -435,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
         or_fields<false>(s_rec, s_x, k);
         __syncthreads();
 
-        uint8_t *const pay = job.payload;
+        BF16D_GMEM uint8_t *const pay = job.payload;
         const uint64_t cap = job.capacity;
         const uint64_t D = kHeader + 4 * job.nb + offsets[t];
         const uint32_t pm = k.pb + k.mb;
@@ -448,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
             const uint32_t v = sh4 ? ((hi << (8 * sh4)) | (lo >> (32 - 8 * sh4))) : hi;
             const uint64_t A = a0 + 4ull * u;
             if (A >= D && A + 4 <= D + pm && A + 4 <= cap) {
-                *reinterpret_cast<uint32_t *>(pay + A) = v;
+                *reinterpret_cast<BF16D_GMEM uint32_t *>(pay + A) = v;
             } else {
 #pragma unroll
                 for (uint32_t q = 0; q < 4; ++q) {
@@ -467,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
             const uint64_t at = rare0 + 2 * kk;
             if (at + 2 <= cap) {
                 if ((at & 1) == 0) {
-                    *reinterpret_cast<uint16_t *>(pay + at) = (uint16_t)xs;
+                    *reinterpret_cast<BF16D_GMEM uint16_t *>(pay + at) = (uint16_t)xs;
                 } else {
                     pay[at] = (uint8_t)xs;
                     pay[at + 1] = (uint8_t)(xs >> 8);
@@ -512,8 +537,8 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     const uint64_t P = kHeader + 4 * job.nb + pos + mant + rare;
     const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
     if (status == BF16D_OK) {
-        uint32_t *h = reinterpret_cast<uint32_t *>(job.payload);
-        uint64_t *h64 = reinterpret_cast<uint64_t *>(job.payload);
+        BF16D_GMEM uint32_t *h = reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload);
+        BF16D_GMEM uint64_t *h64 = reinterpret_cast<BF16D_GMEM uint64_t *>(job.payload);
         h[0] = kMagicLo;
         h[1] = kMagicHi;
         h[2] = BF16D_FORMAT_VERSION;

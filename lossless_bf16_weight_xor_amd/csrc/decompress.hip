@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
         lens[k] = 0;
         if (!table_ok || d >= job.nb) continue;
         const uint32_t desc =
-            *reinterpret_cast<const uint32_t *>(job.payload + kHeader + 4 * d);
+            *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + kHeader + 4 * d);
         const uint32_t L = block_length(job.n, d);
         const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
         uint32_t pb;
@@ -134,8 +134,8 @@ __global__ void prepare_kernel(const DecompressJob *__restrict__ jobs,
     DecompressState *st = &state[j];
     bool ok = job.payload_bytes >= kHeader;
     if (ok) {
-        const uint32_t *h = reinterpret_cast<const uint32_t *>(job.payload);
-        const uint64_t *h64 = reinterpret_cast<const uint64_t *>(job.payload);
+        BF16D_GMEM const uint32_t *h = reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload);
+        BF16D_GMEM const uint64_t *h64 = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload);
         ok = h[0] == kMagicLo && h[1] == kMagicHi && h[2] == BF16D_FORMAT_VERSION &&
              h[3] == kBlock && h64[2] == job.n && job.payload_bytes >= kHeader + 4 * job.nb &&
              st->desc_bad == 0 && st->sum_c == h64[3] && st->sum_r == h64[4] &&
@@ -146,19 +146,59 @@ __global__ void prepare_kernel(const DecompressJob *__restrict__ jobs,
     st->state = ok ? kStateReady : kStateRejected;
 }
 
-// -------------------------------------------------------------------- apply ---
-// Records up to kStage bytes are staged in LDS; fields beyond are read from
-// HBM (only dense blocks have larger records).
-constexpr uint32_t kStage = 6144;
-constexpr uint32_t kStageWords = kStage / 4;
+// --------------------------------------------------------------------- plan ---
+// One thread per tile: gathers the tile's weight and record addresses and its
+// descriptor, so that an apply workgroup starts from one load.  Tiles of jobs
+// that were rejected get length 0 and are skipped.
+__global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
+                            const DecompressState *__restrict__ state,
+                            const uint64_t *__restrict__ start, uint32_t count,
+                            const uint64_t *__restrict__ offsets, ApplyPlan *__restrict__ plan,
+                            uint64_t tiles) {
+    for (uint64_t t = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; t < tiles;
+         t += (uint64_t)gridDim.x * blockDim.x) {
+        uint32_t lo = 0, hi = count;   // invariant: start[lo] <= t < start[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (start[mid] <= t) lo = mid; else hi = mid;
+        }
+        const DecompressJob &job = jobs[lo];
+        ApplyPlan p;
+        p.w = nullptr;
+        p.rec = nullptr;
+        p.desc = 0;
+        p.len_room = 0;
+        p.job = lo;
+        p.block = 0;
+        if (state[lo].state == kStateReady) {
+            const uint64_t b = t - job.block0;
+            const uint64_t D = kHeader + 4 * job.nb + offsets[t];
+            const uint64_t room = job.payload_bytes - D;   // prepare checked D <= payload_bytes
+            p.w = job.weights + b * kBlock;
+            p.rec = job.payload + D;
+            p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + kHeader + 4 * b);
+            p.len_room = block_length(job.n, b) | (uint32_t)(room < 0x3FFFFu ? room : 0x3FFFFu)
+                                                      << 14;
+            p.block = (uint32_t)b;
+        }
+        plan[t] = p;
+    }
+}
 
-// Bit reader over a record: bits [0, 8*kStage - 32) of the window come from
-// LDS; later bits come from the payload in global memory.
+// -------------------------------------------------------------------- apply ---
+// The first kStageChunks 16-byte words of the record window (which starts at
+// the 16-byte boundary at or before the record) are staged in LDS, one load
+// per thread; fields beyond are read from HBM (only dense blocks have such
+// long records).
+constexpr uint32_t kStageChunks = 252;
+constexpr uint32_t kStageWords = 4 * kStageChunks;
+
+// Bit reader over a record: window dwords [0, kStageWords - 1) come from LDS,
+// later ones from the payload in global memory.
 struct RecordBits {
-    const uint32_t *lds;        // staged dwords; window bit 0 = payload byte `a0`
-    const uint8_t *payload;
-    uint64_t a0;                // 4-aligned payload offset of the window
-    uint64_t payload_bytes;
+    const uint32_t *lds;        // staged dwords; window byte 0 = win[0]
+    BF16D_GMEM const uint8_t *win;   // 16-byte aligned start of the window
+    uint32_t room;              // payload bytes from win[0] to the end (capped)
     uint32_t rb0;               // window bit of record bit 0
 
     __device__ __forceinline__ uint32_t get(uint32_t bitpos, uint32_t width) const {
@@ -169,9 +209,9 @@ struct RecordBits {
             v = (uint64_t)lds[d] | ((uint64_t)lds[d + 1] << 32);
         } else {
             v = 0;
-            const uint64_t at = a0 + 4ull * d;
+            const uint32_t at = 4 * d;
             for (uint32_t t = 0; t < 8; ++t)
-                if (at + t < payload_bytes) v |= (uint64_t)payload[at + t] << (8 * t);
+                if (at + t < room) v |= (uint64_t)win[at + t] << (8 * t);
         }
         const uint64_t mask = (width >= 32) ? 0xFFFFFFFFull : ((1ull << width) - 1);
         return (uint32_t)((v >> sh) & mask);
@@ -179,61 +219,115 @@ struct RecordBits {
 };
 
 struct ApplyShared {
-    uint32_t a[kWaves], b[kWaves], c[kWaves];
+    uint32_t a[kWaves], b[kWaves], c[kWaves], f[kWaves];
 };
 
-// Decode tile `tile` of job `j` and XOR it onto the weights.  s_x must be
-// all zero on entry; it is all zero again on return.  kRollback: undo a
-// previous pass (same decode, no checksum).
-template <bool kRollback>
-__device__ __forceinline__ void apply_tile(const DecompressJob &job, uint32_t j, uint64_t tile,
-                                           DecompressState *__restrict__ state,
-                                           const uint64_t *__restrict__ offsets,
-                                           uint64_t *__restrict__ partial, uint16_t *s_x,
-                                           uint32_t *s_raw, ApplyShared &sa) {
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t b = tile - job.block0;
-    const uint64_t base = b * kBlock;
-    const uint32_t L = block_length(job.n, b);
+// OR of `v` over the workgroup; also a barrier.  (The library's
+// __syncthreads_or would take 256 more bytes of LDS.)
+__device__ __forceinline__ uint32_t block_any(uint32_t v, ApplyShared &sa) {
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t any = __ballot(v != 0) != 0;
+    if (lane == 0) sa.f[wave] = any;
+    __syncthreads();
+    uint32_t out = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kWaves; ++w) out |= sa.f[w];
+    return out;
+}
 
-    // old weights first: their latency overlaps the decode
-    uint4 o[kChunksPerThread];
+struct TileGeom {
+    uint32_t L, c, r, code, pb, mb, len, lead;
+    bool stage;   // this thread stages a 16-byte word of the record window
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe) {
+    TileGeom g;
+    g.L = pe.len_room & 0x3FFFu;
+    g.c = pe.desc & 0x3FFFu;
+    g.r = (pe.desc >> 14) & 0x3FFFu;
+    g.code = pe.desc >> 28;
+    g.pb = g.code == kCodeBitmap ? (g.L + 7) / 8 : (g.c * g.code + 7) / 8;
+    g.mb = (7 * g.c + 7) / 8;
+    g.len = g.pb + g.mb + 2 * g.r;
+    g.lead = (uint32_t)((uintptr_t)pe.rec & 15);
+    g.stage = threadIdx.x < kStageChunks && 16 * threadIdx.x < g.lead + g.len;
+    return g;
+}
+
+// This thread's 16-byte word of a tile's record window.  Every thread loads,
+// at an offset clamped to the last 16 bytes that lie wholly inside the
+// payload, under uniform branches only, so that the wait before the decode
+// can leave the later weight loads in flight.  fix_record_word then redoes,
+// byte by byte, the one word that crosses the payload's end.
+__device__ __forceinline__ uint4 load_record_word(const ApplyPlan &pe) {
+    const TileGeom g = tile_geom(pe);
+    const uint32_t room = g.lead + (pe.len_room >> 14);
+    if (g.L == 0 || room < 16) return make_uint4(0, 0, 0, 0);
+    const uint32_t lim = (room & ~15u) - 16;
+    const uint32_t off = 16 * threadIdx.x < lim ? 16 * threadIdx.x : lim;
+    return *reinterpret_cast<BF16D_GMEM const uint4 *>(pe.rec - g.lead + off);
+}
+
+__device__ __forceinline__ uint4 fix_record_word(const ApplyPlan &pe, uint4 rv) {
+    const uint32_t tid = threadIdx.x;
+    const TileGeom g = tile_geom(pe);
+    const uint32_t room = g.lead + (pe.len_room >> 14);
+    if (g.L == 0 || !g.stage || 16 * tid + 16 <= room) return rv;
+    BF16D_GMEM const uint8_t *win = pe.rec - g.lead;
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (uint32_t t = 0; t < 16; ++t)
+        if (16 * tid + t < room) w[t >> 2] |= (uint32_t)win[16 * tid + t] << (8 * (t & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// This thread's 4 chunks of old weights.  kFull (a whole block): four
+// unconditional 16-byte loads; otherwise (the short last block of a tensor)
+// element by element up to L, zero beyond.
+template <bool kFull>
+__device__ __forceinline__ void load_old(const ApplyPlan &pe, uint4 (&o)[kChunksPerThread]) {
+    const uint32_t L = pe.len_room & 0x3FFFu;
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-        const uint32_t e0 = 8 * (tid + kThreads * i);
-        o[i] = make_uint4(0, 0, 0, 0);
-        if (e0 < L) o[i] = load_chunk(job.weights + base + e0, L - e0);
-    }
-    const uint32_t desc = *reinterpret_cast<const uint32_t *>(job.payload + kHeader + 4 * b);
-    const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
-    const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
-    const uint32_t mb = (7 * c + 7) / 8;
-    const uint32_t len = pb + mb + 2 * r;
-    const uint64_t D = kHeader + 4 * job.nb + offsets[tile];
-
-    // stage the first kStage bytes of the record window
-    RecordBits rb;
-    rb.lds = s_raw;
-    rb.payload = job.payload;
-    rb.payload_bytes = job.payload_bytes;
-    rb.rb0 = 8 * (uint32_t)(D & 3);
-    rb.a0 = D & ~3ull;
-    {
-        const uint32_t nraw = (uint32_t)((D & 3) + len + 3) / 4 + 1;
-        const uint32_t n_stage = nraw < kStageWords + 4 ? nraw : kStageWords + 4;
-        for (uint32_t u = tid; u < n_stage; u += kThreads) {
-            const uint64_t A = rb.a0 + 4ull * u;
-            uint32_t v = 0;
-            if (A + 4 <= job.payload_bytes) {
-                v = *reinterpret_cast<const uint32_t *>(job.payload + A);
-            } else {
-                for (uint32_t t = 0; t < 4; ++t)
-                    if (A + t < job.payload_bytes) v |= (uint32_t)job.payload[A + t] << (8 * t);
-            }
-            s_raw[u] = v;
+        const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
+        if (kFull) {
+            o[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(pe.w + e0);
+        } else {
+            o[i] = make_uint4(0, 0, 0, 0);
+            if (e0 < L) o[i] = load_chunk(pe.w + e0, L - e0);
         }
     }
-    __syncthreads();   // record staged
+}
+
+__device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv, uint32_t *s_raw) {
+    if (tile_geom(pe).stage) reinterpret_cast<uint4 *>(s_raw)[threadIdx.x] = rv;
+}
+
+// Decode one tile and XOR it onto the weights.
+//   On entry: s_x is all zero and s_raw holds this tile's record window; both
+//   were written before this call by this workgroup, and this call's first
+//   barrier makes them visible.  On return s_x is all zero again.
+//   `next` / `rv_next`: the following tile and this thread's word of its
+//   record window, loaded by the caller before this call so that its latency
+//   overlaps the decode; it is written to s_raw once this tile's record has
+//   been read.
+//   kRollback: undo a previous pass (same decode, no checksum).
+template <bool kRollback>
+__device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o)[kChunksPerThread],
+                                            uint64_t tile, const ApplyPlan &next, uint4 rv_next,
+                                            DecompressState *__restrict__ state,
+                                            uint64_t *__restrict__ partial, uint16_t *s_x,
+                                            uint32_t *s_raw, ApplyShared &sa) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const TileGeom g = tile_geom(pe);
+    const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
+
+    RecordBits rb;
+    rb.lds = s_raw;
+    rb.win = pe.rec - g.lead;
+    rb.room = g.lead + (pe.len_room >> 14);
+    rb.rb0 = 8 * g.lead;
+
+    __syncthreads();   // record staged; s_x clear
 
     // ---- decode the record into s_x, checking that it is canonical ----
     const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
@@ -370,11 +464,12 @@ __device__ __forceinline__ void apply_tile(const DecompressJob &job, uint32_t j,
     }
     if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
         bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
-    bad = __syncthreads_or(bad);   // s_x complete
+    bad = block_any(bad, sa);   // s_x complete; every read of s_raw done
+    stage_record_word(next, rv_next, s_raw);
 
     // ---- new = old ^ tile; store only changed chunks; clear the tile ----
     uint64_t acc = 0;
-    const uint64_t kg0 = ((base >> 2) + 1 + 2 * tid) * kGamma;
+    const uint64_t kg0 = (((uint64_t)pe.block * kBlock >> 2) + 1 + 2 * tid) * kGamma;
     constexpr uint64_t kRoundKg = (uint64_t)(2 * kThreads) * kGamma;
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
@@ -387,10 +482,10 @@ __device__ __forceinline__ void apply_tile(const DecompressJob &job, uint32_t j,
         if (dirty) {
             reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
             if (!bad) {
-                nw = make_uint4(o[i].x ^ t.x, o[i].y ^ t.y, o[i].z ^ t.z, o[i].w ^ t.w);
-                uint16_t *dstp = job.weights + base + e0;
+                nw = make_uint4(nw.x ^ t.x, nw.y ^ t.y, nw.z ^ t.z, nw.w ^ t.w);
+                BF16D_GMEM uint16_t *dstp = pe.w + e0;
                 if (valid == 8) {
-                    *reinterpret_cast<uint4 *>(dstp) = nw;
+                    *reinterpret_cast<BF16D_GMEM uint4 *>(dstp) = nw;
                 } else {
                     for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
                 }
@@ -405,46 +500,106 @@ __device__ __forceinline__ void apply_tile(const DecompressJob &job, uint32_t j,
     if (!kRollback) {
         acc = wave_sum(acc);
         if (lane == 0) partial[kWaves * tile + wave] = acc;
-        if (tid == 0 && bad) atomicOr(&state[j].block_bad, 1u);
+        if (tid == 0 && bad) atomicOr(&state[pe.job].block_bad, 1u);
     }
 }
 
-// The apply pass: one workgroup per tile of the jobs that passed the
-// header and descriptor checks.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
-void apply_kernel(const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
-                  const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
+// A persistent pass over the tiles (used for the rollback); workgroup g takes tiles
+// g, g + G, g + 2G, ...  Per tile, the old weights are loaded first, then the
+// next tile's record word and the plan entry of the tile after it; the decode
+// runs while they are in flight.  LDS is kept at 20 KiB so that 8 workgroups
+// (8 waves per SIMD) fit on a CU.
+//   kRollback = false: every tile of every job that passed its checks.
+//   kRollback = true : only the tiles of jobs marked for rollback; the grid
+//                      exits at once when there are none.
+template <bool kRollback>
+__device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
+                                           DecompressState *__restrict__ state,
+                                           uint64_t *__restrict__ partial, uint64_t tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];        // dense XOR tile
+    __shared__ __attribute__((aligned(16))) uint32_t s_raw[kStageWords];  // staged record
+    __shared__ ApplyShared sa;
+    const uint64_t G = gridDim.x;
+    uint64_t t = blockIdx.x;
+    if (t >= tiles) return;
+    ApplyPlan none;
+    none.w = nullptr;
+    none.rec = nullptr;
+    none.desc = none.len_room = none.job = none.block = 0;
+    auto fetch = [&](uint64_t u) -> ApplyPlan {
+        if (u >= tiles) return none;
+        ApplyPlan p = plan[u];
+        if (kRollback && (p.len_room & 0x3FFFu) && state[p.job].rollback == 0) p = none;
+        return p;
+    };
+    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
+        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+    ApplyPlan pc = fetch(t);
+    ApplyPlan pn = fetch(t + G);
+    stage_record_word(pc, fix_record_word(pc, load_record_word(pc)), s_raw);
+    for (;;) {
+        const uint32_t L = pc.len_room & 0x3FFFu;
+        uint4 o[kChunksPerThread];
+        load_old<false>(pc, o);
+        const uint4 rv_next = fix_record_word(pn, load_record_word(pn));
+        const ApplyPlan pnn = fetch(t + 2 * G);
+        if (L)
+            finish_tile<kRollback>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa);
+        else
+            stage_record_word(pn, rv_next, s_raw);   // nothing read this tile's record
+        t += G;
+        if (t >= tiles) break;
+        pc = pn;
+        pn = pnn;
+    }
+}
+
+// One tile of the apply pass, from its loads to its stores.  Whole blocks
+// and the short last block of a tensor are compiled separately, so that the
+// wave waits only for the record word before the decode and the weight
+// loads stay in flight meanwhile.
+template <bool kFull>
+__device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
+                                          DecompressState *__restrict__ state,
+                                          uint64_t *__restrict__ partial, uint16_t *s_x,
+                                          uint32_t *s_raw, ApplyShared &sa) {
+    uint4 rv = load_record_word(pe);
+    uint4 o[kChunksPerThread];
+    load_old<kFull>(pe, o);
+    rv = fix_record_word(pe, rv);
+    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
+        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+    stage_record_word(pe, rv, s_raw);
+    ApplyPlan none;
+    none.w = nullptr;
+    none.rec = nullptr;
+    none.desc = none.len_room = none.job = none.block = 0;
+    finish_tile<false>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x, s_raw,
+                       sa);
+}
+
+// The apply pass: one workgroup per tile.  Its plan entry is the only load
+// before the record and the old weights are requested.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
                   uint64_t *__restrict__ partial) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];   // dense XOR tile
-    __shared__ uint32_t s_raw[kStageWords + 4];                       // staged record
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];        // dense XOR tile
+    __shared__ __attribute__((aligned(16))) uint32_t s_raw[kStageWords];  // staged record
     __shared__ ApplyShared sa;
     const uint64_t tile = blockIdx.x;
-    const uint32_t j = tile_job[tile];
-    if (state[j].state != kStateReady) return;
-    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
-        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
-    // (the barrier after staging orders this clearing before the decode)
-    apply_tile<false>(jobs[j], j, tile, state, offsets, partial, s_x, s_raw, sa);
+    const ApplyPlan pe = plan[tile];
+    const uint32_t L = pe.len_room & 0x3FFFu;
+    if (L == kBlock)
+        apply_one<true>(pe, tile, state, partial, s_x, s_raw, sa);
+    else if (L != 0)   // 0: the job was rejected
+        apply_one<false>(pe, tile, state, partial, s_x, s_raw, sa);
 }
 
-// The undo pass, for failed jobs only: a persistent grid that exits at once
-// when nothing failed.
-__global__ __launch_bounds__(kThreads) void rollback_kernel(
-    const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
-    const uint32_t *__restrict__ tile_job, const uint64_t *__restrict__ offsets,
-    const Control *__restrict__ ctrl, uint64_t tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
-    __shared__ uint32_t s_raw[kStageWords + 4];
-    __shared__ ApplyShared sa;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void rollback_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
+                     const Control *__restrict__ ctrl, uint64_t tiles) {
     if (ctrl->any_rollback == 0) return;
-    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
-        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
-    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const uint32_t j = tile_job[tile];
-        if (state[j].rollback == 0) continue;   // uniform across the workgroup
-        apply_tile<true>(jobs[j], j, tile, state, offsets, nullptr, s_x, s_raw, sa);
-        __syncthreads();   // LDS reused by the next tile
-    }
+    apply_pass<true>(plan, state, nullptr, tiles);
 }
 
 // ----------------------------------------------------------------- finalize ---
@@ -493,12 +648,12 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     auto *jobs = reinterpret_cast<const DecompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
     auto *dstart = reinterpret_cast<const uint64_t *>(ws + l.dtile_start);
-    auto *map = reinterpret_cast<uint32_t *>(ws + l.tile_job);
     auto *offsets = reinterpret_cast<uint64_t *>(ws + l.status);
     auto *partial = reinterpret_cast<uint64_t *>(ws + l.partial);
     auto *dmap = reinterpret_cast<uint32_t *>(ws + l.dtile_job);
     auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
     auto *state = reinterpret_cast<DecompressState *>(ws + l.state);
+    auto *plan = reinterpret_cast<ApplyPlan *>(ws + l.plan);
 
     launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
     launch_zero_words(reinterpret_cast<uint32_t *>(state),
@@ -511,10 +666,12 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     prepare_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(jobs, state,
                                                                                count);
     if (tiles) {
-        launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
+        const uint64_t g = (tiles + kThreads - 1) / kThreads;
+        plan_kernel<<<(uint32_t)(g < 4096 ? g : 4096), kThreads, 0, stream>>>(
+            jobs, state, bstart, count, offsets, plan, tiles);
         if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
             return hipErrorInvalidValue;
-        apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, state, map, offsets, partial);
+        apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(plan, state, partial);
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
     }
@@ -522,7 +679,7 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
                                                                results);
     if (tiles) {
         rollback_kernel<<<persistent_grid((const void *)rollback_kernel, tiles), kThreads, 0,
-                          stream>>>(jobs, state, map, offsets, ctrl, tiles);
+                          stream>>>(plan, state, ctrl, tiles);
     }
     return hipGetLastError();
 }

@@ -41,12 +41,22 @@ constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
 
+// Pointers into the caller's buffers, as device code sees them: global memory
+// (address space 1), so that accesses compile to global rather than flat
+// instructions and wait only on the vector-memory counter.  Host code sees
+// plain pointers of the same size.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define BF16D_GMEM __attribute__((address_space(1)))
+#else
+#define BF16D_GMEM
+#endif
+
 // ---- device-side job tables (copied into the workspace by the host) ---------
 struct alignas(64) CompressJob {
-    const uint16_t *src;
-    const uint16_t *dst;
+    BF16D_GMEM const uint16_t *src;
+    BF16D_GMEM const uint16_t *dst;
     uint64_t n;
-    uint8_t *payload;
+    BF16D_GMEM uint8_t *payload;
     uint64_t capacity;
     uint64_t block0;   // first global tile index of this job
     uint64_t nb;       // blocks of this job
@@ -56,9 +66,9 @@ struct alignas(64) CompressJob {
 enum JobState : uint32_t { kStateReady = 1, kStateRejected = 2 };
 
 struct alignas(64) DecompressJob {
-    uint16_t *weights;
+    BF16D_GMEM uint16_t *weights;
     uint64_t n;
-    const uint8_t *payload;
+    BF16D_GMEM const uint8_t *payload;
     uint64_t payload_bytes;
     uint64_t checksum;
     uint64_t block0;   // first global tile index
@@ -75,6 +85,19 @@ struct alignas(64) DecompressState {
     uint32_t rollback;     // the apply pass must be undone
 };
 
+// decompress: everything the apply pass needs about one tile, gathered once
+// by the plan kernel so that a workgroup starts with a single (scalar) load
+struct alignas(32) ApplyPlan {
+    BF16D_GMEM uint16_t *w;          // first weight of the block
+    BF16D_GMEM const uint8_t *rec;   // first byte of the block's record
+    uint32_t desc;        // the block's descriptor
+    uint32_t len_room;    // block length (bits 0..13; 0 = skip the tile) | payload bytes
+                          // left from `rec`, capped at 2^18 - 1 (bits 14..31)
+    uint32_t job;
+    uint32_t block;       // block index within the job
+};
+static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
+
 struct alignas(64) Control {
     uint32_t ticket;          // (unused) dynamic tile ids
     uint32_t dticket;         // dynamic tile ids for the descriptor-scan look-back
@@ -86,7 +109,7 @@ struct alignas(64) Control {
 // Workspace layout, computed identically by every entry point.
 struct Layout {
     size_t control, jobs, block_start, dtile_start, tile_job, status, partial, desc,
-        dtile_job, dstatus, state, slots, overflow, total;
+        dtile_job, dstatus, state, slots, overflow, plan, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -114,6 +137,7 @@ inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool 
     l.state = take(sizeof(DecompressState) * size_t(count));
     l.slots = take(compress ? size_t(kSlot) * tiles : 0);     // compress: record slots
     l.overflow = take(compress ? 4 * tiles : 0);              // compress: overflowing tiles
+    l.plan = take(compress ? 0 : sizeof(ApplyPlan) * tiles);  // decompress: per-tile plan
     l.total = off;
     return l;
 }
@@ -387,8 +411,8 @@ __device__ __forceinline__ uint32_t chunk_elem(const uint4 &v, int s) {
 }
 
 // Load 8 bf16 patterns at p, of which the first `valid` (<= 8) exist.
-__device__ __forceinline__ uint4 load_chunk(const uint16_t *p, uint32_t valid) {
-    if (valid >= 8) return *reinterpret_cast<const uint4 *>(p);
+__device__ __forceinline__ uint4 load_chunk(BF16D_GMEM const uint16_t *p, uint32_t valid) {
+    if (valid >= 8) return *reinterpret_cast<BF16D_GMEM const uint4 *>(p);
     uint32_t w[4] = {0, 0, 0, 0};
     for (uint32_t s = 0; s < valid; ++s) w[s >> 1] |= (uint32_t)p[s] << (16 * (s & 1));
     return make_uint4(w[0], w[1], w[2], w[3]);

@@ -86,8 +86,11 @@ def _mutate_mantissa(v: torch.Tensor, gen: torch.Generator) -> torch.Tensor:
                              dtype=torch.int32) * 2 - 1
         step = torch.empty(todo.numel(), device=v.device, dtype=torch.float32)
         step.geometric_(0.5, generator=gen)
-        cand = m[todo] + sign * step.to(torch.int32)
-        ok = (cand >= 0) & (cand <= 127)
+        k = step.to(torch.int32)
+        cand = m[todo] + sign * k
+        # geometric_ can return 0 when its uniform draw is exactly 1; that is
+        # outside the support {1, 2, ...} and is redrawn like a binade crossing
+        ok = (k >= 1) & (cand >= 0) & (cand <= 127)
         out[todo[ok]] = cand[ok]
         todo = todo[~ok]
     return (v & 0xFF80) | out
