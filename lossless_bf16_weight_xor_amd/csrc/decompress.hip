@@ -216,7 +216,25 @@ struct RecordBits {
         const uint64_t mask = (width >= 32) ? 0xFFFFFFFFull : ((1ull << width) - 1);
         return (uint32_t)((v >> sh) & mask);
     }
+
+    // `width` (<= 32) bits at `bitpos` of a record that lies wholly in the
+    // staged window.
+    __device__ __forceinline__ uint32_t get_staged(uint32_t bitpos, uint32_t width) const {
+        const uint32_t wb = rb0 + bitpos;
+        const uint32_t d = wb >> 5;
+        const uint32_t v = __builtin_amdgcn_alignbit(lds[d + 1], lds[d], wb & 31);
+        return width >= 32 ? v : v & ((1u << width) - 1);
+    }
 };
+
+// Bits [pos, pos + 32) of the 96-bit little-endian window w0 | w1 | w2
+// (pos < 96; bits past the window read as zero).
+__device__ __forceinline__ uint32_t window_bits(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                uint32_t pos) {
+    if (pos < 32) return __builtin_amdgcn_alignbit(w1, w0, pos);
+    if (pos < 64) return __builtin_amdgcn_alignbit(w2, w1, pos - 32);
+    return w2 >> (pos - 64);
+}
 
 struct ApplyShared {
     uint32_t a[kWaves], b[kWaves], c[kWaves], f[kWaves];
@@ -224,8 +242,8 @@ struct ApplyShared {
 
 // OR of `v` over the workgroup; also a barrier.  (The library's
 // __syncthreads_or would take 256 more bytes of LDS.)
-__device__ __forceinline__ uint32_t block_any(uint32_t v, ApplyShared &sa) {
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ uint32_t block_any(uint32_t v, ApplyShared &sa, uint32_t tid) {
+    const uint32_t lane = tid & 63, wave = tid >> 6;
     const uint32_t any = __ballot(v != 0) != 0;
     if (lane == 0) sa.f[wave] = any;
     __syncthreads();
@@ -240,7 +258,7 @@ struct TileGeom {
     bool stage;   // this thread stages a 16-byte word of the record window
 };
 
-__device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe) {
+__device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe, uint32_t tid) {
     TileGeom g;
     g.L = pe.len_room & 0x3FFFu;
     g.c = pe.desc & 0x3FFFu;
@@ -250,27 +268,31 @@ __device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe) {
     g.mb = (7 * g.c + 7) / 8;
     g.len = g.pb + g.mb + 2 * g.r;
     g.lead = (uint32_t)((uintptr_t)pe.rec & 15);
-    g.stage = threadIdx.x < kStageChunks && 16 * threadIdx.x < g.lead + g.len;
+    g.stage = tid < kStageChunks && 16 * tid < g.lead + g.len;
     return g;
 }
 
 // This thread's 16-byte word of a tile's record window.  Every thread loads,
-// at an offset clamped to the last 16 bytes that lie wholly inside the
-// payload, under uniform branches only, so that the wait before the decode
-// can leave the later weight loads in flight.  fix_record_word then redoes,
-// byte by byte, the one word that crosses the payload's end.
-__device__ __forceinline__ uint4 load_record_word(const ApplyPlan &pe) {
-    const TileGeom g = tile_geom(pe);
+// at an offset clamped to the record's last word and to the last 16 bytes
+// that lie wholly inside the payload, under uniform branches only, so that
+// the wait before the decode can leave the later weight loads in flight.
+// fix_record_word then redoes, byte by byte, the one word that crosses the
+// payload's end.
+__device__ __forceinline__ uint4 load_record_word(const ApplyPlan &pe, uint32_t tid) {
+    const TileGeom g = tile_geom(pe, tid);
     const uint32_t room = g.lead + (pe.len_room >> 14);
-    if (g.L == 0 || room < 16) return make_uint4(0, 0, 0, 0);
-    const uint32_t lim = (room & ~15u) - 16;
-    const uint32_t off = 16 * threadIdx.x < lim ? 16 * threadIdx.x : lim;
+    if (g.L == 0 || g.len == 0 || room < 16) return make_uint4(0, 0, 0, 0);
+    // threads past the record reload its last word (the same cache line), so
+    // the window costs no HBM traffic beyond the record
+    const uint32_t last = ((g.lead + g.len + 15) & ~15u) - 16;
+    const uint32_t lim0 = (room & ~15u) - 16;
+    const uint32_t lim = last < lim0 ? last : lim0;
+    const uint32_t off = 16 * tid < lim ? 16 * tid : lim;
     return *reinterpret_cast<BF16D_GMEM const uint4 *>(pe.rec - g.lead + off);
 }
 
-__device__ __forceinline__ uint4 fix_record_word(const ApplyPlan &pe, uint4 rv) {
-    const uint32_t tid = threadIdx.x;
-    const TileGeom g = tile_geom(pe);
+__device__ __forceinline__ uint4 fix_record_word(const ApplyPlan &pe, uint4 rv, uint32_t tid) {
+    const TileGeom g = tile_geom(pe, tid);
     const uint32_t room = g.lead + (pe.len_room >> 14);
     if (g.L == 0 || !g.stage || 16 * tid + 16 <= room) return rv;
     BF16D_GMEM const uint8_t *win = pe.rec - g.lead;
@@ -284,11 +306,12 @@ __device__ __forceinline__ uint4 fix_record_word(const ApplyPlan &pe, uint4 rv) 
 // unconditional 16-byte loads; otherwise (the short last block of a tensor)
 // element by element up to L, zero beyond.
 template <bool kFull>
-__device__ __forceinline__ void load_old(const ApplyPlan &pe, uint4 (&o)[kChunksPerThread]) {
+__device__ __forceinline__ void load_old(const ApplyPlan &pe, uint4 (&o)[kChunksPerThread],
+                                         uint32_t tid) {
     const uint32_t L = pe.len_room & 0x3FFFu;
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
-        const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
+        const uint32_t e0 = 8 * (tid + kThreads * i);
         if (kFull) {
             o[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(pe.w + e0);
         } else {
@@ -298,8 +321,99 @@ __device__ __forceinline__ void load_old(const ApplyPlan &pe, uint4 (&o)[kChunks
     }
 }
 
-__device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv, uint32_t *s_raw) {
-    if (tile_geom(pe).stage) reinterpret_cast<uint4 *>(s_raw)[threadIdx.x] = rv;
+__device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv, uint32_t *s_raw,
+                                                  uint32_t tid) {
+    if (tile_geom(pe, tid).stage) reinterpret_cast<uint4 *>(s_raw)[tid] = rv;
+}
+
+// Gap-list decode of a block with at most kFastFields fields per thread
+// whose record lies wholly in the staged window: thread t owns fields
+// [t*F, t*F + F), reads them from one window of three (gaps) and two
+// (mantissas) LDS dwords, keeps them in registers, and writes the XOR of
+// every changed element into s_x.  Returns this thread's share of `bad`.
+constexpr uint32_t kFastFields = 4;
+
+__device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint32_t c,
+                                                      uint32_t r, uint32_t w, uint32_t L,
+                                                      uint32_t mant0, uint32_t rare0,
+                                                      uint16_t *s_x, ApplyShared &sa,
+                                                      uint32_t tid) {
+    const uint32_t lane = tid & 63, wave = tid >> 6;
+    const uint32_t F = (c + kThreads - 1) / kThreads;
+    const uint32_t jb = tid * F < c ? tid * F : c;
+    const uint32_t nf = (jb + F < c ? jb + F : c) - jb;
+    uint32_t g0 = 0, g1 = 0, g2 = 0, m0 = 0, m1 = 0, gsh = 0, msh = 0;
+    if (nf) {
+        const uint32_t gb = rb.rb0 + jb * w, mb = rb.rb0 + mant0 + 7 * jb;
+        const uint32_t gd = gb >> 5, md = mb >> 5;
+        gsh = gb & 31;
+        msh = mb & 31;
+        g0 = rb.lds[gd];
+        g1 = rb.lds[gd + 1];
+        g2 = rb.lds[gd + 2];
+        m0 = rb.lds[md];
+        m1 = rb.lds[md + 1];
+    }
+    const uint32_t gmask = (1u << w) - 1;
+    uint32_t gk[kFastFields], mk[kFastFields];
+    uint32_t sum_g1 = 0, esc = 0, top = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kFastFields; ++k) {
+        gk[k] = window_bits(g0, g1, g2, gsh + k * w) & gmask;
+        const uint32_t mp = msh + 7 * k;
+        mk[k] = (mp < 32 ? __builtin_amdgcn_alignbit(m1, m0, mp) : m1 >> (mp - 32)) & kMant;
+        if (k < nf) {
+            sum_g1 += gk[k] + 1;
+            esc += mk[k] == 0;
+            top |= w ? gk[k] >> (w - 1) : 1u;   // the field uses its top bit
+        }
+    }
+    // escapes before this lane (esc <= 4): by bit planes of ballots
+    const uint64_t e1 = __ballot(esc & 1), e2 = __ballot(esc & 2), e4 = __ballot(esc & 4);
+    const uint64_t below = (1ull << lane) - 1;
+    const uint32_t e_lane = __popcll(e1 & below) + 2 * __popcll(e2 & below) +
+                            4 * __popcll(e4 & below);
+    const uint32_t e_wave = __popcll(e1) + 2 * __popcll(e2) + 4 * __popcll(e4);
+    const uint32_t inc_g = wave_incl_add(sum_g1);
+    const uint32_t top_wave = __ballot(top) != 0;
+    if (lane == 0) {
+        sa.a[wave] = lane63(inc_g);
+        sa.b[wave] = e_wave;
+        sa.c[wave] = top_wave;
+    }
+    __syncthreads();
+    uint32_t run = inc_g - sum_g1, e = e_lane;
+    uint32_t total_g1 = 0, esc_total = 0, any_top = 0;
+#pragma unroll
+    for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+        if (w2 < wave) {
+            run += sa.a[w2];
+            e += sa.b[w2];
+        }
+        total_g1 += sa.a[w2];
+        esc_total += sa.b[w2];
+        any_top |= sa.c[w2];
+    }
+    uint32_t bad = (total_g1 - 1 >= L) | (esc_total != r) | (any_top == 0);
+#pragma unroll
+    for (uint32_t k = 0; k < kFastFields; ++k) {
+        if (k < nf) {
+            run += gk[k] + 1;
+            const uint32_t p = run - 1;
+            uint32_t x = mk[k];
+            if (x == 0) {
+                if (e < r) {
+                    x = rb.get_staged(rare0 + 16 * e, 16);
+                    bad |= (x & kExpSign) == 0;
+                } else {
+                    bad = 1;
+                }
+                ++e;
+            }
+            if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
+        }
+    }
+    return bad;
 }
 
 // Decode one tile and XOR it onto the weights.
@@ -316,9 +430,9 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                                             uint64_t tile, const ApplyPlan &next, uint4 rv_next,
                                             DecompressState *__restrict__ state,
                                             uint64_t *__restrict__ partial, uint16_t *s_x,
-                                            uint32_t *s_raw, ApplyShared &sa) {
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const TileGeom g = tile_geom(pe);
+                                            uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
+    const uint32_t lane = tid & 63, wave = tid >> 6;
+    const TileGeom g = tile_geom(pe, tid);
     const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
 
     RecordBits rb;
@@ -327,160 +441,175 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     rb.room = g.lead + (pe.len_room >> 14);
     rb.rb0 = 8 * g.lead;
 
-    __syncthreads();   // record staged; s_x clear
-
     // ---- decode the record into s_x, checking that it is canonical ----
+    // A block without changes has an empty record (its descriptor was
+    // checked): nothing to decode and nothing to write.
+    const bool changed = c != 0;
     const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
     uint32_t bad = 0;
-    if (code == kCodeBitmap) {
-        // thread t owns bitmap bits [32t, 32t + 32) = elements 32t .. 32t+31
-        const uint32_t lo = 32 * tid, seg_end = 8 * pb;
-        uint32_t word = 0;
-        if (lo < seg_end) {
-            word = rb.get(lo, 32);
-            if (lo + 32 > seg_end) word &= (1u << (seg_end - lo)) - 1;
-        }
-        const uint32_t valid_mask =
-            lo + 32 <= L ? 0xFFFFFFFFu : (lo >= L ? 0u : (1u << (L - lo)) - 1);
-        bad |= (word & ~valid_mask) != 0;               // pad bits must be zero
-        word &= valid_mask;
-        const uint32_t pop = __popc(word);
-        const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
-        const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
-        if (lane == 0) {
-            sa.a[wave] = lane63(inc_pop);
-            sa.b[wave] = lane63(inc_last);
-        }
-        __syncthreads();
-        uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
-        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-            if (w2 < wave) {
-                rank0 += sa.a[w2];
-                prev1 = umax32(prev1, sa.b[w2]);
+    if (changed) {
+        __syncthreads();   // record staged; s_x clear
+        if (code != kCodeBitmap && c <= kFastFields * kThreads &&
+            g.lead + g.len + 12 <= 4 * kStageWords) {
+            bad = decode_delta_fast(rb, c, r, code, L, mant0, rare0, s_x, sa, tid);
+            if (tid == 0 && 8 * pb > c * code)               // position padding
+                bad |= rb.get(c * code, 8 * pb - c * code) != 0;
+        } else if (code == kCodeBitmap) {
+            // thread t owns bitmap bits [32t, 32t + 32) = elements 32t .. 32t+31
+            const uint32_t lo = 32 * tid, seg_end = 8 * pb;
+            uint32_t word = 0;
+            if (lo < seg_end) {
+                word = rb.get(lo, 32);
+                if (lo + 32 > seg_end) word &= (1u << (seg_end - lo)) - 1;
             }
-            total += sa.a[w2];
-        }
-        bad |= total != c;
-        // gaps before each set bit, and the escapes among this thread's fields
-        uint32_t maxg = 0, esc = 0;
-        {
-            uint32_t bits = word, jj = rank0, p1 = prev1;
+            const uint32_t valid_mask =
+                lo + 32 <= L ? 0xFFFFFFFFu : (lo >= L ? 0u : (1u << (L - lo)) - 1);
+            bad |= (word & ~valid_mask) != 0;               // pad bits must be zero
+            word &= valid_mask;
+            const uint32_t pop = __popc(word);
+            const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
+            const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
+            if (lane == 0) {
+                sa.a[wave] = lane63(inc_pop);
+                sa.b[wave] = lane63(inc_last);
+            }
+            __syncthreads();
+            uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) {
+                    rank0 += sa.a[w2];
+                    prev1 = umax32(prev1, sa.b[w2]);
+                }
+                total += sa.a[w2];
+            }
+            bad |= total != c;
+            // gaps before each set bit, and the escapes among this thread's fields
+            uint32_t maxg = 0, esc = 0;
+            {
+                uint32_t bits = word, jj = rank0, p1 = prev1;
+                while (bits) {
+                    const uint32_t p = lo + __ffs(bits) - 1;
+                    bits &= bits - 1;
+                    maxg = umax32(maxg, p - p1);
+                    p1 = p + 1;
+                    esc += rb.get(mant0 + 7 * jj, 7) == 0;
+                    ++jj;
+                }
+            }
+            const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
+            __syncthreads();   // sa.a / sa.b reads done
+            if (lane == 0) {
+                sa.a[wave] = lane63(inc_esc);
+                sa.c[wave] = wmax;
+            }
+            __syncthreads();
+            uint32_t e = inc_esc - esc, esc_total = 0;
+            maxg = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) e += sa.a[w2];
+                esc_total += sa.a[w2];
+                maxg = umax32(maxg, sa.c[w2]);
+            }
+            bad |= esc_total != r;
+            bad |= !(pb < (c * bit_length(maxg) + 7) / 8);   // a bitmap only when smaller
+            uint32_t bits = word, jj = rank0;
             while (bits) {
                 const uint32_t p = lo + __ffs(bits) - 1;
                 bits &= bits - 1;
-                maxg = umax32(maxg, p - p1);
-                p1 = p + 1;
-                esc += rb.get(mant0 + 7 * jj, 7) == 0;
+                uint32_t x = rb.get(mant0 + 7 * jj, 7);
+                if (x == 0) {
+                    if (e < r) {
+                        x = rb.get(rare0 + 16 * e, 16);
+                        bad |= (x & kExpSign) == 0;
+                    } else {
+                        bad = 1;
+                    }
+                    ++e;
+                }
+                s_x[p] = (uint16_t)x;
                 ++jj;
             }
-        }
-        const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
-        __syncthreads();   // sa.a / sa.b reads done
-        if (lane == 0) {
-            sa.a[wave] = lane63(inc_esc);
-            sa.c[wave] = wmax;
-        }
-        __syncthreads();
-        uint32_t e = inc_esc - esc, esc_total = 0;
-        maxg = 0;
-        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-            if (w2 < wave) e += sa.a[w2];
-            esc_total += sa.a[w2];
-            maxg = umax32(maxg, sa.c[w2]);
-        }
-        bad |= esc_total != r;
-        bad |= !(pb < (c * bit_length(maxg) + 7) / 8);   // a bitmap only when smaller
-        uint32_t bits = word, jj = rank0;
-        while (bits) {
-            const uint32_t p = lo + __ffs(bits) - 1;
-            bits &= bits - 1;
-            uint32_t x = rb.get(mant0 + 7 * jj, 7);
-            if (x == 0) {
-                if (e < r) {
-                    x = rb.get(rare0 + 16 * e, 16);
-                    bad |= (x & kExpSign) == 0;
-                } else {
-                    bad = 1;
+        } else {
+            // gap list of width w: thread t owns fields [t*F, t*F + F)
+            const uint32_t w = code;
+            const uint32_t F = (c + kThreads - 1) / kThreads;
+            const uint32_t jb = tid * F < c ? tid * F : c;
+            const uint32_t je = jb + F < c ? jb + F : c;
+            uint32_t sum_g1 = 0, esc = 0, maxg = 0;
+            for (uint32_t jj = jb; jj < je; ++jj) {
+                const uint32_t g = w ? rb.get(jj * w, w) : 0;
+                sum_g1 += g + 1;
+                maxg = umax32(maxg, g);
+                esc += rb.get(mant0 + 7 * jj, 7) == 0;
+            }
+            const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
+            const uint32_t wmax = lane63(wave_incl_max(maxg));
+            if (lane == 0) {
+                sa.a[wave] = lane63(inc_g);
+                sa.b[wave] = lane63(inc_e);
+                sa.c[wave] = wmax;
+            }
+            __syncthreads();
+            uint32_t run = inc_g - sum_g1, e = inc_e - esc;
+            uint32_t total_g1 = 0, esc_total = 0;
+            maxg = 0;
+            for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+                if (w2 < wave) {
+                    run += sa.a[w2];
+                    e += sa.b[w2];
                 }
-                ++e;
+                total_g1 += sa.a[w2];
+                esc_total += sa.b[w2];
+                maxg = umax32(maxg, sa.c[w2]);
             }
-            s_x[p] = (uint16_t)x;
-            ++jj;
-        }
-    } else {
-        // gap list of width w: thread t owns fields [t*F, t*F + F)
-        const uint32_t w = code;
-        const uint32_t F = (c + kThreads - 1) / kThreads;
-        const uint32_t jb = tid * F < c ? tid * F : c;
-        const uint32_t je = jb + F < c ? jb + F : c;
-        uint32_t sum_g1 = 0, esc = 0, maxg = 0;
-        for (uint32_t jj = jb; jj < je; ++jj) {
-            const uint32_t g = w ? rb.get(jj * w, w) : 0;
-            sum_g1 += g + 1;
-            maxg = umax32(maxg, g);
-            esc += rb.get(mant0 + 7 * jj, 7) == 0;
-        }
-        const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
-        const uint32_t wmax = lane63(wave_incl_max(maxg));
-        if (lane == 0) {
-            sa.a[wave] = lane63(inc_g);
-            sa.b[wave] = lane63(inc_e);
-            sa.c[wave] = wmax;
-        }
-        __syncthreads();
-        uint32_t run = inc_g - sum_g1, e = inc_e - esc;
-        uint32_t total_g1 = 0, esc_total = 0;
-        maxg = 0;
-        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-            if (w2 < wave) {
-                run += sa.a[w2];
-                e += sa.b[w2];
-            }
-            total_g1 += sa.a[w2];
-            esc_total += sa.b[w2];
-            maxg = umax32(maxg, sa.c[w2]);
-        }
-        bad |= (c > 0) && (total_g1 - 1 >= L);          // last position inside the block
-        bad |= esc_total != r;
-        bad |= bit_length(maxg) != w;                    // width is minimal
-        for (uint32_t jj = jb; jj < je; ++jj) {
-            const uint32_t g = w ? rb.get(jj * w, w) : 0;
-            run += g + 1;
-            const uint32_t p = run - 1;
-            uint32_t x = rb.get(mant0 + 7 * jj, 7);
-            if (x == 0) {
-                if (e < r) {
-                    x = rb.get(rare0 + 16 * e, 16);
-                    bad |= (x & kExpSign) == 0;
-                } else {
-                    bad = 1;
+            bad |= (c > 0) && (total_g1 - 1 >= L);          // last position inside the block
+            bad |= esc_total != r;
+            bad |= bit_length(maxg) != w;                    // width is minimal
+            for (uint32_t jj = jb; jj < je; ++jj) {
+                const uint32_t g = w ? rb.get(jj * w, w) : 0;
+                run += g + 1;
+                const uint32_t p = run - 1;
+                uint32_t x = rb.get(mant0 + 7 * jj, 7);
+                if (x == 0) {
+                    if (e < r) {
+                        x = rb.get(rare0 + 16 * e, 16);
+                        bad |= (x & kExpSign) == 0;
+                    } else {
+                        bad = 1;
+                    }
+                    ++e;
                 }
-                ++e;
+                if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
             }
-            if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
+            if (tid == 0 && 8 * pb > c * w)                  // position padding
+                bad |= rb.get(c * w, 8 * pb - c * w) != 0;
         }
-        if (tid == 0 && 8 * pb > c * w)                  // position padding
-            bad |= rb.get(c * w, 8 * pb - c * w) != 0;
+        if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
+            bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
+        bad = block_any(bad, sa, tid);   // s_x complete; every read of s_raw done
     }
-    if (tid == 0 && 8 * mb > 7 * c)                      // mantissa padding
-        bad |= rb.get(mant0 + 7 * c, 8 * mb - 7 * c) != 0;
-    bad = block_any(bad, sa);   // s_x complete; every read of s_raw done
-    stage_record_word(next, rv_next, s_raw);
+    stage_record_word(next, rv_next, s_raw, tid);
 
     // ---- new = old ^ tile; store only changed chunks; clear the tile ----
     uint64_t acc = 0;
-    const uint64_t kg0 = (((uint64_t)pe.block * kBlock >> 2) + 1 + 2 * tid) * kGamma;
-    constexpr uint64_t kRoundKg = (uint64_t)(2 * kThreads) * kGamma;
+    uint64_t kg = (((uint64_t)pe.block * kBlock >> 2) + 1 + 2 * tid) * kGamma;
+    // per-round key step and G as opaque uniform values: kept in SGPRs rather
+    // than folded into per-chunk 64-bit constants held in VGPRs
+    uint64_t round_kg = (uint64_t)(2 * kThreads) * kGamma, gamma = kGamma;
+    asm volatile("" : "+s"(round_kg), "+s"(gamma));
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
         const uint32_t q = tid + kThreads * i;
         const uint32_t e0 = 8 * q;
         const uint32_t valid = e0 < L ? (L - e0 < 8 ? L - e0 : 8) : 0;
-        const uint4 t = reinterpret_cast<const uint4 *>(s_x)[q];
+        const uint4 t = changed ? reinterpret_cast<const uint4 *>(s_x)[q] : make_uint4(0, 0, 0, 0);
         const bool dirty = (t.x | t.y | t.z | t.w) != 0;
         uint4 nw = o[i];
         if (dirty) {
-            reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
+            // tid >> 16 is 0; written so the zero is not one more register
+            // held across the persistent loop
+            const uint32_t z = tid >> 16;
+            reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(z, z, z, z);
             if (!bad) {
                 nw = make_uint4(nw.x ^ t.x, nw.y ^ t.y, nw.z ^ t.z, nw.w ^ t.w);
                 BF16D_GMEM uint16_t *dstp = pe.w + e0;
@@ -492,9 +621,9 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
             }
         }
         if (!kRollback) {
-            const uint64_t kg = kg0 + i * kRoundKg;
             if (valid > 0) acc += mix64(((uint64_t)nw.y << 32 | nw.x) ^ kg);
-            if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + kGamma));
+            if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + gamma));
+            kg += round_kg;
         }
     }
     if (!kRollback) {
@@ -504,14 +633,29 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     }
 }
 
-// A persistent pass over the tiles (used for the rollback); workgroup g takes tiles
-// g, g + G, g + 2G, ...  Per tile, the old weights are loaded first, then the
-// next tile's record word and the plan entry of the tile after it; the decode
-// runs while they are in flight.  LDS is kept at 20 KiB so that 8 workgroups
-// (8 waves per SIMD) fit on a CU.
+// One step of the persistent pass: tile `pc` (its record already staged in
+// s_raw) from its weight loads to its stores, with the next tile's record
+// word loaded meanwhile.  Whole blocks and the short last block of a tensor
+// are compiled separately (see load_old).
+template <bool kRollback, bool kFull>
+__device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &pn, uint64_t t,
+                                          DecompressState *__restrict__ state,
+                                          uint64_t *__restrict__ partial, uint16_t *s_x,
+                                          uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
+    uint4 o[kChunksPerThread];
+    load_old<kFull>(pc, o, tid);
+    const uint4 rv_next = fix_record_word(pn, load_record_word(pn, tid), tid);
+    finish_tile<kRollback>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa, tid);
+}
+
+// A persistent pass over the tiles (the rollback); workgroup g takes tiles
+// g, g + G, g + 2G, ...  While a tile is decoded, its old weights and the next tile's
+// record word are in flight, and the plan entry of the tile after that has
+// been requested; the next tile's record is staged in LDS as soon as this
+// one's has been read, so its decode can start at once.  LDS is kept at
+// 20 KiB so that 8 workgroups (8 waves per SIMD) fit on a CU.
 //   kRollback = false: every tile of every job that passed its checks.
-//   kRollback = true : only the tiles of jobs marked for rollback; the grid
-//                      exits at once when there are none.
+//   kRollback = true : only the tiles of jobs marked for rollback.
 template <bool kRollback>
 __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
                                            DecompressState *__restrict__ state,
@@ -536,17 +680,24 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
         reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
     ApplyPlan pc = fetch(t);
     ApplyPlan pn = fetch(t + G);
-    stage_record_word(pc, fix_record_word(pc, load_record_word(pc)), s_raw);
+    {
+        const uint32_t tid = threadIdx.x;
+        stage_record_word(pc, fix_record_word(pc, load_record_word(pc, tid), tid), s_raw, tid);
+    }
     for (;;) {
-        const uint32_t L = pc.len_room & 0x3FFFu;
-        uint4 o[kChunksPerThread];
-        load_old<false>(pc, o);
-        const uint4 rv_next = fix_record_word(pn, load_record_word(pn));
+        // the thread index, opaque to the optimiser once per tile: values
+        // derived from it are recomputed per tile instead of being hoisted
+        // out of the loop and held in registers
+        uint32_t tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
         const ApplyPlan pnn = fetch(t + 2 * G);
-        if (L)
-            finish_tile<kRollback>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa);
-        else
-            stage_record_word(pn, rv_next, s_raw);   // nothing read this tile's record
+        const uint32_t L = pc.len_room & 0x3FFFu;
+        if (L == kBlock)
+            pass_step<kRollback, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        else if (L != 0)
+            pass_step<kRollback, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        else   // a skipped tile: nothing reads its record
+            stage_record_word(pn, fix_record_word(pn, load_record_word(pn, tid), tid), s_raw, tid);
         t += G;
         if (t >= tiles) break;
         pc = pn;
@@ -555,31 +706,38 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
 }
 
 // One tile of the apply pass, from its loads to its stores.  Whole blocks
-// and the short last block of a tensor are compiled separately, so that the
-// wave waits only for the record word before the decode and the weight
-// loads stay in flight meanwhile.
+// and the short last block of a tensor are compiled separately (see
+// load_old), so that the wave waits only for the record word before the
+// decode while the weight loads stay in flight.
 template <bool kFull>
 __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
                                           DecompressState *__restrict__ state,
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
                                           uint32_t *s_raw, ApplyShared &sa) {
-    uint4 rv = load_record_word(pe);
+    const uint32_t tid = threadIdx.x;
+    uint4 rv = load_record_word(pe, tid);
     uint4 o[kChunksPerThread];
-    load_old<kFull>(pe, o);
-    rv = fix_record_word(pe, rv);
-    for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
-        reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
-    stage_record_word(pe, rv, s_raw);
+    load_old<kFull>(pe, o, tid);
+    rv = fix_record_word(pe, rv, tid);
+    if (pe.desc & 0x3FFFu) {   // changed elements: the decode needs a clear tile
+        for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
+            reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+        stage_record_word(pe, rv, s_raw, tid);
+    }
     ApplyPlan none;
     none.w = nullptr;
     none.rec = nullptr;
     none.desc = none.len_room = none.job = none.block = 0;
     finish_tile<false>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x, s_raw,
-                       sa);
+                       sa, tid);
 }
 
-// The apply pass: one workgroup per tile.  Its plan entry is the only load
-// before the record and the old weights are requested.
+// The apply pass: one workgroup per tile, 8 workgroups per CU (20 KiB of
+// LDS).  Its plan entry is the only load before the record and the old
+// weights are requested.  Variants that keep a workgroup for several tiles
+// and fetch the next tile's record during the current decode (a persistent
+// loop, or 2 and 3 tiles per workgroup) measured slower on the 7B-shaped
+// checkpoint: the pass is bound by HBM traffic, not by the decode latency.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
                   uint64_t *__restrict__ partial) {
