@@ -333,7 +333,8 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
 __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
     const uint64_t *__restrict__ dstart, const uint32_t *__restrict__ desc,
-    uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets, Control *__restrict__ ctrl) {
+    uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets,
+    PlaceEntry *__restrict__ place, Control *__restrict__ ctrl) {
     __shared__ uint32_t s_tmp[kWaves];
     __shared__ uint32_t s_dt;
     __shared__ uint64_t s_excl;
@@ -348,14 +349,16 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     const uint64_t first = dstart[j];
     const uint64_t ld = dt - first;
 
-    uint32_t lens[kDescPerThread];
+    uint32_t lens[kDescPerThread], descs[kDescPerThread];
     uint32_t mine = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kDescPerThread; ++k) {
         const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
         lens[k] = 0;
+        descs[k] = 0;
         if (b >= job.nb) continue;
         const uint32_t d = desc[job.block0 + b];
+        descs[k] = d;
         const uint64_t left = job.n - b * kBlock;
         const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
         const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
@@ -374,58 +377,89 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
         }
     }
     __syncthreads();
+    // offsets, the descriptor table, and where each slot's record goes
     uint64_t off = s_excl + excl;
+    const uint64_t cap = job.capacity;
 #pragma unroll
     for (uint32_t k = 0; k < kDescPerThread; ++k) {
         const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
-        if (b < job.nb) offsets[job.block0 + b] = off;
+        if (b < job.nb) {
+            offsets[job.block0 + b] = off;
+            if (kHeader + 4 * b + 4 <= cap)
+                *reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload + kHeader + 4 * b) = descs[k];
+            const uint64_t rel = kHeader + 4 * job.nb + off;
+            const uint32_t len = lens[k];
+            PlaceEntry e;
+            e.dst = job.payload + rel;
+            e.len = (len > kSlot || rel >= cap) ? 0u
+                                                 : (uint32_t)(cap - rel < len ? cap - rel : len);
+            e.pad = 0;
+            place[job.block0 + b] = e;
+        }
         off += lens[k];
     }
 }
 
 // ------------------------------------------------------------------- place ---
-// One wave per tile: descriptor into the table, slot into the data region.
-// Every byte of a record belongs to one tile, and stores never reach
-// `capacity`; the dwords a record shares with its neighbours are written
-// byte by byte.
-__global__ __launch_bounds__(kThreads) void place_kernel(
-    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
-    const uint8_t *__restrict__ slots, const uint32_t *__restrict__ desc,
-    const uint64_t *__restrict__ offsets, uint64_t tiles) {
+// Slot -> payload.  Each wave copies kPlaceTiles records: all their slot
+// words are requested before the first store, so enough bytes are in flight
+// per wave.  Lane u of round m produces payload dword u + 64m of a record
+// from slot dwords i - 1 and i (the record's byte offset within a dword is
+// fixed per record); the dwords a record shares with its neighbours, and
+// anything past `capacity`, are written byte by byte or not at all.
+constexpr uint32_t kPlaceTiles = 4;
+constexpr uint32_t kPlaceRounds = kSlot / 256;   // 64 lanes x 4 bytes per round
+
+__global__ __launch_bounds__(kThreads) void place_kernel(const PlaceEntry *__restrict__ place,
+                                                         const uint8_t *__restrict__ slots,
+                                                         uint64_t tiles) {
     const uint32_t lane = threadIdx.x & 63;
-    const uint64_t t = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (t >= tiles) return;
-    const CompressJob job = jobs[tile_job[t]];
-    const uint64_t b = t - job.block0;
-    const uint64_t left = job.n - b * kBlock;
-    const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
-    const uint32_t d = desc[t];
-    const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
-    const uint32_t len = (code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8) +
-                         (7 * c + 7) / 8 + 2 * r;
-    BF16D_GMEM uint8_t *const pay = job.payload;
-    const uint64_t cap = job.capacity;
-    if (lane == 0 && kHeader + 4 * b + 4 <= cap)
-        *reinterpret_cast<BF16D_GMEM uint32_t *>(pay + kHeader + 4 * b) = d;
-    if (len > kSlot || len == 0) return;   // re-encoded elsewhere / nothing to copy
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + t * kSlot);
-    const uint64_t D = kHeader + 4 * job.nb + offsets[t];
-    const uint32_t sh = (uint32_t)(D & 3);
-    const uint64_t a0 = D - sh;
-    const uint32_t words = (sh + len + 3) / 4;
-    const uint32_t src_words = (len + 3) / 4;
-    for (uint32_t u = lane; u < words; u += 64) {
-        const uint32_t hi = u < src_words ? src[u] : 0u;
-        const uint32_t lo = (u && u - 1 < src_words) ? src[u - 1] : 0u;
-        const uint32_t v = sh ? ((hi << (8 * sh)) | (lo >> (32 - 8 * sh))) : hi;
-        const uint64_t A = a0 + 4ull * u;
-        if (A >= D && A + 4 <= D + len && A + 4 <= cap) {
-            *reinterpret_cast<BF16D_GMEM uint32_t *>(pay + A) = v;
-        } else {
+    const uint64_t t0 = ((uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kPlaceTiles;
+    if (t0 >= tiles) return;   // whole wave; the kernel has no barriers
+    uint4 e = make_uint4(0, 0, 0, 0);
+    if (lane < kPlaceTiles && t0 + lane < tiles)
+        e = *reinterpret_cast<const uint4 *>(place + t0 + lane);
+    // a record of up to kSlot bytes at a byte offset of 1..3 spans one payload
+    // dword more than its slot: the extra round reads nothing
+    uint32_t rec[kPlaceTiles][kPlaceRounds + 1];
 #pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) {
-                const uint64_t at = A + k;
-                if (at >= D && at < D + len && at < cap) pay[at] = (uint8_t)(v >> (8 * k));
+    for (uint32_t k = 0; k < kPlaceTiles; ++k) {
+        const uint32_t len = (uint32_t)__builtin_amdgcn_readlane((int)e.z, k);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + (t0 + k) * kSlot);
+#pragma unroll
+        for (uint32_t m = 0; m < kPlaceRounds; ++m) {
+            rec[k][m] = 0;
+            if (256 * m < len && 4 * (lane + 64 * m) < len) rec[k][m] = src[lane + 64 * m];
+        }
+        rec[k][kPlaceRounds] = 0;
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kPlaceTiles; ++k) {
+        const uint32_t len = (uint32_t)__builtin_amdgcn_readlane((int)e.z, k);
+        if (len == 0) continue;
+        const uint64_t D = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e.x, k) |
+                           (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e.y, k) << 32;
+        const uint32_t sh = (uint32_t)(D & 3);
+        BF16D_GMEM uint8_t *const a0 = reinterpret_cast<BF16D_GMEM uint8_t *>(D - sh);
+        const uint32_t nout = (sh + len + 3) / 4;
+        const uint32_t last_hi = ((sh + len - 1) & 3) + 1;   // valid bytes of the last dword
+#pragma unroll
+        for (uint32_t m = 0; m <= kPlaceRounds; ++m) {
+            if (256 * m >= sh + len) continue;
+            const uint32_t cur = rec[k][m];
+            uint32_t prev = wave_shr1(cur);
+            if (lane == 0)
+                prev = m ? (uint32_t)__builtin_amdgcn_readlane((int)rec[k][m > 0 ? m - 1 : 0], 63)
+                         : 0u;
+            const uint32_t v = sh ? __builtin_amdgcn_alignbyte(cur, prev, 4 - sh) : cur;
+            const uint32_t i = lane + 64 * m;
+            if (i < nout) {
+                const uint32_t lo = i == 0 ? sh : 0, hi = i == nout - 1 ? last_hi : 4;
+                if (lo == 0 && hi == 4) {
+                    *reinterpret_cast<BF16D_GMEM uint32_t *>(a0 + 4 * i) = v;
+                } else {
+                    for (uint32_t q = lo; q < hi; ++q) a0[4 * i + q] = (uint8_t)(v >> (8 * q));
+                }
             }
         }
     }
@@ -576,6 +610,7 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
     auto *slots = ws + l.slots;
     auto *overflow = reinterpret_cast<uint32_t *>(ws + l.overflow);
+    auto *place = reinterpret_cast<PlaceEntry *>(ws + l.plan);
 
     launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
     if (tiles) {
@@ -588,9 +623,10 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
-            jobs, dmap, dstart, desc, dstatus, offsets, ctrl);
-        place_kernel<<<(uint32_t)((tiles + kWaves - 1) / kWaves), kThreads, 0, stream>>>(
-            jobs, map, slots, desc, offsets, tiles);
+            jobs, dmap, dstart, desc, dstatus, offsets, place, ctrl);
+        const uint64_t per_block = (uint64_t)kWaves * kPlaceTiles;
+        place_kernel<<<(uint32_t)((tiles + per_block - 1) / per_block), kThreads, 0, stream>>>(
+            place, slots, tiles);
         reencode_kernel<<<persistent_grid((const void *)reencode_kernel, tiles), kThreads, 0,
                           stream>>>(jobs, map, overflow, offsets, ctrl);
     }

@@ -98,6 +98,16 @@ struct alignas(32) ApplyPlan {
 };
 static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
 
+// compress: where one tile's record goes, written by the offsets kernel for
+// the place kernel
+struct alignas(16) PlaceEntry {
+    BF16D_GMEM uint8_t *dst;   // first byte of the record in the payload
+    uint32_t len;              // bytes to copy from the slot: 0 if none (empty, re-encoded
+                               // elsewhere, or past the capacity), else cut at the capacity
+    uint32_t pad;
+};
+static_assert(sizeof(PlaceEntry) == 16, "PlaceEntry is one 16-byte word");
+
 struct alignas(64) Control {
     uint32_t ticket;          // (unused) dynamic tile ids
     uint32_t dticket;         // dynamic tile ids for the descriptor-scan look-back
@@ -137,7 +147,8 @@ inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool 
     l.state = take(sizeof(DecompressState) * size_t(count));
     l.slots = take(compress ? size_t(kSlot) * tiles : 0);     // compress: record slots
     l.overflow = take(compress ? 4 * tiles : 0);              // compress: overflowing tiles
-    l.plan = take(compress ? 0 : sizeof(ApplyPlan) * tiles);  // decompress: per-tile plan
+    // per-tile plan: compress, where each record goes (PlaceEntry); decompress, ApplyPlan
+    l.plan = take(compress ? sizeof(PlaceEntry) * tiles : sizeof(ApplyPlan) * tiles);
     l.total = off;
     return l;
 }
