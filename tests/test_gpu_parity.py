@@ -82,6 +82,35 @@ def test_change_rates_span_both_position_encodings(rate):
     _check_pair(src, dst, f"rate={rate}")
 
 
+def _two_block_pair(p0, c1, r1):
+    """Block 0: one mantissa change at p0 (or none); block 1: c1 changes 8 apart,
+    the first r1 of them also flipping an exponent bit."""
+    n = 2 * 8192
+    old = np.full(n, 0x3F80, dtype=np.uint16)
+    new = old.copy()
+    if p0 is not None:
+        new[p0] ^= 0x0001
+    pos = 8192 + 8 * np.arange(c1)
+    new[pos] ^= 0x0001
+    new[pos[:r1]] ^= 0x0100
+    return old, new
+
+
+# Block 1's record is 2046..2048 bytes (the largest that goes through the
+# 2 KiB slot) and block 0's record (0..3 bytes) puts it at every byte offset
+# within a dword: the copy then spans one dword more than the slot.
+@pytest.mark.parametrize("p0", [None, 0, 1, 300])
+@pytest.mark.parametrize("c1,r1", [(1000, 399), (1003, 396), (1000, 398)])
+def test_largest_slot_records_at_every_byte_offset(p0, c1, r1):
+    old, new = _two_block_pair(p0, c1, r1)
+    payload, _, _ = oracle.compress(old, new)
+    lens = [pv.record_bytes(int(d), pv.block_len(old.size, b))
+            for b, d in enumerate(pv.descriptors(payload, old.size))]
+    assert lens[1] in (2046, 2047, 2048), lens
+    assert (pv.data_offset(old.size) + lens[0]) % 4 == {None: 0, 0: 1, 1: 2, 300: 3}[p0]
+    _check_pair(to_device(old, DEV), to_device(new, DEV), f"p0={p0} c1={c1} r1={r1}")
+
+
 def test_all_rare_changes():
     n = 5 * 8192 + 1
     src, _ = pair((n,), "0", synth.MIX_DEFAULT, 5, DEV)
