@@ -21,6 +21,9 @@ Reported:
   decompress: GB/s of weights, and % of HBM peak on algorithmic bytes (2n + P + 2c)
   roofline  : the encode kernel (the dominant kernel of a step) against 8 TB/s,
               timed with events recorded around it on its stream
+  streamed_receiver : the same decompress with the payloads in pinned host
+              memory, copied in layer by layer while the previous layer is
+              applied (PCIe-inclusive; context, not `value`)
   cpu_baseline : the CPU oracle on a bounded sample of the same workload
 
 Only one GPU is used; --gpus above 1 is refused.
@@ -105,6 +108,72 @@ def measured_traffic():
         return None
 
 
+def layer_groups(names, layers_per_group=1):
+    """Sizes of the groups of consecutive tensors: each transformer layer is a
+    unit, and so is every tensor outside the layers; a group holds
+    `layers_per_group` units."""
+    keys = [".".join(n.split(".")[:2]) if n.startswith("layers.") else n for n in names]
+    units = []
+    for i, k in enumerate(keys):
+        if i and k == keys[i - 1]:
+            units[-1] += 1
+        else:
+            units.append(1)
+    return [sum(units[i:i + layers_per_group]) for i in range(0, len(units), layers_per_group)]
+
+
+def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_group):
+    """The streamed receiver: payloads in pinned host memory, applied layer by
+    layer through two device slots while the next layer's payloads are copied
+    in.  Reported next to the device-resident numbers, never as `value`."""
+    dev = pairs[0][0].device
+    host = bd.StreamedDecompress.pin_packed([p.cpu() for p in payloads])
+    groups = layer_groups(names, layers_per_group)
+    recv = [s.clone() for s, _ in pairs]
+    sd = bd.StreamedDecompress(list(zip(recv, host, cs_new)), groups)
+    # the host-to-device copy of every payload byte on its own
+    P = sum(h.numel() for h in host)
+    flat = torch.empty(P, dtype=torch.uint8).pin_memory()
+    at = 0
+    for h in host:
+        flat[at:at + h.numel()].copy_(h)
+        at += h.numel()
+    dbuf = torch.empty(P, dtype=torch.uint8, device=dev)
+    t_h2d, t_str = [], []
+    direction = 0
+    warm = 2
+    for i in range(steps + warm):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        dbuf.copy_(flat, non_blocking=True)
+        e[1].record()
+        cs = cs_new if direction == 0 else cs_old
+        for j in range(len(cs)):
+            sd.jobs[j].checksum = cs[j]
+        e[2].record()
+        sd.run()
+        e[3].record()
+        torch.cuda.synchronize()
+        assert all(r["status"] == bd.OK for r in sd.results()), "streamed decompress failed"
+        direction ^= 1
+        if i >= warm:
+            t_h2d.append(e[0].elapsed_time(e[1]) / 1e3)
+            t_str.append(e[2].elapsed_time(e[3]) / 1e3)
+    for w, (s, d) in zip(recv, pairs):
+        ref = d if direction == 1 else s
+        assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "streamed not bit-exact"
+    n = sum(s.numel() for s, _ in pairs)
+    ts, th = float(np.median(t_str)), float(np.median(t_h2d))
+    slot = sd.slot_bytes
+    del recv, sd, dbuf
+    return {"layers_per_group": layers_per_group, "groups": len(groups), "slot_bytes": slot,
+            "ms": round(1e3 * ts, 4),
+            "gbps_weights_pcie_inclusive": round(2 * n / ts / 1e9, 2),
+            "h2d_payload_ms": round(1e3 * th, 4), "h2d_gbps": round(P / th / 1e9, 2),
+            "device_resident_decompress_ms": round(1e3 * td, 4),
+            "overlap": round((th + td) / ts, 3)}
+
+
 def cpu_baseline(pairs, gpu_payloads, budget_s: float):
     """The CPU oracle, single-threaded, timed on a bounded sample of the
     workload's tensors, walking from the last tensor back.  Each oracle
@@ -157,6 +226,8 @@ def main():
     ap.add_argument("--limit", type=int, default=None, help="first N tensors only (debug)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")
+    ap.add_argument("--no-streamed", action="store_true",
+                    help="skip the streamed receiver (payloads in pinned host memory)")
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -266,6 +337,11 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    stream_info = None
+    if not args.no_streamed:
+        stream_info = [streamed(bd, names, pairs, payloads, cs_new, cs_old, 5, td, lpg)
+                       for lpg in (1, 4)]
+
     gpu_payloads = [None] * len(pairs)
     cpu = None
     if args.cpu_budget > 0:
@@ -307,6 +383,7 @@ def main():
                                 "achieved": round(dec_alg / t_app / 1e9, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
+        "streamed_receiver": stream_info,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

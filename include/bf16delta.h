@@ -210,6 +210,63 @@ int bf16d_delta_decompress(uint16_t *src_inout, uint64_t n,
                            void *workspace, size_t workspace_bytes,
                            bf16d_result *result, hipStream_t stream);
 
+/* Streamed receiver: payloads in host memory, applied layer by layer.
+ *
+ * The double-buffered pipeline of "GPU-accelerated Weight Teleportation",
+ * sections "Overlapping DE and SM" and "Assembling the weight teleporter":
+ * the payloads wait in host memory, and the model is streamed through two
+ * device slots, one group of tensors (a layer) at a time, so that the copy
+ * of one group overlaps the in-place apply of the previous one and only two
+ * groups' payloads are ever on the device.  Here the copies are host-to-
+ * device DMA transfers on `copy`, and the applies are bf16d_decompress
+ * calls on `compute`.
+ *
+ * One tensor of such a call:
+ *   weights       : device, 16-byte aligned, n elements (as in
+ *                   bf16d_decompress_job).
+ *   payload       : host memory, payload_bytes bytes.  Pinned memory
+ *                   (hipHostMalloc, or a pinned torch tensor) lets the copy
+ *                   run asynchronously; pageable memory is correct but makes
+ *                   the copies synchronous with the host.  It must stay valid
+ *                   and unchanged until `compute` has completed the call.
+ *   checksum      : as in bf16d_decompress_job. */
+typedef struct bf16d_stream_job {
+    uint16_t      *weights;
+    uint64_t       n;
+    const uint8_t *payload;
+    uint64_t       payload_bytes;
+    uint64_t       checksum;
+} bf16d_stream_job;
+
+/* Apply `count` host-resident payloads in place, streamed in `groups`
+ * groups.  Group g holds jobs [group_end[g-1], group_end[g]) (group_end[-1]
+ * is 0); group_end must increase strictly and end at count.
+ *   staging      : device, 16-byte aligned, 2 * slot_bytes bytes: slot 0 at
+ *                  staging, slot 1 at staging + slot_bytes.  slot_bytes must be
+ *                  a multiple of 16.  Group g's payloads are packed into slot
+ *                  g % 2, each at a 16-byte boundary; every group must fit.
+ *   workspace    : device, 16-byte aligned, at least
+ *                  bf16d_workspace_bytes(sum of n, count) bytes; one
+ *                  workspace serves every group, in stream order.
+ *   results      : results[j] for job j, as in bf16d_decompress.
+ *   compute      : stream of the applies; the call's work on `copy` starts
+ *                  only after the work enqueued on `compute` before the call,
+ *                  and results are valid once `compute` has completed.
+ *   copy         : stream of the copies (may equal `compute`, which makes the
+ *                  pipeline serial).  Both streams must be of the same device.
+ * Consecutive payloads of a group that lie in host memory exactly as they are
+ * packed in the slot (each at the next 16-byte boundary after the previous
+ * one) are copied with a single transfer, padding included. */
+ * Returns BF16D_EINVAL (nothing enqueued) for bad arguments, BF16D_EHIP if a
+ * runtime call fails.  Per-job statuses and the weights' final state are
+ * those of bf16d_decompress; a failed job does not affect the others. */
+int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
+                              const uint32_t *group_end, uint32_t groups,
+                              void *staging, size_t slot_bytes,
+                              void *workspace, size_t workspace_bytes,
+                              bf16d_result *results,
+                              hipStream_t compute, hipStream_t copy);
+
 /* Human-readable name of a status code (static storage). */
 const char *bf16d_status_string(int status);
 

@@ -28,7 +28,7 @@ FORMAT = "bf16delta_v1"
 _ALIGN = 256   # payload slots inside an arena start on this boundary
 
 __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_batch",
-           "CompressBatch", "DecompressBatch", "FormatError", "ChecksumError",
+           "CompressBatch", "DecompressBatch", "StreamedDecompress", "FormatError", "ChecksumError",
            "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
 
 
@@ -194,6 +194,74 @@ class DecompressBatch:
                                                self.ws_bytes, self.result_buf.data_ptr(),
                                                _stream(self.device), ev)
         _check_rc(rc, "bf16d_decompress")
+
+    def results(self) -> list[dict]:
+        return _results(self.result_buf, self.count)
+
+
+class StreamedDecompress:
+    """A prepared streamed receiver (bf16d_decompress_streamed): payloads in
+    pinned host memory, applied in place group by group through two device
+    slots, the copies on a stream of their own.
+
+    items  : (weights device tensor, payload host uint8 tensor, checksum);
+             pin the payloads (torch's pin_memory) for the copies to overlap.
+    groups : number of jobs in each group, in order (for a model, a layer).
+    The device slots are sized for the largest group."""
+
+    def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
+                 groups: Sequence[int]):
+        if not items or not groups or sum(groups) != len(items) or min(groups) <= 0:
+            raise ValueError("groups must be positive and cover every item")
+        self.device = items[0][0].device
+        self.count = len(items)
+        self.items = list(items)   # keep the tensors alive
+        self.jobs = (_native.StreamJob * self.count)()
+        pad16 = lambda b: (b + 15) // 16 * 16
+        for j, (w, p, cs) in enumerate(items):
+            if p.device.type != "cpu" or p.dtype != torch.uint8 or not p.is_contiguous():
+                raise TypeError("payloads must be contiguous uint8 tensors in host memory")
+            self.jobs[j] = _native.StreamJob(_weights_ptr(w, "weights"), w.numel(),
+                                             p.data_ptr() if p.numel() else None, p.numel(),
+                                             int(cs) & 0xFFFFFFFFFFFFFFFF)
+        ends, at, slot = [], 0, 16
+        for g in groups:
+            slot = max(slot, sum(pad16(self.items[j][1].numel()) for j in range(at, at + g)))
+            at += g
+            ends.append(at)
+        self.groups = len(ends)
+        self.group_end = (ctypes.c_uint32 * self.groups)(*ends)
+        self.slot_bytes = pad16(slot)
+        self.staging = torch.empty(2 * self.slot_bytes, dtype=torch.uint8, device=self.device)
+        self.ws_bytes = workspace_bytes(sum(w.numel() for w, _, _ in items), self.count)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
+                                      device=self.device)
+        self.copy_stream = torch.cuda.Stream(device=self.device)
+
+    @staticmethod
+    def pin_packed(payloads: Sequence[torch.Tensor]) -> list[torch.Tensor]:
+        """Copies of `payloads` packed into one pinned host buffer, each at the
+        next 16-byte boundary: the layout in which a group's payloads are
+        copied to the device with one transfer."""
+        pad16 = lambda b: (b + 15) // 16 * 16
+        total = sum(pad16(p.numel()) for p in payloads)
+        flat = torch.empty(max(total, 16), dtype=torch.uint8).pin_memory()
+        out, at = [], 0
+        for p in payloads:
+            view = flat[at:at + p.numel()]
+            view.copy_(p.reshape(-1).view(torch.uint8))
+            out.append(view)
+            at += pad16(p.numel())
+        return out
+
+    def run(self) -> None:
+        """Enqueue the call on the current stream (copies on self.copy_stream)."""
+        rc = _native.lib().bf16d_decompress_streamed(
+            self.jobs, self.count, self.group_end, self.groups, self.staging.data_ptr(),
+            self.slot_bytes, self.workspace.data_ptr(), self.ws_bytes,
+            self.result_buf.data_ptr(), _stream(self.device), self.copy_stream.cuda_stream)
+        _check_rc(rc, "bf16d_decompress_streamed")
 
     def results(self) -> list[dict]:
         return _results(self.result_buf, self.count)

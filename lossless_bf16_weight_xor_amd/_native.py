@@ -20,8 +20,8 @@ FORMAT_VERSION = 1
 
 EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress",
             "bf16d_decompress", "bf16d_compress_ex", "bf16d_decompress_ex",
-            "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_status_string",
-            "bf16d_format_version")
+            "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_decompress_streamed",
+            "bf16d_status_string", "bf16d_format_version")
 
 
 class Result(ctypes.Structure):
@@ -37,6 +37,12 @@ class CompressJob(ctypes.Structure):
 
 
 class DecompressJob(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_void_p), ("n", ctypes.c_uint64),
+                ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64),
+                ("checksum", ctypes.c_uint64)]
+
+
+class StreamJob(ctypes.Structure):
     _fields_ = [("weights", ctypes.c_void_p), ("n", ctypes.c_uint64),
                 ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64),
                 ("checksum", ctypes.c_uint64)]
@@ -79,6 +85,10 @@ def lib():
         L.bf16d_decompress_ex.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp, vp,
                                           ctypes.POINTER(Events)]
         L.bf16d_decompress_ex.restype = ctypes.c_int
+        L.bf16d_decompress_streamed.argtypes = [ctypes.POINTER(StreamJob), u32,
+                                                ctypes.POINTER(ctypes.c_uint32), u32, vp, sz, vp,
+                                                sz, vp, vp, vp]
+        L.bf16d_decompress_streamed.restype = ctypes.c_int
         L.bf16d_delta_compress.argtypes = [vp, vp, u64, vp, u64, vp, sz, vp, vp]
         L.bf16d_delta_compress.restype = ctypes.c_int
         L.bf16d_delta_decompress.argtypes = [vp, u64, vp, u64, u64, vp, sz, vp, vp]

@@ -51,6 +51,49 @@ int upload(void *ws, const std::vector<uint8_t> &host, size_t at, hipStream_t st
 
 }  // namespace
 
+namespace bf16d {
+
+int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p) {
+    p.bstart.assign(size_t(count) + 1, 0);
+    p.dstart.assign(size_t(count) + 1, 0);
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_decompress_job &J = jobs[j];
+        if (J.n > 0 && (!J.weights || !aligned16(J.weights))) return BF16D_EINVAL;
+        // an empty payload may be NULL; it is then rejected on the device as too short
+        if ((J.payload_bytes > 0 && !J.payload) || !aligned16(J.payload)) return BF16D_EINVAL;
+        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        const uint64_t nb = blocks_of(J.n);
+        p.bstart[j + 1] = p.bstart[j] + nb;
+        p.dstart[j + 1] = p.dstart[j] + (nb + kDescTile - 1) / kDescTile;
+    }
+    p.tiles = p.bstart[count];
+    p.dtiles = p.dstart[count];
+    return p.tiles >= kMaxTiles ? BF16D_EINVAL : BF16D_OK;
+}
+
+size_t decompress_table_bytes(const Layout &l, uint32_t count) {
+    return l.dtile_start + 8 * (size_t(count) + 1) - l.jobs;
+}
+
+void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
+                      const Layout &l, uint8_t *out) {
+    auto *dj = reinterpret_cast<DecompressJob *>(out);
+    for (uint32_t j = 0; j < count; ++j) {
+        dj[j].weights = (BF16D_GMEM uint16_t *)jobs[j].weights;
+        dj[j].n = jobs[j].n;
+        dj[j].payload = (BF16D_GMEM const uint8_t *)jobs[j].payload;
+        dj[j].payload_bytes = jobs[j].payload_bytes;
+        dj[j].checksum = jobs[j].checksum;
+        dj[j].block0 = p.bstart[j];
+        dj[j].nb = p.bstart[j + 1] - p.bstart[j];
+        dj[j].dtile0 = p.dstart[j];
+    }
+    std::memcpy(out + (l.block_start - l.jobs), p.bstart.data(), 8 * p.bstart.size());
+    std::memcpy(out + (l.dtile_start - l.jobs), p.dstart.data(), 8 * p.dstart.size());
+}
+
+}  // namespace bf16d
+
 extern "C" {
 
 uint64_t bf16d_max_payload_bytes(uint64_t n) {
@@ -64,7 +107,9 @@ size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
     const uint64_t tiles = blocks_of(total_n) + count;
     const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
     const size_t c = make_layout(tiles, dtiles, count, true).total;
-    const size_t d = make_layout(tiles, dtiles, count, false).total;
+    // decompress; the streamed form also keeps every group's job table (at
+    // most 1024 bytes per job with alignment) after the decompress layout
+    const size_t d = make_layout(tiles, dtiles, count, false).total + 256 + 1024 * size_t(count);
     return c > d ? c : d;
 }
 
@@ -137,49 +182,30 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *
                         const bf16d_events *events) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
-    std::vector<uint64_t> bstart(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
+    DecompressPrep prep;
+    int rc = decompress_prep(jobs, count, prep);
+    if (rc != BF16D_OK) return rc;
+    const Layout l = make_layout(prep.tiles, prep.dtiles, count, false);
+    if (workspace_bytes < l.total) return BF16D_EINVAL;
     std::vector<Range> ranges;
     ranges.reserve(2 * size_t(count) + 1);
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_decompress_job &J = jobs[j];
-        if (J.n > 0 && (!J.weights || !aligned16(J.weights))) return BF16D_EINVAL;
-        // an empty payload may be NULL; it is then rejected on the device as too short
-        if ((J.payload_bytes > 0 && !J.payload) || !aligned16(J.payload)) return BF16D_EINVAL;
-        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
-        const uint64_t nb = blocks_of(J.n);
-        bstart[j + 1] = bstart[j] + nb;
-        dstart[j + 1] = dstart[j] + (nb + kDescTile - 1) / kDescTile;
         ranges.push_back({reinterpret_cast<uintptr_t>(J.weights),
                           reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n, true});
         ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
                           reinterpret_cast<uintptr_t>(J.payload) + J.payload_bytes, false});
     }
-    const uint64_t tiles = bstart[count], dtiles = dstart[count];
-    if (tiles >= kMaxTiles) return BF16D_EINVAL;
-    const Layout l = make_layout(tiles, dtiles, count, false);
-    if (workspace_bytes < l.total) return BF16D_EINVAL;
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + l.total, true});
     if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
 
-    std::vector<uint8_t> host(l.dtile_start + 8 * (size_t(count) + 1) - l.jobs, 0);
-    auto *dj = reinterpret_cast<DecompressJob *>(host.data());
-    for (uint32_t j = 0; j < count; ++j) {
-        dj[j].weights = (BF16D_GMEM uint16_t *)jobs[j].weights;
-        dj[j].n = jobs[j].n;
-        dj[j].payload = (BF16D_GMEM const uint8_t *)jobs[j].payload;
-        dj[j].payload_bytes = jobs[j].payload_bytes;
-        dj[j].checksum = jobs[j].checksum;
-        dj[j].block0 = bstart[j];
-        dj[j].nb = bstart[j + 1] - bstart[j];
-        dj[j].dtile0 = dstart[j];
-    }
-    std::memcpy(host.data() + (l.block_start - l.jobs), bstart.data(), 8 * bstart.size());
-    std::memcpy(host.data() + (l.dtile_start - l.jobs), dstart.data(), 8 * dstart.size());
-    int rc = upload(workspace, host, l.jobs, stream);
+    std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
+    decompress_table(jobs, count, prep, l, host.data());
+    rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
-    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
-                             stream, events) == hipSuccess
+    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, prep.tiles, prep.dtiles,
+                             results, stream, events) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "bf16delta.h"
 
 namespace bf16d {
@@ -443,6 +445,18 @@ __device__ __forceinline__ uint64_t chunk_checksum(const uint4 &v, uint64_t e, u
 
 // ---- kernel launchers (defined in the .hip files) ------------------------------
 namespace bf16d {
+// host side of a decompress call (api.hip): checks the jobs and lays out the
+// job table; decompress_table writes the bytes [l.jobs, l.dtile_start +
+// 8 * (count + 1)) of the workspace as they must be uploaded
+struct DecompressPrep {
+    std::vector<uint64_t> bstart, dstart;   // first tile / descriptor tile of each job
+    uint64_t tiles = 0, dtiles = 0;
+};
+int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p);
+size_t decompress_table_bytes(const Layout &l, uint32_t count);
+void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
+                      const Layout &l, uint8_t *out);
+
 // workgroups of a persistent kernel: as many as fit on the device at once
 uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds = 0);
 void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,

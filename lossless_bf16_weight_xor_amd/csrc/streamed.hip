@@ -1,0 +1,174 @@
+// streamed.hip -- the streamed receiver: host-resident payloads applied in
+// place group by group through two device slots.
+//
+// The double-buffered pipeline of "GPU-accelerated Weight Teleportation",
+// sections "Overlapping DE and SM" and "Assembling the weight teleporter",
+// on MI355X: the DMA engines copy group g's payloads into slot g % 2 on the
+// copy stream while the CUs apply group g - 1 from the other slot on the
+// compute stream.  Events order each copy after the apply that last read its
+// slot, and each apply after its copy.  Everything is validated before any
+// work is enqueued.
+#include <algorithm>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace bf16d;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+uint64_t align16(uint64_t v) { return (v + 15) & ~uint64_t(15); }
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+// The device ranges written by the call (weights, both slots, workspace) may
+// not overlap.
+bool spans_disjoint(std::vector<Span> v) {
+    v.erase(std::remove_if(v.begin(), v.end(), [](const Span &s) { return s.hi <= s.lo; }),
+            v.end());
+    std::sort(v.begin(), v.end(), [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < v.size(); ++i)
+        if (v[i].lo < v[i - 1].hi) return false;
+    return true;
+}
+
+struct Events {
+    hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, applied[2] = {nullptr, nullptr};
+    bool ok = true;
+    Events() {
+        ok = hipEventCreateWithFlags(&start, hipEventDisableTiming) == hipSuccess;
+        for (int s = 0; s < 2 && ok; ++s)
+            ok = hipEventCreateWithFlags(&copied[s], hipEventDisableTiming) == hipSuccess &&
+                 hipEventCreateWithFlags(&applied[s], hipEventDisableTiming) == hipSuccess;
+    }
+    ~Events() {
+        // an event still pending in a stream is released once it completes
+        if (start) (void)hipEventDestroy(start);
+        for (int s = 0; s < 2; ++s) {
+            if (copied[s]) (void)hipEventDestroy(copied[s]);
+            if (applied[s]) (void)hipEventDestroy(applied[s]);
+        }
+    }
+};
+
+}  // namespace
+
+extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
+                                         const uint32_t *group_end, uint32_t groups,
+                                         void *staging, size_t slot_bytes, void *workspace,
+                                         size_t workspace_bytes, bf16d_result *results,
+                                         hipStream_t compute, hipStream_t copy) {
+    if (!jobs || count == 0 || !group_end || groups == 0 || groups > count || !staging ||
+        !aligned16(staging) || slot_bytes == 0 || slot_bytes % 16 != 0 || !workspace ||
+        !aligned16(workspace) || !results)
+        return BF16D_EINVAL;
+    // groups partition [0, count) in order; each group's payloads fit a slot.
+    // Each group's decompress jobs point into its slot.
+    std::vector<bf16d_decompress_job> dj(count);
+    std::vector<uint64_t> offset(count, 0);
+    std::vector<Span> spans;
+    spans.reserve(size_t(count) + 3);
+    uint32_t first = 0;
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t end = group_end[g];
+        if (end <= first || end > count || (g + 1 == groups && end != count)) return BF16D_EINVAL;
+        uint8_t *slot = static_cast<uint8_t *>(staging) + (g % 2) * slot_bytes;
+        uint64_t packed = 0;
+        for (uint32_t j = first; j < end; ++j) {
+            const bf16d_stream_job &J = jobs[j];
+            if (J.payload_bytes > 0 && !J.payload) return BF16D_EINVAL;
+            if (J.payload_bytes > slot_bytes) return BF16D_EINVAL;
+            offset[j] = packed;
+            packed += align16(J.payload_bytes);
+            dj[j] = {J.weights, J.n, slot + offset[j], J.payload_bytes, J.checksum};
+            spans.push_back({reinterpret_cast<uintptr_t>(J.weights),
+                             reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n});
+        }
+        if (packed > slot_bytes) return BF16D_EINVAL;
+        first = end;
+    }
+    // every group's job table, laid out as its decompress call expects, all
+    // uploaded at once after the largest group's workspace layout
+    std::vector<DecompressPrep> prep(groups);
+    std::vector<Layout> lay(groups);
+    std::vector<size_t> table_at(groups);
+    size_t base = 0, tables = 0;
+    first = 0;
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t end = group_end[g], cnt = end - first;
+        if (decompress_prep(dj.data() + first, cnt, prep[g]) != BF16D_OK) return BF16D_EINVAL;
+        lay[g] = make_layout(prep[g].tiles, prep[g].dtiles, cnt, false);
+        base = std::max(base, lay[g].total);
+        table_at[g] = tables;
+        tables += align_up(decompress_table_bytes(lay[g], cnt), 256);
+        first = end;
+    }
+    base = align_up(base, 256);
+    const size_t need = base + tables;
+    if (workspace_bytes < need) return BF16D_EINVAL;
+    spans.push_back({reinterpret_cast<uintptr_t>(staging),
+                     reinterpret_cast<uintptr_t>(staging) + 2 * slot_bytes});
+    spans.push_back({reinterpret_cast<uintptr_t>(workspace),
+                     reinterpret_cast<uintptr_t>(workspace) + need});
+    if (!spans_disjoint(spans)) return BF16D_EINVAL;
+    std::vector<uint8_t> host(tables, 0);
+    first = 0;
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t end = group_end[g];
+        decompress_table(dj.data() + first, end - first, prep[g], lay[g], host.data() + table_at[g]);
+        // the kernels of group g read their job table from its place after `base`
+        const size_t jobs_at = base + table_at[g];
+        lay[g].block_start = jobs_at + (lay[g].block_start - lay[g].jobs);
+        lay[g].dtile_start = jobs_at + (lay[g].dtile_start - lay[g].jobs);
+        lay[g].jobs = jobs_at;
+        first = end;
+    }
+
+    Events ev;
+    if (!ev.ok) return BF16D_EHIP;
+    auto fail = [](hipError_t e) { return e != hipSuccess; };
+    auto *ws = static_cast<uint8_t *>(workspace);
+    // one upload of every job table (the source is pageable: the runtime
+    // stages it before returning), then copies start after it and after the
+    // caller's earlier work on the compute stream
+    if (fail(hipMemcpyAsync(ws + base, host.data(), host.size(), hipMemcpyHostToDevice,
+                            compute)) ||
+        fail(hipEventRecord(ev.start, compute)) || fail(hipStreamWaitEvent(copy, ev.start, 0)))
+        return BF16D_EHIP;
+    first = 0;
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t end = group_end[g], s = g % 2;
+        uint8_t *slot = static_cast<uint8_t *>(staging) + s * slot_bytes;
+        // the slot is free once the apply of group g - 2 has read it
+        if (g >= 2 && fail(hipStreamWaitEvent(copy, ev.applied[s], 0))) return BF16D_EHIP;
+        // one copy per run of payloads that lie in host memory exactly as
+        // they are packed in the slot (the padding between them then comes
+        // along; nothing reads it)
+        for (uint32_t j = first; j < end;) {
+            if (jobs[j].payload_bytes == 0) {
+                ++j;
+                continue;
+            }
+            uint32_t k = j + 1;
+            while (k < end && jobs[k].payload_bytes > 0 &&
+                   jobs[k].payload == jobs[j].payload + (offset[k] - offset[j]))
+                ++k;
+            const uint64_t bytes = offset[k - 1] - offset[j] + jobs[k - 1].payload_bytes;
+            if (fail(hipMemcpyAsync(slot + offset[j], jobs[j].payload, bytes,
+                                    hipMemcpyHostToDevice, copy)))
+                return BF16D_EHIP;
+            j = k;
+        }
+        if (fail(hipEventRecord(ev.copied[s], copy)) ||
+            fail(hipStreamWaitEvent(compute, ev.copied[s], 0)) ||
+            fail(launch_decompress(lay[g], ws, end - first, prep[g].tiles, prep[g].dtiles,
+                                   results + first, compute, nullptr)) ||
+            fail(hipEventRecord(ev.applied[s], compute)))
+            return BF16D_EHIP;
+        first = end;
+    }
+    return BF16D_OK;
+}

@@ -103,3 +103,43 @@ def test_python_api_refuses_cpu_tensors(native):
         delta_compress(src, src.clone())
     with pytest.raises(ValueError):
         delta_compress(src, src.clone(), compression_format="arc_v3")
+
+
+def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
+    """bf16d_decompress_streamed checks every argument before it enqueues
+    anything, so these calls need no GPU (the pointers are never touched)."""
+    lib = native.lib()
+    assert ctypes.sizeof(native.StreamJob) == 40
+    res = (native.Result * 4)()
+    payload = ctypes.create_string_buffer(64)
+    base = 1 << 40                     # fake 16-byte aligned device addresses
+    w0, w1, staging, ws = base, base + (1 << 24), base + (2 << 24), base + (3 << 24)
+    WS = 1 << 22
+    jobs = (native.StreamJob * 2)(native.StreamJob(w0, 100, ctypes.addressof(payload), 64, 0),
+                                  native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
+
+    def call(jobs=jobs, count=2, ends=(1, 2), staging=staging, slot=4096, ws=ws, ws_bytes=WS,
+             results=ctypes.addressof(res)):
+        ge = (ctypes.c_uint32 * max(1, len(ends)))(*ends) if ends is not None else None
+        return lib.bf16d_decompress_streamed(jobs, count, ge, len(ends) if ends else 0, staging,
+                                             slot, ws, ws_bytes, results, None, None)
+
+    E = native.EINVAL
+    assert call(count=0) == E
+    assert call(ends=None) == E
+    assert call(ends=(1,)) == E                 # groups must end at count
+    assert call(ends=(2, 2)) == E               # strictly increasing
+    assert call(ends=(1, 2, 2)) == E            # more groups than jobs
+    assert call(staging=staging + 8) == E       # staging alignment
+    assert call(slot=4100) == E                 # slot size not a multiple of 16
+    assert call(slot=48) == E                   # a payload larger than a slot
+    assert call(ends=(2,), slot=112) == E       # a group that does not fit (2 x 64 > 112)
+    assert call(ws_bytes=16) == E               # workspace too small
+    assert call(results=None) == E
+    assert call(staging=w0 + 64) == E           # staging overlaps the weights
+    bad = (native.StreamJob * 2)(native.StreamJob(w0 + 2, 100, ctypes.addressof(payload), 64, 0),
+                                 native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
+    assert call(jobs=bad) == E                  # weights alignment
+    nopay = (native.StreamJob * 2)(native.StreamJob(w0, 100, None, 64, 0),
+                                   native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
+    assert call(jobs=nopay) == E                # a payload of 64 bytes at NULL

@@ -1,0 +1,86 @@
+"""GPU tests of the streamed receiver (bf16d_decompress_streamed): host-resident
+payloads applied in place group by group through two device slots.
+
+The payloads come from the GPU compressor, whose bytes the other parity tests
+pin to the oracle; here the streamed apply must rebuild every tensor bit for
+bit, and each failure must end exactly as the oracle's decoder ends it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_weight_xor_amd as bd
+import oracle
+from lossless_bf16_weight_xor_amd import synth
+from tests.gpu_util import log, to_u16
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+SHAPES = [(3 * 8192 + 77,), (8192,), (4096, 64), (1,), (0,), (70001,), (2 * 8192,),
+          (513, 129), (8191,), (5 * 8192 + 3,), (12345,), (64, 64)]
+
+
+def _make(seed0=500):
+    pairs = [synth.make_pair(shape, "0.03", synth.MIX_ADVERSARIAL, seed0 + i, DEV)
+             for i, shape in enumerate(SHAPES)]
+    pairs = [(s.reshape(-1), d.reshape(-1)) for s, d in pairs]
+    out = bd.compress_batch(pairs)
+    payloads = [p.cpu().pin_memory() for p, _, _ in out]
+    checksums = [cs for _, cs, _ in out]
+    return pairs, payloads, checksums
+
+
+def _run(pairs, payloads, checksums, groups):
+    recv = [s.clone() for s, _ in pairs]
+    sd = bd.StreamedDecompress(list(zip(recv, payloads, checksums)), groups)
+    sd.run()
+    return recv, sd.results()
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("groups", [[3, 1, 4, 4], [1] * 12, [12], [5, 7]])
+def test_streamed_apply_rebuilds_every_tensor(groups, packed):
+    """packed: all payloads in one pinned buffer at 16-byte boundaries, so each
+    group goes over in one transfer; otherwise one pinned tensor each."""
+    log(f"case streamed groups={groups} packed={packed}")
+    pairs, payloads, checksums = _make()
+    if packed:
+        payloads = bd.StreamedDecompress.pin_packed(payloads)
+    recv, res = _run(pairs, payloads, checksums, groups)
+    assert [r["status"] for r in res] == [bd.OK] * len(pairs)
+    for j, (w, (_, d)) in enumerate(zip(recv, pairs)):
+        assert torch.equal(w.view(torch.int16), d.view(torch.int16)), f"tensor {j}"
+
+
+def test_streamed_failures_match_the_oracle():
+    log("case streamed failures")
+    pairs, payloads, checksums = _make(seed0=900)
+    payloads = [p.clone().pin_memory() for p in payloads]
+    checksums = list(checksums)
+    checksums[2] ^= 1                                  # wrong checksum
+    payloads[5][-1] ^= 0x40                            # last record byte of a dense tensor
+    payloads[9][70] ^= 0x01                            # a descriptor byte
+    recv, res = _run(pairs, payloads, checksums, [4, 4, 4])
+    for j, ((s, d), r) in enumerate(zip(pairs, res)):
+        w = to_u16(s).copy()
+        want = oracle.decompress_inplace(w, payloads[j].numpy(), checksums[j])
+        assert r["status"] == want, f"tensor {j}: {r['status']} vs oracle {want}"
+        assert np.array_equal(to_u16(recv[j]), w), f"tensor {j}: final weights"
+    assert res[2]["status"] == bd.ECHECKSUM
+    assert {res[5]["status"], res[9]["status"]} <= {bd.EFORMAT, bd.ECHECKSUM}
+    assert all(res[j]["status"] == bd.OK for j in (0, 1, 3, 4, 6, 7, 8, 10, 11))
+
+
+def test_streamed_many_groups_reuse_both_slots_in_turn():
+    """40 one-tensor groups: each slot is refilled 20 times, so every copy
+    waits for the apply two groups back."""
+    log("case streamed 40 groups")
+    pairs = [synth.make_pair((8192 * (1 + i % 3) + i,), "0.05", synth.MIX_DEFAULT, 1300 + i, DEV)
+             for i in range(40)]
+    out = bd.compress_batch(pairs)
+    payloads = [p.cpu().pin_memory() for p, _, _ in out]
+    recv, res = _run(pairs, payloads, [cs for _, cs, _ in out], [1] * 40)
+    assert all(r["status"] == bd.OK for r in res)
+    for w, (_, d) in zip(recv, pairs):
+        assert torch.equal(w.view(torch.int16), d.view(torch.int16))
