@@ -256,7 +256,7 @@ typedef struct bf16d_stream_job {
  *                  pipeline serial).  Both streams must be of the same device.
  * Consecutive payloads of a group that lie in host memory exactly as they are
  * packed in the slot (each at the next 16-byte boundary after the previous
- * one) are copied with a single transfer, padding included. */
+ * one) are copied with a single transfer, padding included.
  * Returns BF16D_EINVAL (nothing enqueued) for bad arguments, BF16D_EHIP if a
  * runtime call fails.  Per-job statuses and the weights' final state are
  * those of bf16d_decompress; a failed job does not affect the others. */

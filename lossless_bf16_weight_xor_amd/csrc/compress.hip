@@ -279,7 +279,7 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
                                            uint64_t *__restrict__ partial,
                                            uint32_t *__restrict__ overflow,
                                            Control *__restrict__ ctrl) {
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
     uint4 o[kChunksPerThread], nw[kChunksPerThread];
     load_tile<kFull>(tr, o, nw);
     // while the loads are in flight: clear the record, build the gap table
@@ -303,7 +303,7 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
     } else if (tid == 0) {
         overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
     }
-    if (lane == 0) partial[kWaves * t + wave] = acc;
+    if (lane == 0) partial[kWaves * t + (tid >> 6)] = acc;
     if (tid == 0) desc_out[t] = k.desc;
 }
 
@@ -334,8 +334,10 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
     const uint64_t *__restrict__ dstart, const uint32_t *__restrict__ desc,
     uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets,
-    PlaceEntry *__restrict__ place, Control *__restrict__ ctrl) {
+    PlaceEntry *__restrict__ place, const uint64_t *__restrict__ partial,
+    JobSums *__restrict__ sums, Control *__restrict__ ctrl) {
     __shared__ uint32_t s_tmp[kWaves];
+    __shared__ unsigned long long s_tmp64[kWaves];
     __shared__ uint32_t s_dt;
     __shared__ uint64_t s_excl;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -351,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
 
     uint32_t lens[kDescPerThread], descs[kDescPerThread];
     uint32_t mine = 0;
+    unsigned long long c_sum = 0, r_sum = 0, pos_sum = 0, mant_sum = 0, nbm = 0, S = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kDescPerThread; ++k) {
         const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
@@ -359,12 +362,19 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
         if (b >= job.nb) continue;
         const uint32_t d = desc[job.block0 + b];
         descs[k] = d;
+#pragma unroll
+        for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * (job.block0 + b) + w];
         const uint64_t left = job.n - b * kBlock;
         const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
         const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
         const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
         lens[k] = pb + (7 * c + 7) / 8 + 2 * r;
         mine += lens[k];
+        c_sum += c;
+        r_sum += r;
+        pos_sum += pb;
+        mant_sum += (7 * c + 7) / 8;
+        nbm += code == kCodeBitmap;
     }
     uint32_t total;
     uint32_t excl = block_exclusive_sum(mine, s_tmp, total);
@@ -397,6 +407,21 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
             place[job.block0 + b] = e;
         }
         off += lens[k];
+    }
+    // the header totals of the job
+    c_sum = block_sum(c_sum, s_tmp64);
+    r_sum = block_sum(r_sum, s_tmp64);
+    pos_sum = block_sum(pos_sum, s_tmp64);
+    mant_sum = block_sum(mant_sum, s_tmp64);
+    nbm = block_sum(nbm, s_tmp64);
+    S = block_sum(S, s_tmp64);
+    if (tid == 0) {
+        atomicAdd(&sums[j].csum, S);   // exact mod 2^64, in any order
+        atomicAdd(&sums[j].c, c_sum);
+        atomicAdd(&sums[j].r, r_sum);
+        atomicAdd(&sums[j].pos, pos_sum);
+        atomicAdd(&sums[j].mant, mant_sum);
+        atomicAdd(&sums[j].nbm, nbm);
     }
 }
 
@@ -542,31 +567,14 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
 // ---------------------------------------------------------------- finalize ---
 // One workgroup per job: header, checksum and result.
 __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
-    const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ desc,
-    const uint64_t *__restrict__ partial, bf16d_result *__restrict__ results) {
-    __shared__ unsigned long long s_tmp[kWaves];
-    const CompressJob job = jobs[blockIdx.x];
-    unsigned long long S = 0, c = 0, r = 0, pos = 0, mant = 0, nbm = 0;
-    for (uint64_t b = threadIdx.x; b < job.nb; b += kThreads) {
-        const uint64_t t = job.block0 + b;
-        const uint32_t d = desc[t];
-        const uint64_t left = job.n - b * kBlock;
-        const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
-        const uint32_t cb = d & 0x3FFFu, rb = (d >> 14) & 0x3FFFu, code = d >> 28;
-        for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * t + w];
-        c += cb;
-        r += rb;
-        pos += code == kCodeBitmap ? (L + 7) / 8 : (cb * code + 7) / 8;
-        mant += (7 * cb + 7) / 8;
-        nbm += code == kCodeBitmap;
-    }
-    S = block_sum(S, s_tmp);
-    c = block_sum(c, s_tmp);
-    r = block_sum(r, s_tmp);
-    pos = block_sum(pos, s_tmp);
-    mant = block_sum(mant, s_tmp);
-    nbm = block_sum(nbm, s_tmp);
-    if (threadIdx.x != 0) return;
+    const CompressJob *__restrict__ jobs, const JobSums *__restrict__ sums, uint32_t count,
+    bf16d_result *__restrict__ results) {
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= count) return;
+    const CompressJob job = jobs[j];
+    const JobSums js = sums[j];
+    const unsigned long long S = js.csum, c = js.c, r = js.r, pos = js.pos, mant = js.mant,
+                             nbm = js.nbm;
     const uint64_t rare = 2 * r;
     const uint64_t P = kHeader + 4 * job.nb + pos + mant + rare;
     const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
@@ -592,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     res.n_changed = c;
     res.n_rare = r;
     res.n_bitmap_blocks = nbm;
-    results[blockIdx.x] = res;
+    results[j] = res;
 }
 
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
@@ -605,6 +613,7 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     auto *map = reinterpret_cast<uint32_t *>(ws + l.tile_job);
     auto *offsets = reinterpret_cast<uint64_t *>(ws + l.status);
     auto *partial = reinterpret_cast<uint64_t *>(ws + l.partial);
+    auto *sums = reinterpret_cast<JobSums *>(ws + l.sums);
     auto *desc = reinterpret_cast<uint32_t *>(ws + l.desc);
     auto *dmap = reinterpret_cast<uint32_t *>(ws + l.dtile_job);
     auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
@@ -613,6 +622,8 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     auto *place = reinterpret_cast<PlaceEntry *>(ws + l.plan);
 
     launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
+    launch_zero_words(reinterpret_cast<uint32_t *>(sums), sizeof(JobSums) / 4 * (uint64_t)count,
+                      stream);
     if (tiles) {
         launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
         launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
@@ -623,14 +634,15 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
-            jobs, dmap, dstart, desc, dstatus, offsets, place, ctrl);
+            jobs, dmap, dstart, desc, dstatus, offsets, place, partial, sums, ctrl);
         const uint64_t per_block = (uint64_t)kWaves * kPlaceTiles;
         place_kernel<<<(uint32_t)((tiles + per_block - 1) / per_block), kThreads, 0, stream>>>(
             place, slots, tiles);
         reencode_kernel<<<persistent_grid((const void *)reencode_kernel, tiles), kThreads, 0,
                           stream>>>(jobs, map, overflow, offsets, ctrl);
     }
-    compress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, desc, partial, results);
+    compress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+        jobs, sums, count, results);
     return hipGetLastError();
 }
 

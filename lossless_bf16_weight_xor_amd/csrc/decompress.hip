@@ -760,22 +760,43 @@ void rollback_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__rest
     apply_pass<true>(plan, state, nullptr, tiles);
 }
 
+// ------------------------------------------------------------- checksum sum ---
+// The checksum sum S of every job that was applied: one workgroup per 2048
+// blocks (the descriptor-scan tiles) sums its blocks' per-wave partials and
+// adds them to the job's total with one atomic (exact mod 2^64 in any order).
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(
+    const DecompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
+    const DecompressState *__restrict__ state, const uint64_t *__restrict__ partial,
+    JobSums *__restrict__ sums) {
+    __shared__ unsigned long long s_tmp[kWaves];
+    const uint64_t dt = blockIdx.x;
+    const uint32_t j = dtile_job[dt];
+    if (state[j].state != kStateReady) return;   // uniform: nothing was applied
+    const DecompressJob &job = jobs[j];
+    const uint64_t ld = dt - job.dtile0;
+    unsigned long long S = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kDescPerThread; ++k) {
+        const uint64_t b = ld * kDescTile + kDescPerThread * threadIdx.x + k;
+        if (b < job.nb)
+#pragma unroll
+            for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * (job.block0 + b) + w];
+    }
+    S = block_sum(S, s_tmp);
+    if (threadIdx.x == 0) atomicAdd(&sums[j].csum, S);
+}
+
 // ----------------------------------------------------------------- finalize ---
 __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
     const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
-    const uint64_t *__restrict__ partial, Control *__restrict__ ctrl,
+    const JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
     bf16d_result *__restrict__ results) {
-    __shared__ unsigned long long s_tmp[kWaves];
-    const uint32_t j = blockIdx.x;
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= count) return;
     const DecompressJob job = jobs[j];
     DecompressState *st = &state[j];
     const bool ready = st->state == kStateReady;
-    unsigned long long S = 0;
-    if (ready)
-        for (uint64_t b = threadIdx.x; b < job.nb; b += kThreads)
-            for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * (job.block0 + b) + w];
-    S = block_sum(S, s_tmp);
-    if (threadIdx.x != 0) return;
+    const unsigned long long S = sums[j].csum;
     bf16d_result res;
     res.reserved = 0;
     res.payload_bytes = job.payload_bytes;
@@ -808,6 +829,7 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     auto *dstart = reinterpret_cast<const uint64_t *>(ws + l.dtile_start);
     auto *offsets = reinterpret_cast<uint64_t *>(ws + l.status);
     auto *partial = reinterpret_cast<uint64_t *>(ws + l.partial);
+    auto *sums = reinterpret_cast<JobSums *>(ws + l.sums);
     auto *dmap = reinterpret_cast<uint32_t *>(ws + l.dtile_job);
     auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
     auto *state = reinterpret_cast<DecompressState *>(ws + l.state);
@@ -816,6 +838,8 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
     launch_zero_words(reinterpret_cast<uint32_t *>(state),
                       sizeof(DecompressState) / 4 * (uint64_t)count, stream);
+    launch_zero_words(reinterpret_cast<uint32_t *>(sums), sizeof(JobSums) / 4 * (uint64_t)count,
+                      stream);
     if (dtiles) {
         launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
         desc_scan_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(jobs, dmap, dstatus, offsets,
@@ -832,9 +856,11 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
         apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(plan, state, partial);
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
+        sum_partials_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(jobs, dmap, state,
+                                                                       partial, sums);
     }
-    decompress_finalize_kernel<<<count, kThreads, 0, stream>>>(jobs, state, partial, ctrl,
-                                                               results);
+    decompress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+        jobs, state, sums, ctrl, count, results);
     if (tiles) {
         rollback_kernel<<<persistent_grid((const void *)rollback_kernel, tiles), kThreads, 0,
                           stream>>>(plan, state, ctrl, tiles);

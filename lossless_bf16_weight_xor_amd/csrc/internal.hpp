@@ -100,6 +100,15 @@ struct alignas(32) ApplyPlan {
 };
 static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
 
+// per-job sums (zeroed at the start of a call), accumulated with one atomic
+// per job and scan tile of 2048 blocks: the checksum sum S (both directions,
+// from the per-wave partials) and, for compress, the header totals.  (One
+// atomic per wave and tile, straight from the main kernels, contends on the
+// few addresses and measured much slower.)
+struct alignas(64) JobSums {
+    unsigned long long csum, c, r, pos, mant, nbm, pad0, pad1;
+};
+
 // compress: where one tile's record goes, written by the offsets kernel for
 // the place kernel
 struct alignas(16) PlaceEntry {
@@ -120,7 +129,7 @@ struct alignas(64) Control {
 
 // Workspace layout, computed identically by every entry point.
 struct Layout {
-    size_t control, jobs, block_start, dtile_start, tile_job, status, partial, desc,
+    size_t control, jobs, block_start, dtile_start, tile_job, status, partial, sums, desc,
         dtile_job, dstatus, state, slots, overflow, plan, total;
 };
 
@@ -143,6 +152,7 @@ inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool 
     l.tile_job = take(4 * tiles);
     l.status = take(8 * tiles);     // record offsets
     l.partial = take(8 * kWaves * tiles);   // per-wave checksum partial sums of each tile
+    l.sums = take(sizeof(JobSums) * size_t(count));   // per-job sums (atomic)
     l.desc = take(4 * tiles);       // compress: descriptor copies
     l.dtile_job = take(4 * dtiles);
     l.dstatus = take(8 * dtiles);
