@@ -210,6 +210,55 @@ int bf16d_delta_decompress(uint16_t *src_inout, uint64_t n,
                            void *workspace, size_t workspace_bytes,
                            bf16d_result *result, hipStream_t stream);
 
+/* Remapped apply: the new weights land on a physical layout that differs
+ * from the logical tensor the payload was made from.
+ *
+ * "GPU-accelerated Weight Teleportation", sections "A strong baseline with
+ * Blackwell-native DE" and "Working with low-precision RL": fused kernels
+ * may keep weights in a reordered physical layout (for example gate and up
+ * projections paired in groups of 64 rows); the XOR mask is remapped the
+ * same way through address metadata prepared on the CPU, and one launch
+ * applies it to the whole model.  Here that metadata is a list of segments
+ * per tensor.
+ *
+ * Logical elements [first, first + count) of a tensor live at dst[0, count).
+ *   first  : a multiple of BF16D_BLOCK_ELEMS (8192): segments are
+ *            block-granular, so each block of the payload lands in one
+ *            place.  Gate/up pairing in groups of 64 rows qualifies whenever
+ *            a row holds at least 128 elements.
+ *   count  : elements; every segment but the tensor's last must hold a
+ *            multiple of 8192.
+ *   dst    : device, 16-byte aligned.
+ * The segments of a tensor must follow one another (segment k + 1 starts
+ * where segment k ends), start at 0 and cover exactly n elements.  The
+ * checksum is that of the logical tensor, as compress computed it. */
+typedef struct bf16d_segment {
+    uint64_t  first;
+    uint64_t  count;
+    uint16_t *dst;
+} bf16d_segment;
+
+/* The segments of one tensor (host memory).  count == 0 means no remap: the
+ * job's weights pointer is used as in bf16d_decompress.  With count > 0 the
+ * job's weights pointer must be NULL. */
+typedef struct bf16d_remap {
+    const bf16d_segment *segments;
+    uint32_t             count;
+} bf16d_remap;
+
+/* Workspace bytes that suffice for a remapped decompress of `count` jobs
+ * totalling total_n elements and total_segments segments. */
+size_t bf16d_workspace_bytes_remapped(uint64_t total_n, uint32_t count,
+                                      uint64_t total_segments);
+
+/* bf16d_decompress with remaps[j] for job j (remaps may be NULL: no remap).
+ * Statuses, rollback and argument errors are those of bf16d_decompress; the
+ * segments' physical ranges are the weights that are written, and they may
+ * not overlap one another, a payload or the workspace. */
+int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
+                              uint32_t count, void *workspace, size_t workspace_bytes,
+                              bf16d_result *results, hipStream_t stream);
+
 /* Streamed receiver: payloads in host memory, applied layer by layer.
  *
  * The double-buffered pipeline of "GPU-accelerated Weight Teleportation",

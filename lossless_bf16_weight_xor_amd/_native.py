@@ -21,6 +21,7 @@ FORMAT_VERSION = 1
 EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress",
             "bf16d_decompress", "bf16d_compress_ex", "bf16d_decompress_ex",
             "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_decompress_streamed",
+            "bf16d_decompress_remapped", "bf16d_workspace_bytes_remapped",
             "bf16d_status_string", "bf16d_format_version")
 
 
@@ -46,6 +47,14 @@ class StreamJob(ctypes.Structure):
     _fields_ = [("weights", ctypes.c_void_p), ("n", ctypes.c_uint64),
                 ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64),
                 ("checksum", ctypes.c_uint64)]
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("first", ctypes.c_uint64), ("count", ctypes.c_uint64), ("dst", ctypes.c_void_p)]
+
+
+class Remap(ctypes.Structure):
+    _fields_ = [("segments", ctypes.POINTER(Segment)), ("count", ctypes.c_uint32)]
 
 
 class Events(ctypes.Structure):
@@ -89,6 +98,11 @@ def lib():
                                                 ctypes.POINTER(ctypes.c_uint32), u32, vp, sz, vp,
                                                 sz, vp, vp, vp]
         L.bf16d_decompress_streamed.restype = ctypes.c_int
+        L.bf16d_decompress_remapped.argtypes = [ctypes.POINTER(DecompressJob),
+                                                ctypes.POINTER(Remap), u32, vp, sz, vp, vp]
+        L.bf16d_decompress_remapped.restype = ctypes.c_int
+        L.bf16d_workspace_bytes_remapped.argtypes = [u64, u32, u64]
+        L.bf16d_workspace_bytes_remapped.restype = sz
         L.bf16d_delta_compress.argtypes = [vp, vp, u64, vp, u64, vp, sz, vp, vp]
         L.bf16d_delta_compress.restype = ctypes.c_int
         L.bf16d_delta_decompress.argtypes = [vp, u64, vp, u64, u64, vp, sz, vp, vp]

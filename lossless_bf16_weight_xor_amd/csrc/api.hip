@@ -53,12 +53,32 @@ int upload(void *ws, const std::vector<uint8_t> &host, size_t at, hipStream_t st
 
 namespace bf16d {
 
-int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p) {
+// a remap's segments: block-aligned, in order, back to back from 0, covering n
+bool remap_valid(const bf16d_remap &m, uint64_t n) {
+    if (!m.segments) return false;
+    uint64_t at = 0;
+    for (uint32_t k = 0; k < m.count; ++k) {
+        const bf16d_segment &g = m.segments[k];
+        if (g.first != at || g.first % kBlock != 0 || g.count == 0 || !g.dst ||
+            !aligned16(g.dst) || g.count > (UINT64_MAX >> 2) - at)
+            return false;
+        if (k + 1 < m.count && g.count % kBlock != 0) return false;
+        at += g.count;
+    }
+    return at == n;
+}
+
+int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p,
+                    const bf16d_remap *remaps) {
     p.bstart.assign(size_t(count) + 1, 0);
     p.dstart.assign(size_t(count) + 1, 0);
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_decompress_job &J = jobs[j];
-        if (J.n > 0 && (!J.weights || !aligned16(J.weights))) return BF16D_EINVAL;
+        if (remaps && remaps[j].count > 0) {
+            if (J.weights || !remap_valid(remaps[j], J.n)) return BF16D_EINVAL;
+        } else if (J.n > 0 && (!J.weights || !aligned16(J.weights))) {
+            return BF16D_EINVAL;
+        }
         // an empty payload may be NULL; it is then rejected on the device as too short
         if ((J.payload_bytes > 0 && !J.payload) || !aligned16(J.payload)) return BF16D_EINVAL;
         if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
@@ -87,12 +107,88 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
         dj[j].block0 = p.bstart[j];
         dj[j].nb = p.bstart[j + 1] - p.bstart[j];
         dj[j].dtile0 = p.dstart[j];
+        dj[j].segs = nullptr;
+        dj[j].nsegs = 0;
     }
     std::memcpy(out + (l.block_start - l.jobs), p.bstart.data(), 8 * p.bstart.size());
     std::memcpy(out + (l.dtile_start - l.jobs), p.dstart.data(), 8 * p.dstart.size());
 }
 
 }  // namespace bf16d
+
+namespace {
+
+// The batched decompress, optionally remapped: checks, job table (and the
+// remap segments after the layout), upload, launch.
+int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps, uint32_t count,
+                    void *workspace, size_t workspace_bytes, bf16d_result *results,
+                    hipStream_t stream, const bf16d_events *events) {
+    if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
+        return BF16D_EINVAL;
+    DecompressPrep prep;
+    int rc = decompress_prep(jobs, count, prep, remaps);
+    if (rc != BF16D_OK) return rc;
+    const Layout l = make_layout(prep.tiles, prep.dtiles, count, false);
+    size_t nsegs = 0;
+    if (remaps)
+        for (uint32_t j = 0; j < count; ++j) nsegs += remaps[j].count;
+    const size_t seg_at = align_up(l.total, 256);
+    const size_t need = nsegs ? seg_at + sizeof(RemapSegment) * nsegs : l.total;
+    if (workspace_bytes < need) return BF16D_EINVAL;
+    std::vector<Range> ranges;
+    ranges.reserve(2 * size_t(count) + nsegs + 1);
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_decompress_job &J = jobs[j];
+        if (remaps && remaps[j].count > 0) {
+            for (uint32_t k = 0; k < remaps[j].count; ++k) {
+                const bf16d_segment &g = remaps[j].segments[k];
+                ranges.push_back({reinterpret_cast<uintptr_t>(g.dst),
+                                  reinterpret_cast<uintptr_t>(g.dst) + 2 * g.count, true});
+            }
+        } else {
+            ranges.push_back({reinterpret_cast<uintptr_t>(J.weights),
+                              reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n, true});
+        }
+        ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
+                          reinterpret_cast<uintptr_t>(J.payload) + J.payload_bytes, false});
+    }
+    ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
+                      reinterpret_cast<uintptr_t>(workspace) + need, true});
+    if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
+
+    std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
+    decompress_table(jobs, count, prep, l, host.data());
+    std::vector<uint8_t> segs(sizeof(RemapSegment) * nsegs, 0);
+    if (nsegs) {
+        auto *dj = reinterpret_cast<DecompressJob *>(host.data());
+        auto *ds = reinterpret_cast<RemapSegment *>(segs.data());
+        auto *dev = reinterpret_cast<const RemapSegment *>(static_cast<uint8_t *>(workspace) +
+                                                           seg_at);
+        size_t at = 0;
+        for (uint32_t j = 0; j < count; ++j) {
+            if (remaps[j].count == 0) continue;
+            dj[j].segs = dev + at;
+            dj[j].nsegs = remaps[j].count;
+            for (uint32_t k = 0; k < remaps[j].count; ++k, ++at) {
+                const bf16d_segment &g = remaps[j].segments[k];
+                ds[at].first = g.first;
+                ds[at].count = g.count;
+                ds[at].dst = (BF16D_GMEM uint16_t *)g.dst;
+                ds[at].pad = 0;
+            }
+        }
+        rc = upload(workspace, segs, seg_at, stream);
+        if (rc != BF16D_OK) return rc;
+    }
+    rc = upload(workspace, host, l.jobs, stream);
+    if (rc != BF16D_OK) return rc;
+    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, prep.tiles, prep.dtiles,
+                             results, stream, events) == hipSuccess
+               ? BF16D_OK
+               : BF16D_EHIP;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -180,34 +276,19 @@ int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *wor
 int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
                         size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
                         const bf16d_events *events) {
-    if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
-        return BF16D_EINVAL;
-    DecompressPrep prep;
-    int rc = decompress_prep(jobs, count, prep);
-    if (rc != BF16D_OK) return rc;
-    const Layout l = make_layout(prep.tiles, prep.dtiles, count, false);
-    if (workspace_bytes < l.total) return BF16D_EINVAL;
-    std::vector<Range> ranges;
-    ranges.reserve(2 * size_t(count) + 1);
-    for (uint32_t j = 0; j < count; ++j) {
-        const bf16d_decompress_job &J = jobs[j];
-        ranges.push_back({reinterpret_cast<uintptr_t>(J.weights),
-                          reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n, true});
-        ranges.push_back({reinterpret_cast<uintptr_t>(J.payload),
-                          reinterpret_cast<uintptr_t>(J.payload) + J.payload_bytes, false});
-    }
-    ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
-                      reinterpret_cast<uintptr_t>(workspace) + l.total, true});
-    if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
+    return decompress_call(jobs, nullptr, count, workspace, workspace_bytes, results, stream,
+                           events);
+}
 
-    std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
-    decompress_table(jobs, count, prep, l, host.data());
-    rc = upload(workspace, host, l.jobs, stream);
-    if (rc != BF16D_OK) return rc;
-    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, prep.tiles, prep.dtiles,
-                             results, stream, events) == hipSuccess
-               ? BF16D_OK
-               : BF16D_EHIP;
+size_t bf16d_workspace_bytes_remapped(uint64_t total_n, uint32_t count, uint64_t total_segments) {
+    return bf16d_workspace_bytes(total_n, count) + 256 + sizeof(RemapSegment) * total_segments;
+}
+
+int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
+                              uint32_t count, void *workspace, size_t workspace_bytes,
+                              bf16d_result *results, hipStream_t stream) {
+    return decompress_call(jobs, remaps, count, workspace, workspace_bytes, results, stream,
+                           nullptr);
 }
 
 int bf16d_delta_compress(const uint16_t *src, const uint16_t *dst, uint64_t n, uint8_t *payload,

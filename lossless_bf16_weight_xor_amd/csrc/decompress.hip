@@ -174,7 +174,17 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
             const uint64_t b = t - job.block0;
             const uint64_t D = kHeader + 4 * job.nb + offsets[t];
             const uint64_t room = job.payload_bytes - D;   // prepare checked D <= payload_bytes
-            p.w = job.weights + b * kBlock;
+            if (job.nsegs == 0) {
+                p.w = job.weights + b * kBlock;
+            } else {   // the segment holding block b (segments are block-aligned)
+                const uint64_t e = b * kBlock;
+                uint32_t slo = 0, shi = job.nsegs;   // segs[slo].first <= e < segs[shi].first
+                while (shi - slo > 1) {
+                    const uint32_t mid = (slo + shi) >> 1;
+                    if (job.segs[mid].first <= e) slo = mid; else shi = mid;
+                }
+                p.w = job.segs[slo].dst + (e - job.segs[slo].first);
+            }
             p.rec = job.payload + D;
             p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + kHeader + 4 * b);
             p.len_room = block_length(job.n, b) | (uint32_t)(room < 0x3FFFFu ? room : 0x3FFFFu)

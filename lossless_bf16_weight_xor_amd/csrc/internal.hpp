@@ -67,6 +67,14 @@ struct alignas(64) CompressJob {
 
 enum JobState : uint32_t { kStateReady = 1, kStateRejected = 2 };
 
+// one segment of a remapped tensor: logical elements [first, first + count)
+// live at dst (first is block-aligned)
+struct alignas(32) RemapSegment {
+    uint64_t first, count;
+    BF16D_GMEM uint16_t *dst;
+    uint64_t pad;
+};
+
 struct alignas(64) DecompressJob {
     BF16D_GMEM uint16_t *weights;
     uint64_t n;
@@ -76,6 +84,8 @@ struct alignas(64) DecompressJob {
     uint64_t block0;   // first global tile index
     uint64_t nb;       // blocks
     uint64_t dtile0;   // first global descriptor-scan tile index
+    const RemapSegment *segs;   // remapped: the job's segments; else nullptr
+    uint32_t nsegs;             // 0: no remap, the weights pointer is used
 };
 
 // per-job device state of a decompress call (zeroed by the setup kernel)
@@ -462,7 +472,8 @@ struct DecompressPrep {
     std::vector<uint64_t> bstart, dstart;   // first tile / descriptor tile of each job
     uint64_t tiles = 0, dtiles = 0;
 };
-int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p);
+int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p,
+                    const bf16d_remap *remaps = nullptr);
 size_t decompress_table_bytes(const Layout &l, uint32_t count);
 void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
                       const Layout &l, uint8_t *out);

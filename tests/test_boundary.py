@@ -143,3 +143,34 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
     nopay = (native.StreamJob * 2)(native.StreamJob(w0, 100, None, 64, 0),
                                    native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
     assert call(jobs=nopay) == E                # a payload of 64 bytes at NULL
+
+
+def test_remapped_arguments_are_rejected_before_any_gpu_work(native):
+    """bf16d_decompress_remapped checks the segments before it enqueues
+    anything; none of these calls reaches the GPU."""
+    lib = native.lib()
+    assert ctypes.sizeof(native.Segment) == 24
+    res = (native.Result * 2)()
+    base = 1 << 40
+    ws, pay = base, base + (1 << 30)
+    WS = int(lib.bf16d_workspace_bytes_remapped(3 * 8192, 1, 4))
+    job = native.DecompressJob(None, 3 * 8192, pay, 64, 0)
+    A, B = base + (2 << 30), base + (3 << 30)
+
+    def call(segs, job=job, ws_bytes=WS):
+        arr = (native.Segment * len(segs))(*[native.Segment(*s) for s in segs])
+        remap = (native.Remap * 1)(native.Remap(arr, len(segs)))
+        return lib.bf16d_decompress_remapped(ctypes.byref(job), remap, 1, ws, ws_bytes,
+                                            ctypes.addressof(res), None)
+
+    E = native.EINVAL
+    ok = [(0, 8192, A), (8192, 2 * 8192, B)]
+    assert call(ok, ws_bytes=16) == E                                # workspace too small
+    assert call(ok, job=native.DecompressJob(A, 3 * 8192, pay, 64, 0)) == E   # weights set too
+    assert call([(0, 8192, A), (8192, 8192, B)]) == E                # covers less than n
+    assert call([(0, 8192, A), (16384, 8192, B)]) == E               # a gap
+    assert call([(8192, 3 * 8192, A)]) == E                          # does not start at 0
+    assert call([(0, 100, A), (100, 3 * 8192 - 100, B)]) == E        # not block-aligned
+    assert call([(0, 8192, A + 8), (8192, 2 * 8192, B)]) == E        # dst alignment
+    assert call([(0, 8192, A), (8192, 2 * 8192, A + 4096)]) == E     # segments overlap
+    assert call([(0, 8192, A), (8192, 2 * 8192, None)]) == E         # no destination

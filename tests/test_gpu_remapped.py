@@ -1,0 +1,86 @@
+"""GPU parity of the remapped apply (bf16d_decompress_remapped): payloads made
+from logical tensors land on a reordered physical layout.
+
+The layout of "GPU-accelerated Weight Teleportation", section "Working with
+low-precision RL": gate and up projections paired in groups of 64 rows in one
+fused buffer.  The expected physical buffer is built on the CPU by pairing the
+logical new weights the same way; the payloads themselves are pinned to the
+oracle by the other parity tests, and every job's status here must match the
+oracle's decoder run on the logical tensors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_weight_xor_amd as bd
+import oracle
+from lossless_bf16_weight_xor_amd import synth
+from tests.gpu_util import log, to_u16
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+G = 64   # rows per group
+
+
+def _paired(gate, up):
+    """[2R, C] with rows gate[64g:64g+64], up[64g:64g+64] for each group g."""
+    R, C = gate.shape
+    out = torch.empty((2 * R, C), dtype=gate.dtype, device=gate.device)
+    for g in range(R // G):
+        out[2 * G * g: 2 * G * g + G] = gate[G * g: G * (g + 1)]
+        out[2 * G * g + G: 2 * G * (g + 1)] = up[G * g: G * (g + 1)]
+    return out
+
+
+def _segments(fused, which, R, C):
+    """(first, view) segments of gate (which=0) or up (which=1) in `fused`."""
+    flat = fused.reshape(-1)
+    return [(G * g * C, flat[(2 * G * g + which * G) * C: (2 * G * g + which * G + G) * C])
+            for g in range(R // G)]
+
+
+@pytest.mark.parametrize("R,C", [(512, 128), (256, 4096)])
+def test_gate_up_paired_in_groups_of_64(R, C):
+    log(f"case remapped gate/up R={R} C={C}")
+    (g0, g1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 2000 + R, DEV)
+    (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 3000 + R, DEV)
+    # an identity job and a ragged two-segment job in the same call
+    (x0, x1) = synth.make_pair((70001,), "0.05", synth.MIX_ADVERSARIAL, 4000 + R, DEV)
+    (y0, y1) = synth.make_pair((3 * 8192 + 77,), "0.05", synth.MIX_ADVERSARIAL, 5000 + R, DEV)
+    out = bd.compress_batch([(g0.reshape(-1), g1.reshape(-1)), (u0.reshape(-1), u1.reshape(-1)),
+                             (x0, x1), (y0, y1)])
+    fused = _paired(g0, u0)
+    want = _paired(g1, u1)
+    xw = x0.clone()
+    ya = torch.empty(2 * 8192, dtype=torch.bfloat16, device=DEV).copy_(y0[:2 * 8192])
+    yb = torch.empty(8192 + 77, dtype=torch.bfloat16, device=DEV).copy_(y0[2 * 8192:])
+    items = [((R * C, _segments(fused, 0, R, C)), out[0][0], out[0][1]),
+             ((R * C, _segments(fused, 1, R, C)), out[1][0], out[1][1]),
+             (xw, out[2][0], out[2][1]),
+             ((y0.numel(), [(0, ya), (2 * 8192, yb)]), out[3][0], out[3][1])]
+    res = bd.decompress_remapped(items)
+    assert [r["status"] for r in res] == [bd.OK] * 4
+    assert torch.equal(fused.view(torch.int16), want.view(torch.int16))
+    assert torch.equal(xw.view(torch.int16), x1.view(torch.int16))
+    assert torch.equal(torch.cat([ya, yb]).view(torch.int16), y1.view(torch.int16))
+
+
+def test_remapped_failure_leaves_the_physical_layout_old():
+    log("case remapped failure")
+    R, C = 256, 128
+    (g0, g1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 6000, DEV)
+    (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 6001, DEV)
+    out = bd.compress_batch([(g0.reshape(-1), g1.reshape(-1)), (u0.reshape(-1), u1.reshape(-1))])
+    fused = _paired(g0, u0)
+    old = fused.clone()
+    bad_payload = out[1][0].clone()
+    bad_payload[-1] ^= 0x20
+    items = [((R * C, _segments(fused, 0, R, C)), out[0][0], out[0][1] ^ 1),   # wrong checksum
+             ((R * C, _segments(fused, 1, R, C)), bad_payload, out[1][1])]     # bad record
+    res = bd.decompress_remapped(items)
+    for j, (src, payload, cs) in enumerate([(g0, out[0][0], out[0][1] ^ 1),
+                                             (u0, bad_payload, out[1][1])]):
+        w = to_u16(src).copy()
+        assert res[j]["status"] == oracle.decompress_inplace(w, payload.cpu().numpy(), cs)
+        assert res[j]["status"] != bd.OK
+    assert torch.equal(fused.view(torch.int16), old.view(torch.int16))
