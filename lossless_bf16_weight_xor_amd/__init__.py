@@ -28,7 +28,8 @@ FORMAT = "bf16delta_v1"
 _ALIGN = 256   # payload slots inside an arena start on this boundary
 
 __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_batch",
-           "CompressBatch", "DecompressBatch", "StreamedDecompress", "decompress_remapped", "FormatError", "ChecksumError",
+           "CompressBatch", "DecompressBatch", "StreamedDecompress", "RemappedBatch",
+           "decompress_remapped", "FormatError", "ChecksumError",
            "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
 
 
@@ -267,48 +268,68 @@ class StreamedDecompress:
         return _results(self.result_buf, self.count)
 
 
-def decompress_remapped(items) -> list[dict]:
-    """Apply payloads in place onto remapped physical layouts in one batched
-    call (bf16d_decompress_remapped).
+class RemappedBatch:
+    """A prepared remapped decompress (bf16d_decompress_remapped): payloads
+    made from logical tensors, applied in place onto reordered physical
+    layouts in one batched call.
 
     items: (target, payload, checksum) per tensor.  target is either a weights
     tensor (no remap) or (n, segments) with segments a list of (first, view):
     logical elements [first, first + view.numel()) of the n-element tensor
     live in `view` (a contiguous 16-bit device view, `first` a multiple of
-    8192).  Returns the per-job result dicts."""
-    if not items:
-        raise ValueError("empty batch")
-    count = len(items)
-    jobs = (DecompressJob * count)()
-    remaps = (_native.Remap * count)()
-    keep, total_n, total_segs, device = [], 0, 0, None
-    for j, (target, payload, checksum) in enumerate(items):
-        if payload.dtype != torch.uint8 or payload.device.type != "cuda" or \
-                not payload.is_contiguous():
-            raise TypeError("payload must be a contiguous uint8 device tensor")
-        device = payload.device
-        if isinstance(target, torch.Tensor):
-            n, wptr = target.numel(), _weights_ptr(target, "weights")
-            remaps[j] = _native.Remap(None, 0)
-        else:
-            n, segs = target
-            arr = (_native.Segment * len(segs))()
-            for k, (first, view) in enumerate(segs):
-                arr[k] = _native.Segment(first, view.numel(), _weights_ptr(view, "segment"))
-            keep.append(arr)
-            remaps[j] = _native.Remap(arr, len(segs))
-            wptr, total_segs = None, total_segs + len(segs)
-        jobs[j] = DecompressJob(wptr, n, payload.data_ptr() if payload.numel() else None,
-                                payload.numel(), int(checksum) & 0xFFFFFFFFFFFFFFFF)
-        total_n += n
-    L = _native.lib()
-    ws_bytes = int(L.bf16d_workspace_bytes_remapped(total_n, count, total_segs))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
-    res = torch.empty(count * RESULT_BYTES, dtype=torch.uint8, device=device)
-    rc = L.bf16d_decompress_remapped(jobs, remaps, count, ws.data_ptr(), ws_bytes,
-                                     res.data_ptr(), _stream(device))
-    _check_rc(rc, "bf16d_decompress_remapped")
-    return _results(res, count)
+    8192)."""
+
+    def __init__(self, items):
+        if not items:
+            raise ValueError("empty batch")
+        self.count = len(items)
+        self.items = list(items)   # keep the tensors alive
+        self.jobs = (DecompressJob * self.count)()
+        self.remaps = (_native.Remap * self.count)()
+        self._keep = []
+        total_n, total_segs, device = 0, 0, None
+        for j, (target, payload, checksum) in enumerate(items):
+            if payload.dtype != torch.uint8 or payload.device.type != "cuda" or \
+                    not payload.is_contiguous():
+                raise TypeError("payload must be a contiguous uint8 device tensor")
+            device = payload.device
+            if isinstance(target, torch.Tensor):
+                n, wptr = target.numel(), _weights_ptr(target, "weights")
+                self.remaps[j] = _native.Remap(None, 0)
+            else:
+                n, segs = target
+                arr = (_native.Segment * len(segs))()
+                for k, (first, view) in enumerate(segs):
+                    arr[k] = _native.Segment(first, view.numel(), _weights_ptr(view, "segment"))
+                self._keep.append(arr)
+                self.remaps[j] = _native.Remap(arr, len(segs))
+                wptr, total_segs = None, total_segs + len(segs)
+            self.jobs[j] = DecompressJob(wptr, n, payload.data_ptr() if payload.numel() else None,
+                                         payload.numel(), int(checksum) & 0xFFFFFFFFFFFFFFFF)
+            total_n += n
+        self.device = device
+        self.ws_bytes = int(_native.lib().bf16d_workspace_bytes_remapped(total_n, self.count,
+                                                                         total_segs))
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
+                                      device=device)
+
+    def run(self) -> None:
+        rc = _native.lib().bf16d_decompress_remapped(
+            self.jobs, self.remaps, self.count, self.workspace.data_ptr(), self.ws_bytes,
+            self.result_buf.data_ptr(), _stream(self.device))
+        _check_rc(rc, "bf16d_decompress_remapped")
+
+    def results(self) -> list[dict]:
+        return _results(self.result_buf, self.count)
+
+
+def decompress_remapped(items) -> list[dict]:
+    """One remapped decompress call (see RemappedBatch); returns the per-job
+    result dicts."""
+    batch = RemappedBatch(items)
+    batch.run()
+    return batch.results()
 
 
 def _first_capacity(n: int) -> int:

@@ -162,8 +162,7 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     if (nsegs) {
         auto *dj = reinterpret_cast<DecompressJob *>(host.data());
         auto *ds = reinterpret_cast<RemapSegment *>(segs.data());
-        auto *dev = reinterpret_cast<const RemapSegment *>(static_cast<uint8_t *>(workspace) +
-                                                           seg_at);
+        auto *dev = (BF16D_GMEM const RemapSegment *)(static_cast<uint8_t *>(workspace) + seg_at);
         size_t at = 0;
         for (uint32_t j = 0; j < count; ++j) {
             if (remaps[j].count == 0) continue;

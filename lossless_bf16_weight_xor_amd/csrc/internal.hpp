@@ -84,7 +84,7 @@ struct alignas(64) DecompressJob {
     uint64_t block0;   // first global tile index
     uint64_t nb;       // blocks
     uint64_t dtile0;   // first global descriptor-scan tile index
-    const RemapSegment *segs;   // remapped: the job's segments; else nullptr
+    BF16D_GMEM const RemapSegment *segs;   // remapped: the job's segments; else nullptr
     uint32_t nsegs;             // 0: no remap, the weights pointer is used
 };
 
