@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
 }
 
 // ---------------------------------------------------------------- finalize ---
-// One workgroup per job: header, checksum and result.
+// One thread per job: header, checksum and result.
 __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     const CompressJob *__restrict__ jobs, const JobSums *__restrict__ sums, uint32_t count,
     bf16d_result *__restrict__ results) {
