@@ -23,6 +23,8 @@ Reported:
               timed with events recorded around it on its stream
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
+  codec_race : the host race of general-purpose codecs over every payload,
+              and the payload % of the weights after it
   streamed_receiver : the same decompress with the payloads in pinned host
               memory, copied in layer by layer while the previous layer is
               applied (PCIe-inclusive; context, not `value`)
@@ -176,6 +178,34 @@ def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_g
             "overlap": round((th + td) / ts, 3)}
 
 
+def codec_race(bd, payloads, threads):
+    """The host codec race over every payload (trainer side), then the race
+    decode into one pinned buffer (receiver side), on `threads` CPU threads.
+    The pages give 0.19% of the BF16 weight size as the average payload of
+    real RL deltas; this workload's changes are synthetic, so that figure is
+    context only."""
+    host = [p.cpu() for p in payloads]
+    raw = sum(h.numel() for h in host)
+    t0 = time.perf_counter()
+    frames = bd.race_compress(host, bd.DEFAULT_RACE, threads=threads)
+    t_race = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    back = bd.race_decompress(frames, threads=threads, pin=True)
+    t_dec = time.perf_counter() - t0
+    assert all(torch.equal(a, b) for a, b in zip(back, host)), "race round trip not exact"
+    raced = sum(f.frame.numel() for f in frames)
+    winners = {}
+    for f in frames:
+        key = f"{f.codec}-{f.level}" if f.codec != "stored" else "stored"
+        winners[key] = winners.get(key, 0) + 1
+    return {"candidates": [f"{c}-{l}" for c, l in bd.DEFAULT_RACE], "threads": threads,
+            "structured_bytes": raw, "raced_bytes": raced,
+            "raced_over_structured": round(raced / raw, 4),
+            "race_s": round(t_race, 3), "race_mb_per_s": round(raw / t_race / 1e6, 1),
+            "decode_s": round(t_dec, 3), "decode_mb_per_s": round(raw / t_dec / 1e6, 1),
+            "winners": winners}
+
+
 def remapped(bd, names, shapes, pairs, payloads, cs_new, cs_old, steps):
     """The same batched decompress with every layer's gate and up projections
     paired in groups of 64 rows in one fused buffer (the physical layout of a
@@ -291,6 +321,10 @@ def main():
                     help="skip the streamed receiver (payloads in pinned host memory)")
     ap.add_argument("--no-remapped", action="store_true",
                     help="skip the remapped apply (gate/up paired in groups of 64 rows)")
+    ap.add_argument("--no-race", action="store_true",
+                    help="skip the host codec race over the payloads")
+    ap.add_argument("--race-threads", type=int, default=16,
+                    help="CPU threads of the codec race (capped at the host's cores)")
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -412,6 +446,13 @@ def main():
         remap_info = remapped(bd, names, [sp.shape for sp in specs], pairs, payloads, cs_new,
                               cs_old, 4)
 
+    race_info = None
+    if not args.no_race:
+        race_info = codec_race(bd, payloads, max(1, min(args.race_threads, os.cpu_count() or 1)))
+        race_info["payload_pct_after_race"] = round(100 * race_info["raced_bytes"] / w_bytes, 4)
+        log(f"codec race: {race_info['raced_bytes']} B "
+            f"({race_info['payload_pct_after_race']}% of orig) in {race_info['race_s']} s")
+
     gpu_payloads = [None] * len(pairs)
     cpu = None
     if args.cpu_budget > 0:
@@ -455,6 +496,7 @@ def main():
                                 "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,
+        "codec_race": race_info,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

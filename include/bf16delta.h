@@ -93,6 +93,7 @@ extern "C" {
 #define BF16D_EFORMAT   3  /* decompress: malformed or mismatched payload; weights end old */
 #define BF16D_ECHECKSUM 4  /* decompress: rebuilt weights fail the checksum; weights end old */
 #define BF16D_EHIP      5  /* a HIP runtime call failed */
+#define BF16D_ECODEC    6  /* codec race: the frame's codec library is not available here */
 
 #define BF16D_BLOCK_ELEMS    8192
 #define BF16D_HEADER_BYTES   64
@@ -315,6 +316,105 @@ int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
                               void *workspace, size_t workspace_bytes,
                               bf16d_result *results,
                               hipStream_t compute, hipStream_t copy);
+
+/* Codec race (host only): general-purpose compression of payloads.
+ *
+ * "Every byte counts: ARCv3 and the case for cross-region RL", section "Deep
+ * dive into ARCv3": on top of the structured encoding, every tensor's output
+ * is compressed by several general-purpose algorithms running in parallel on
+ * the CPU, and the smallest result is kept.  The pages name no codec.  Here
+ * the candidates are the caller's list of (codec, level) pairs drawn from
+ * zstd, LZ4, LZ4-HC, zlib, Brotli and xz; their runtime libraries
+ * (libzstd.so.1, liblz4.so.1, libz.so.1, libbrotlienc.so.1 /
+ * libbrotlidec.so.1, liblzma.so.5) are opened on first use, so a host without
+ * one of them only loses that codec.  These calls touch no GPU.
+ *
+ * Frame, little-endian:
+ *   magic "BF16DRC1", u32 codec, i32 level, u64 raw_bytes, u64 raw_hash,
+ *   then the body: the codec's standard output for the raw bytes (zstd
+ *   frame, LZ4 block, zlib stream, Brotli stream, xz stream), or the raw
+ *   bytes themselves for BF16D_CODEC_STORED.
+ *   raw_hash = mix64(S ^ raw_bytes), S = sum mod 2^64 of
+ *   mix64(W_k ^ (k + 1) * 0x9E3779B97F4A7C15) over the little-endian u64
+ *   words W_k of the raw bytes, the last one zero-padded (the construction of
+ *   the weights' checksum, over bytes).
+ * Levels: zstd -5..22; LZ4 acceleration 1..65537; LZ4-HC 1..12; zlib 1..9;
+ * Brotli quality 0..11 (window 2^22); xz preset 0..6 (CRC32 check).
+ * LZ4 and LZ4-HC take inputs below 0x7E000000 bytes; larger inputs skip
+ * them. */
+#define BF16D_CODEC_STORED 0
+#define BF16D_CODEC_ZSTD   1
+#define BF16D_CODEC_LZ4    2
+#define BF16D_CODEC_LZ4HC  3
+#define BF16D_CODEC_ZLIB   4
+#define BF16D_CODEC_BROTLI 5
+#define BF16D_CODEC_XZ     6
+#define BF16D_RACE_FRAME_HEADER 32
+
+/* One candidate of the race. */
+typedef struct bf16d_codec {
+    uint32_t codec;
+    int32_t  level;
+} bf16d_codec;
+
+/* One buffer to compress or decompress.  All pointers are host memory.
+ *   in, in_bytes      : the input (race_compress: a payload; race_decompress:
+ *                       a frame).  in may be NULL when in_bytes is 0.
+ *   out, out_capacity : the output buffer, owned by the caller; it must not
+ *                       overlap in.
+ *   out_bytes         : written by the call: bytes stored in out.
+ *   codec, level      : written by the call: the frame's codec and level.
+ *   status            : written by the call: BF16D_OK or, for
+ *                       race_decompress, the job's error. */
+typedef struct bf16d_race_job {
+    const uint8_t *in;
+    uint64_t       in_bytes;
+    uint8_t       *out;
+    uint64_t       out_capacity;
+    uint64_t       out_bytes;
+    uint32_t       codec;
+    int32_t        level;
+    int32_t        status;
+    uint32_t       reserved;
+} bf16d_race_job;
+
+/* 1 if the codec's runtime library could be opened on this host (the stored
+ * codec always is), else 0. */
+int bf16d_codec_available(uint32_t codec);
+
+/* Frame bytes that always suffice for a raw input of `bytes`: the header plus
+ * the input (a frame never exceeds the stored one). */
+uint64_t bf16d_race_bound(uint64_t bytes);
+
+/* Race the candidates over every job's input and keep, per job, the smallest
+ * frame.  The stored frame always takes part and wins ties; among codecs a
+ * tie goes to the earlier candidate, so the result does not depend on thread
+ * timing.  Jobs and candidates run on `threads` host threads (0: one per
+ * hardware thread; at most 1024), largest inputs first.
+ * out_capacity must be at least bf16d_race_bound(in_bytes).  Returns
+ * BF16D_EINVAL, with nothing written, for a NULL array or pointer, a short
+ * output, an unknown codec, a level out of range, a codec that is not
+ * available, or more than 64 candidates.  Otherwise every job ends BF16D_OK:
+ * a codec that fails simply loses. */
+int bf16d_race_compress(bf16d_race_job *jobs, uint32_t count,
+                        const bf16d_codec *candidates, uint32_t n_candidates,
+                        uint32_t threads);
+
+/* Read a frame's header: raw size, codec and level (any of the out-pointers
+ * may be NULL).  Returns BF16D_EFORMAT for a short frame, a bad magic or an
+ * unknown codec, else BF16D_OK. */
+int bf16d_race_frame_info(const uint8_t *frame, uint64_t frame_bytes, uint64_t *raw_bytes,
+                          uint32_t *codec, int32_t *level);
+
+/* Decode every job's frame into its output, on `threads` host threads as
+ * above.  Per job: BF16D_EFORMAT for a malformed frame, a body the codec
+ * rejects, or a decoded size other than the header's; BF16D_ECAPACITY if
+ * out_capacity is below the raw size (nothing written); BF16D_ECODEC if the
+ * codec's library is not available; BF16D_EFORMAT also when the decoded
+ * bytes fail raw_hash; else BF16D_OK with out_bytes = raw size.
+ * The bytes of out are unspecified after an error.  Returns BF16D_EINVAL for
+ * a NULL array or a NULL pointer with a non-zero size, else BF16D_OK. */
+int bf16d_race_decompress(bf16d_race_job *jobs, uint32_t count, uint32_t threads);
 
 /* Human-readable name of a status code (static storage). */
 const char *bf16d_status_string(int status);

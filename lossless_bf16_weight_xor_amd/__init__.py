@@ -3,7 +3,9 @@
 Python binding of libbf16delta (include/bf16delta.h).  It only marshals
 arguments: torch tensors supply device memory and streams, and every step of
 compression and decompression runs in the library's HIP kernels.  There is no
-CPU fallback; tensors must live on a HIP device.
+CPU fallback; tensors must live on a HIP device.  The one host step is the
+codec race over finished payloads (race_compress / race_decompress), which the
+pages run on the CPU by design; it too runs in the library.
 
 The call shapes follow "Every byte counts: ARCv3 and the case for
 cross-region RL", section "Using ARCv3":
@@ -29,7 +31,8 @@ _ALIGN = 256   # payload slots inside an arena start on this boundary
 
 __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_batch",
            "CompressBatch", "DecompressBatch", "StreamedDecompress", "RemappedBatch",
-           "decompress_remapped", "FormatError", "ChecksumError",
+           "decompress_remapped", "race_compress", "race_decompress", "codec_available",
+           "RaceFrame", "DEFAULT_RACE", "FormatError", "ChecksumError",
            "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
 
 
@@ -392,3 +395,106 @@ def delta_decompress(src: torch.Tensor, compressed_diff: torch.Tensor, checksum:
     if r["status"] != OK:
         raise RuntimeError(_native.status_string(r["status"]))
     return src
+
+
+# ------------------------------------------------------------- codec race ---
+# The one host step of the path: "Every byte counts: ARCv3 and the case for
+# cross-region RL", section "Deep dive into ARCv3", races general-purpose
+# codecs over each tensor's output on the CPU and keeps the smallest.  The race
+# itself runs in the library (bf16d_race_compress / bf16d_race_decompress);
+# this only marshals host buffers.
+
+# candidates raced when the caller names none: fast and strong settings of the
+# common families, about 4 minutes of one core per GB of payload; xz and the
+# highest levels are left to callers with more idle cores
+DEFAULT_RACE = (("lz4", 1), ("zstd", 1), ("zstd", 3), ("zstd", 9), ("zlib", 6), ("brotli", 5))
+
+
+class RaceFrame(tuple):
+    """(frame uint8 host tensor, codec name, level) of one raced payload."""
+    __slots__ = ()
+
+    def __new__(cls, frame, codec, level):
+        return super().__new__(cls, (frame, codec, level))
+
+    frame = property(lambda self: self[0])
+    codec = property(lambda self: self[1])
+    level = property(lambda self: self[2])
+
+
+_CODEC_NAMES = {v: k for k, v in _native.CODECS.items()}
+
+
+def codec_available(name: str) -> bool:
+    """Whether this host has the runtime library of codec `name`."""
+    return bool(_native.lib().bf16d_codec_available(_native.CODECS[name]))
+
+
+def _host_u8(buf, what: str) -> torch.Tensor:
+    if not isinstance(buf, torch.Tensor):
+        buf = torch.from_numpy(buf) if hasattr(buf, "__array_interface__") else buf
+    if (not isinstance(buf, torch.Tensor) or buf.device.type != "cpu"
+            or buf.dtype != torch.uint8 or not buf.is_contiguous()):
+        raise TypeError(f"{what} must be a contiguous uint8 buffer in host memory")
+    return buf.reshape(-1)
+
+
+def _ptr(t: torch.Tensor):
+    return t.data_ptr() if t.numel() else None
+
+
+def race_compress(payloads, candidates=DEFAULT_RACE, threads: int = 0) -> list[RaceFrame]:
+    """Race `candidates` ((codec name, level) pairs) over every host payload on
+    `threads` CPU threads (0: all) and return each payload's smallest frame."""
+    ins = [_host_u8(p, "payload") for p in payloads]
+    cands = (_native.Codec * max(len(candidates), 1))()
+    for k, (name, level) in enumerate(candidates):
+        if name not in _native.CODECS:
+            raise ValueError(f"unknown codec {name!r}")
+        cands[k] = _native.Codec(_native.CODECS[name], level)
+    lib = _native.lib()
+    outs = [torch.empty(int(lib.bf16d_race_bound(t.numel())), dtype=torch.uint8) for t in ins]
+    jobs = (_native.RaceJob * max(len(ins), 1))()
+    for j, (t, o) in enumerate(zip(ins, outs)):
+        jobs[j] = _native.RaceJob(_ptr(t), t.numel(), o.data_ptr(), o.numel(), 0, 0, 0, 0, 0)
+    rc = lib.bf16d_race_compress(jobs, len(ins), cands, len(candidates), threads)
+    if rc != OK:
+        raise ValueError(f"bf16d_race_compress: {_native.status_string(rc)} (an unknown or "
+                         f"unavailable codec, or a level out of range)")
+    return [RaceFrame(o[:jobs[j].out_bytes], _CODEC_NAMES[jobs[j].codec], jobs[j].level)
+            for j, o in enumerate(outs)]
+
+
+def race_decompress(frames, threads: int = 0, pin: bool = False) -> list[torch.Tensor]:
+    """Decode race frames back into payloads (uint8 host tensors).  With
+    pin=True the payloads are packed into one pinned buffer at 16-byte
+    boundaries, the layout StreamedDecompress copies in one transfer per
+    group.  Raises FormatError for a malformed frame."""
+    ins = [_host_u8(f[0] if isinstance(f, RaceFrame) else f, "frame") for f in frames]
+    lib = _native.lib()
+    raw = []
+    for t in ins:
+        n = ctypes.c_uint64(0)
+        if lib.bf16d_race_frame_info(_ptr(t), t.numel(), ctypes.byref(n), None, None) != OK:
+            raise FormatError("not a race frame")
+        raw.append(n.value)
+    pad16 = lambda b: (b + 15) // 16 * 16
+    if pin:
+        flat = torch.empty(max(sum(pad16(b) for b in raw), 16), dtype=torch.uint8,
+                           pin_memory=True)
+        at = [0]
+        for b in raw[:-1]:
+            at.append(at[-1] + pad16(b))
+        outs = [flat[a:a + b] for a, b in zip(at, raw)]
+    else:
+        outs = [torch.empty(b, dtype=torch.uint8) for b in raw]
+    jobs = (_native.RaceJob * max(len(ins), 1))()
+    for j, (t, o) in enumerate(zip(ins, outs)):
+        jobs[j] = _native.RaceJob(_ptr(t), t.numel(), _ptr(o), o.numel(), 0, 0, 0, 0, 0)
+    rc = lib.bf16d_race_decompress(jobs, len(ins), threads)
+    _check_rc(rc, "bf16d_race_decompress")
+    for j in range(len(ins)):
+        if jobs[j].status != OK:
+            err = FormatError if jobs[j].status == EFORMAT else RuntimeError
+            raise err(f"frame {j}: {_native.status_string(jobs[j].status)}")
+    return outs

@@ -13,7 +13,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library must share)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta.so")
 
-OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP = 0, 1, 2, 3, 4, 5
+OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, ECODEC = 0, 1, 2, 3, 4, 5, 6
 BLOCK_ELEMS = 8192
 HEADER_BYTES = 64
 FORMAT_VERSION = 1
@@ -22,7 +22,12 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress"
             "bf16d_decompress", "bf16d_compress_ex", "bf16d_decompress_ex",
             "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_decompress_streamed",
             "bf16d_decompress_remapped", "bf16d_workspace_bytes_remapped",
-            "bf16d_status_string", "bf16d_format_version")
+            "bf16d_status_string", "bf16d_format_version", "bf16d_codec_available",
+            "bf16d_race_bound", "bf16d_race_compress", "bf16d_race_frame_info",
+            "bf16d_race_decompress")
+
+CODECS = {"stored": 0, "zstd": 1, "lz4": 2, "lz4hc": 3, "zlib": 4, "brotli": 5, "xz": 6}
+RACE_FRAME_HEADER = 32
 
 
 class Result(ctypes.Structure):
@@ -55,6 +60,18 @@ class Segment(ctypes.Structure):
 
 class Remap(ctypes.Structure):
     _fields_ = [("segments", ctypes.POINTER(Segment)), ("count", ctypes.c_uint32)]
+
+
+class Codec(ctypes.Structure):
+    _fields_ = [("codec", ctypes.c_uint32), ("level", ctypes.c_int32)]
+
+
+class RaceJob(ctypes.Structure):
+    _fields_ = [("in_", ctypes.c_void_p), ("in_bytes", ctypes.c_uint64),
+                ("out", ctypes.c_void_p), ("out_capacity", ctypes.c_uint64),
+                ("out_bytes", ctypes.c_uint64), ("codec", ctypes.c_uint32),
+                ("level", ctypes.c_int32), ("status", ctypes.c_int32),
+                ("reserved", ctypes.c_uint32)]
 
 
 class Events(ctypes.Structure):
@@ -111,6 +128,19 @@ def lib():
         L.bf16d_status_string.restype = ctypes.c_char_p
         L.bf16d_format_version.argtypes = []
         L.bf16d_format_version.restype = ctypes.c_int
+        L.bf16d_codec_available.argtypes = [u32]
+        L.bf16d_codec_available.restype = ctypes.c_int
+        L.bf16d_race_bound.argtypes = [u64]
+        L.bf16d_race_bound.restype = u64
+        L.bf16d_race_compress.argtypes = [ctypes.POINTER(RaceJob), u32, ctypes.POINTER(Codec),
+                                          u32, u32]
+        L.bf16d_race_compress.restype = ctypes.c_int
+        L.bf16d_race_frame_info.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint64),
+                                            ctypes.POINTER(ctypes.c_uint32),
+                                            ctypes.POINTER(ctypes.c_int32)]
+        L.bf16d_race_frame_info.restype = ctypes.c_int
+        L.bf16d_race_decompress.argtypes = [ctypes.POINTER(RaceJob), u32, u32]
+        L.bf16d_race_decompress.restype = ctypes.c_int
         _lib = L
     return _lib
 

@@ -312,6 +312,7 @@ const char *bf16d_status_string(int status) {
         case BF16D_EFORMAT: return "EFORMAT: malformed or mismatched payload";
         case BF16D_ECHECKSUM: return "ECHECKSUM: rebuilt weights fail the checksum";
         case BF16D_EHIP: return "EHIP: HIP runtime error";
+        case BF16D_ECODEC: return "ECODEC: codec library not available";
         default: return "unknown status";
     }
 }

@@ -84,3 +84,20 @@ def test_streamed_many_groups_reuse_both_slots_in_turn():
     assert all(r["status"] == bd.OK for r in res)
     for w, (_, d) in zip(recv, pairs):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16))
+
+
+def test_raced_payloads_stream_into_the_receiver():
+    """The whole trip: GPU compress, the host codec race on the trainer side,
+    race decode into one pinned buffer on the receiver side, then the
+    streamed apply.  Every tensor must come out bit for bit."""
+    log("case raced payloads -> streamed receiver")
+    pairs, payloads, checksums = _make(seed0=1700)
+    frames = bd.race_compress([p.cpu() for p in payloads], bd.DEFAULT_RACE, threads=8)
+    assert sum(f.frame.numel() for f in frames) <= sum(32 + p.numel() for p in payloads)
+    raw = bd.race_decompress(frames, threads=8, pin=True)
+    for q, p in zip(raw, payloads):
+        assert torch.equal(q, p.cpu())
+    recv, res = _run(pairs, raw, checksums, [4, 4, 4])
+    assert [r["status"] for r in res] == [bd.OK] * len(pairs)
+    for w, (_, d) in zip(recv, pairs):
+        assert torch.equal(w.view(torch.int16), d.view(torch.int16))
