@@ -24,9 +24,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbf16delta_oracle.so")
 
-OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM = 0, 1, 2, 3, 4
+OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EVERSION = 0, 1, 2, 3, 4, 7
 STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", ECAPACITY: "ECAPACITY",
-                EFORMAT: "EFORMAT", ECHECKSUM: "ECHECKSUM"}
+                EFORMAT: "EFORMAT", ECHECKSUM: "ECHECKSUM", EVERSION: "EVERSION"}
+FLAG_OVERWRITE = 1
+HEADER_V2_BYTES = 96
 
 
 class _RefResult(ctypes.Structure):
@@ -64,6 +66,11 @@ def _load():
         lib.bf16d_ref_compress.restype = ctypes.c_int
         lib.bf16d_ref_decompress.argtypes = [p, u64, p, u64, u64]
         lib.bf16d_ref_decompress.restype = ctypes.c_int
+        lib.bf16d_ref_compress_v2.argtypes = [p, p, u64, u64, u64, ctypes.c_uint32, p, u64,
+                                              ctypes.POINTER(_RefResult)]
+        lib.bf16d_ref_compress_v2.restype = ctypes.c_int
+        lib.bf16d_ref_decompress_v2.argtypes = [p, u64, p, u64, u64, p]
+        lib.bf16d_ref_decompress_v2.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -121,3 +128,50 @@ def decompress_inplace(weights: np.ndarray, payload, checksum_value: int) -> int
     return int(_load().bf16d_ref_decompress(weights.ctypes.data, weights.size,
                                             ptr, pay.size,
                                             checksum_value & 0xFFFFFFFFFFFFFFFF))
+
+
+# ------------------------------------------------------------- version 2 ---
+
+def compress_v2_raw(src, dst, base_version: int, target_version: int, flags: int = 0,
+                    capacity: int | None = None):
+    """Version-2 encode (binding, and with flags & FLAG_OVERWRITE absolute
+    values); returns (status, payload ndarray of `capacity` bytes, stats)."""
+    src, dst = _u16(src), _u16(dst)
+    if src.size != dst.size:
+        raise ValueError("src and dst differ in length")
+    n = src.size
+    if capacity is None:
+        capacity = max_payload_bytes(n) + 32
+    buf = np.zeros(max(capacity, 1), dtype=np.uint8)
+    res = _RefResult()
+    st = _load().bf16d_ref_compress_v2(src.ctypes.data, dst.ctypes.data, n,
+                                       base_version & 0xFFFFFFFFFFFFFFFF,
+                                       target_version & 0xFFFFFFFFFFFFFFFF, flags,
+                                       buf.ctypes.data, capacity, ctypes.byref(res))
+    stats = {k: int(getattr(res, k)) for k, _ in _RefResult._fields_}
+    return int(st), buf[:capacity], stats
+
+
+def compress_v2(src, dst, base_version: int, target_version: int, overwrite: bool = False):
+    """Returns (payload ndarray[uint8], checksum, stats) of a version-2 payload."""
+    st, buf, stats = compress_v2_raw(src, dst, base_version, target_version,
+                                     FLAG_OVERWRITE if overwrite else 0)
+    if st != OK:
+        raise RuntimeError(f"oracle compress_v2 failed: {STATUS_NAMES.get(st, st)}")
+    return buf[:stats["payload_bytes"]].copy(), stats["checksum"], stats
+
+
+def decompress_v2_inplace(weights: np.ndarray, payload, checksum_value: int,
+                          version: int | None):
+    """Apply a version-1 or -2 payload with the receiver's version word
+    (None: no word, the binding is not checked).  Returns (status, version
+    word after the call)."""
+    if weights.dtype != np.uint16 or not weights.flags["C_CONTIGUOUS"]:
+        raise TypeError("weights must be a C-contiguous uint16 array")
+    pay = np.ascontiguousarray(payload, dtype=np.uint8).reshape(-1)
+    ptr = pay.ctypes.data if pay.size else None
+    word = None if version is None else np.array([version & 0xFFFFFFFFFFFFFFFF], np.uint64)
+    st = _load().bf16d_ref_decompress_v2(weights.ctypes.data, weights.size, ptr, pay.size,
+                                         checksum_value & 0xFFFFFFFFFFFFFFFF,
+                                         None if word is None else word.ctypes.data)
+    return int(st), (None if word is None else int(word[0]))

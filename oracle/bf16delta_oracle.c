@@ -24,6 +24,15 @@
  *   in place, verify the checksum; on any failure XOR the same mask again
  *   (XOR is its own inverse, "Delta update algebra") so the weights end as
  *   the old ones bit for bit.
+ *
+ *   version 2 (Weight Teleportation, "Eval, fault tolerance, and resuming
+ *   from trained checkpoints": deltas between versions other than the last
+ *   one; the Delta-Compressed Refit summary: absolute overwrites beside XOR
+ *   masks, retry-safe versioning with a joint commit): the header also binds
+ *   the payload to a base and a target version, and an overwrite payload
+ *   carries each changed element's new value instead of its XOR.  The
+ *   receiver's version word must equal the base before anything is touched,
+ *   and becomes the target only together with the new weights.
  */
 #include "bf16delta_oracle.h"
 
@@ -34,6 +43,10 @@
 #define BLOCK_ELEMS     8192u
 #define HEADER_BYTES    64u
 #define FORMAT_VERSION  1u
+/* version 2: a 32-byte binding block follows the v1 header fields */
+#define FORMAT_VERSION_BOUND 2u
+#define HEADER_BYTES_V2 96u
+#define FLAG_OVERWRITE  1u
 #define CODE_BITMAP     15u
 #define CODE_INVALID    14u
 #define EXP_SIGN_BITS   0xFF80u   /* sign (bit 15) and exponent (bits 7..14) */
@@ -145,6 +158,12 @@ static uint64_t pos_segment_bytes(uint32_t code, uint64_t c, uint64_t L) {
 static uint64_t mant_segment_bytes(uint64_t c) { return ceil_div(7 * c, 8); }
 static uint64_t rare_segment_bytes(uint64_t r) { return 2 * r; }
 
+/* An overwrite record has no mantissa segment: its word segment holds the
+ * new value of every changed element (r == c). */
+static uint64_t mant_bytes_mode(uint64_t c, int overwrite) {
+    return overwrite ? 0 : mant_segment_bytes(c);
+}
+
 uint64_t bf16d_ref_max_payload_bytes(uint64_t n) {
     /* per block: position segment <= bitmap size (the smaller encoding is
      * always taken), every element changed and rare for the value streams */
@@ -162,7 +181,7 @@ uint64_t bf16d_ref_max_payload_bytes(uint64_t n) {
 /* One block: fills rec[] (zeroed by the caller, >= 3*8192+2 bytes), returns
  * the record length and the descriptor. */
 static uint64_t encode_block(const uint16_t *src, const uint16_t *dst, uint64_t L,
-                             uint8_t *rec, uint32_t *desc_out,
+                             int overwrite, uint8_t *rec, uint32_t *desc_out,
                              uint64_t *c_out, uint64_t *r_out, int *is_bitmap) {
     uint16_t pos[BLOCK_ELEMS];
     uint16_t val[BLOCK_ELEMS];
@@ -201,6 +220,21 @@ static uint64_t encode_block(const uint16_t *src, const uint16_t *dst, uint64_t 
         }
     }
 
+    if (overwrite) {
+        /* word segment: the absolute new value of every changed element */
+        uint8_t *words = rec + pb;
+        for (uint64_t j = 0; j < c; j++) {
+            uint16_t v = dst[pos[j]];
+            words[2 * j] = (uint8_t)(v & 0xFF);
+            words[2 * j + 1] = (uint8_t)(v >> 8);
+        }
+        *desc_out = (uint32_t)c | ((uint32_t)c << 14) | (code << 28);
+        *c_out = c;
+        *r_out = c;
+        *is_bitmap = (code == CODE_BITMAP);
+        return pb + rare_segment_bytes(c);
+    }
+
     /* mantissa segment: 7-bit mantissa XOR, 0 = "see the rare stream" */
     uint64_t mb = mant_segment_bytes(c);
     for (uint64_t j = 0; j < c; j++) {
@@ -225,15 +259,21 @@ static uint64_t encode_block(const uint16_t *src, const uint16_t *dst, uint64_t 
     return pb + mb + rare_segment_bytes(r);
 }
 
-int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
-                       uint8_t *payload, uint64_t capacity, ref_result *res) {
+/* bound: 0 writes a version-1 payload; otherwise version 2 with the given
+ * binding and flags. */
+static int compress_any(const uint16_t *src, const uint16_t *dst, uint64_t n, int bound,
+                        uint64_t base_version, uint64_t target_version, uint32_t flags,
+                        uint8_t *payload, uint64_t capacity, ref_result *res) {
     if (res == NULL) return REF_EINVAL;
     memset(res, 0, sizeof(*res));
     if (n > 0 && (src == NULL || dst == NULL)) return REF_EINVAL;
     if (payload == NULL && capacity > 0) return REF_EINVAL;
+    if ((flags & ~FLAG_OVERWRITE) != 0 || (!bound && flags != 0)) return REF_EINVAL;
+    const int overwrite = (flags & FLAG_OVERWRITE) != 0;
+    const uint64_t hdr = bound ? HEADER_BYTES_V2 : HEADER_BYTES;
 
     uint64_t nb = ceil_div(n, BLOCK_ELEMS);
-    uint64_t data_off = HEADER_BYTES + 4 * nb;
+    uint64_t data_off = hdr + 4 * nb;
     uint8_t *rec = (uint8_t *)malloc(3 * BLOCK_ELEMS + 16);
     if (rec == NULL) return REF_EINVAL;
 
@@ -247,10 +287,10 @@ int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
         int is_bitmap;
         memset(rec, 0, 3 * BLOCK_ELEMS + 16);
         uint64_t len = encode_block(src + b * BLOCK_ELEMS, dst + b * BLOCK_ELEMS, L,
-                                    rec, &desc, &c, &r, &is_bitmap);
+                                    overwrite, rec, &desc, &c, &r, &is_bitmap);
         /* descriptor table entry b, then the record at the running offset;
          * nothing is written at or beyond capacity */
-        uint64_t desc_at = HEADER_BYTES + 4 * b;
+        uint64_t desc_at = hdr + 4 * b;
         if (desc_at + 4 <= capacity) put_u32(payload + desc_at, desc);
         for (uint64_t i = 0; i < len; i++)
             if (off + i < capacity) payload[off + i] = rec[i];
@@ -260,7 +300,7 @@ int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
         n_rare += r;
         n_bitmap += (uint64_t)is_bitmap;
         pos_total += pos_segment_bytes(desc >> 28, c, L);
-        mant_total += mant_segment_bytes(c);
+        mant_total += mant_bytes_mode(c, overwrite);
         rare_total += rare_segment_bytes(r);
     }
     free(rec);
@@ -274,7 +314,7 @@ int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
 
     /* header */
     memcpy(payload, MAGIC, 8);
-    put_u32(payload + 8, FORMAT_VERSION);
+    put_u32(payload + 8, bound ? FORMAT_VERSION_BOUND : FORMAT_VERSION);
     put_u32(payload + 12, BLOCK_ELEMS);
     put_u64(payload + 16, n);
     put_u64(payload + 24, n_changed);
@@ -282,20 +322,39 @@ int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
     put_u64(payload + 40, pos_total);
     put_u64(payload + 48, mant_total);
     put_u64(payload + 56, rare_total);
+    if (bound) {
+        put_u64(payload + 64, base_version);
+        put_u64(payload + 72, target_version);
+        put_u32(payload + 80, flags);
+        put_u32(payload + 84, 0);
+        put_u64(payload + 88, 0);
+    }
     return REF_OK;
+}
+
+int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
+                       uint8_t *payload, uint64_t capacity, ref_result *res) {
+    return compress_any(src, dst, n, 0, 0, 0, 0, payload, capacity, res);
+}
+
+int bf16d_ref_compress_v2(const uint16_t *src, const uint16_t *dst, uint64_t n,
+                          uint64_t base_version, uint64_t target_version, uint32_t flags,
+                          uint8_t *payload, uint64_t capacity, ref_result *res) {
+    return compress_any(src, dst, n, 1, base_version, target_version, flags, payload,
+                        capacity, res);
 }
 
 /* ---- decoder ----------------------------------------------------------- */
 
 /* Decode and check one block record; on success fill pos[]/val[] (c entries)
  * and return 1, on any malformation return 0. */
-static int decode_block(const uint8_t *rec, uint32_t desc, uint64_t L,
+static int decode_block(const uint8_t *rec, uint32_t desc, uint64_t L, int overwrite,
                         uint16_t *pos, uint16_t *val) {
     uint64_t c = desc & 0x3FFFu;
     uint64_t r = (desc >> 14) & 0x3FFFu;
     uint32_t code = desc >> 28;
     uint64_t pb = pos_segment_bytes(code, c, L);
-    uint64_t mb = mant_segment_bytes(c);
+    uint64_t mb = mant_bytes_mode(c, overwrite);
     const uint8_t *mant = rec + pb;
     const uint8_t *rare = rec + pb + mb;
 
@@ -333,6 +392,13 @@ static int decode_block(const uint8_t *rec, uint32_t desc, uint64_t L,
             if (get_bits(rec, k, 1)) return 0;
     }
 
+    /* overwrite record: the absolute new values, one word per position */
+    if (overwrite) {
+        for (uint64_t j = 0; j < c; j++)
+            val[j] = (uint16_t)(mant[2 * j] | (mant[2 * j + 1] << 8));
+        return 1;
+    }
+
     /* values: mantissa fields, zero escapes into the rare words */
     uint64_t next_rare = 0;
     for (uint64_t j = 0; j < c; j++) {
@@ -355,20 +421,26 @@ static int decode_block(const uint8_t *rec, uint32_t desc, uint64_t L,
 
 /* XOR every well-formed block's mask onto the weights; returns the number of
  * malformed blocks (which are left alone).  Running it twice is a no-op. */
-static uint64_t apply_pass(uint16_t *weights, uint64_t n, const uint8_t *payload) {
+static uint64_t apply_pass(uint16_t *weights, uint64_t n, const uint8_t *payload,
+                           uint64_t hdr, int overwrite) {
     uint16_t pos[BLOCK_ELEMS];
     uint16_t val[BLOCK_ELEMS];
     uint64_t nb = ceil_div(n, BLOCK_ELEMS);
-    uint64_t off = HEADER_BYTES + 4 * nb;
+    uint64_t off = hdr + 4 * nb;
     uint64_t bad = 0;
     for (uint64_t b = 0; b < nb; b++) {
         uint64_t L = block_len(n, b);
-        uint32_t desc = get_u32(payload + HEADER_BYTES + 4 * b);
+        uint32_t desc = get_u32(payload + hdr + 4 * b);
         uint64_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu;
-        uint64_t len = pos_segment_bytes(desc >> 28, c, L) + mant_segment_bytes(c) +
+        uint64_t len = pos_segment_bytes(desc >> 28, c, L) + mant_bytes_mode(c, overwrite) +
                        rare_segment_bytes(r);
-        if (decode_block(payload + off, desc, L, pos, val)) {
-            for (uint64_t j = 0; j < c; j++) weights[b * BLOCK_ELEMS + pos[j]] ^= val[j];
+        if (decode_block(payload + off, desc, L, overwrite, pos, val)) {
+            for (uint64_t j = 0; j < c; j++) {
+                if (overwrite)
+                    weights[b * BLOCK_ELEMS + pos[j]] = val[j];   /* absolute value */
+                else
+                    weights[b * BLOCK_ELEMS + pos[j]] ^= val[j];  /* XOR mask */
+            }
         } else {
             bad++;
         }
@@ -377,29 +449,44 @@ static uint64_t apply_pass(uint16_t *weights, uint64_t n, const uint8_t *payload
     return bad;
 }
 
-int bf16d_ref_decompress(uint16_t *weights, uint64_t n, const uint8_t *payload,
-                         uint64_t payload_bytes, uint64_t checksum) {
+int bf16d_ref_decompress_v2(uint16_t *weights, uint64_t n, const uint8_t *payload,
+                            uint64_t payload_bytes, uint64_t checksum, uint64_t *version) {
     if ((payload == NULL && payload_bytes > 0) || (n > 0 && weights == NULL)) return REF_EINVAL;
 
-    /* header */
+    /* header: version 1, or version 2 with its binding block */
     if (payload_bytes < HEADER_BYTES) return REF_EFORMAT;
     if (memcmp(payload, MAGIC, 8) != 0) return REF_EFORMAT;
-    if (get_u32(payload + 8) != FORMAT_VERSION) return REF_EFORMAT;
+    uint32_t fv = get_u32(payload + 8);
+    if (fv != FORMAT_VERSION && fv != FORMAT_VERSION_BOUND) return REF_EFORMAT;
+    const int bound = fv == FORMAT_VERSION_BOUND;
+    const uint64_t hdr = bound ? HEADER_BYTES_V2 : HEADER_BYTES;
+    if (payload_bytes < hdr) return REF_EFORMAT;
     if (get_u32(payload + 12) != BLOCK_ELEMS) return REF_EFORMAT;
     if (get_u64(payload + 16) != n) return REF_EFORMAT;
+    uint64_t base_version = 0, target_version = 0;
+    uint32_t flags = 0;
+    if (bound) {
+        base_version = get_u64(payload + 64);
+        target_version = get_u64(payload + 72);
+        flags = get_u32(payload + 80);
+        if ((flags & ~FLAG_OVERWRITE) != 0) return REF_EFORMAT;
+        if (get_u32(payload + 84) != 0 || get_u64(payload + 88) != 0) return REF_EFORMAT;
+    }
+    const int overwrite = (flags & FLAG_OVERWRITE) != 0;
     uint64_t nb = ceil_div(n, BLOCK_ELEMS);
-    if (payload_bytes < HEADER_BYTES + 4 * nb) return REF_EFORMAT;
+    if (payload_bytes < hdr + 4 * nb) return REF_EFORMAT;
 
     /* descriptor table: each entry well formed and in canonical mode, and
      * the totals agree with the header and with the payload length */
     uint64_t sum_c = 0, sum_r = 0, sum_pos = 0, sum_mant = 0, sum_rare = 0;
     for (uint64_t b = 0; b < nb; b++) {
         uint64_t L = block_len(n, b);
-        uint32_t desc = get_u32(payload + HEADER_BYTES + 4 * b);
+        uint32_t desc = get_u32(payload + hdr + 4 * b);
         uint64_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu;
         uint32_t code = desc >> 28;
         if (code == CODE_INVALID) return REF_EFORMAT;
         if (c > L || r > c) return REF_EFORMAT;
+        if (overwrite && r != c) return REF_EFORMAT;   /* one word per change */
         if (code == CODE_BITMAP) {
             if (c == 0) return REF_EFORMAT;
         } else {
@@ -409,25 +496,52 @@ int bf16d_ref_decompress(uint16_t *weights, uint64_t n, const uint8_t *payload,
         sum_c += c;
         sum_r += r;
         sum_pos += pos_segment_bytes(code, c, L);
-        sum_mant += mant_segment_bytes(c);
+        sum_mant += mant_bytes_mode(c, overwrite);
         sum_rare += rare_segment_bytes(r);
     }
     if (sum_c != get_u64(payload + 24) || sum_r != get_u64(payload + 32) ||
         sum_pos != get_u64(payload + 40) || sum_mant != get_u64(payload + 48) ||
         sum_rare != get_u64(payload + 56))
         return REF_EFORMAT;
-    if (HEADER_BYTES + 4 * nb + sum_pos + sum_mant + sum_rare != payload_bytes)
+    if (hdr + 4 * nb + sum_pos + sum_mant + sum_rare != payload_bytes)
         return REF_EFORMAT;
 
-    /* apply; a malformed block or a checksum mismatch undoes the pass */
-    uint64_t bad = apply_pass(weights, n, payload);
-    if (bad != 0) {
-        apply_pass(weights, n, payload);
-        return REF_EFORMAT;
+    /* the binding: a version-2 payload applies only to the version it was
+     * made against; nothing is touched otherwise */
+    if (bound && version != NULL && *version != base_version) return REF_EVERSION;
+
+    if (overwrite) {
+        /* absolute values cannot be undone by applying them again, so the
+         * result is built and checked in a copy, and written back only when
+         * it is right */
+        uint16_t *tmp = (uint16_t *)malloc(2 * n + 2);
+        if (tmp == NULL) return REF_EINVAL;
+        if (n) memcpy(tmp, weights, 2 * n);
+        uint64_t bad = apply_pass(tmp, n, payload, hdr, 1);
+        int st = REF_OK;
+        if (bad != 0) st = REF_EFORMAT;
+        else if (bf16d_ref_checksum(tmp, n) != checksum) st = REF_ECHECKSUM;
+        if (st == REF_OK && n) memcpy(weights, tmp, 2 * n);
+        free(tmp);
+        if (st != REF_OK) return st;
+    } else {
+        /* apply; a malformed block or a checksum mismatch undoes the pass */
+        uint64_t bad = apply_pass(weights, n, payload, hdr, 0);
+        if (bad != 0) {
+            apply_pass(weights, n, payload, hdr, 0);
+            return REF_EFORMAT;
+        }
+        if (bf16d_ref_checksum(weights, n) != checksum) {
+            apply_pass(weights, n, payload, hdr, 0);
+            return REF_ECHECKSUM;
+        }
     }
-    if (bf16d_ref_checksum(weights, n) != checksum) {
-        apply_pass(weights, n, payload);
-        return REF_ECHECKSUM;
-    }
+    /* joint commit: the weights and the version word move together */
+    if (bound && version != NULL) *version = target_version;
     return REF_OK;
+}
+
+int bf16d_ref_decompress(uint16_t *weights, uint64_t n, const uint8_t *payload,
+                         uint64_t payload_bytes, uint64_t checksum) {
+    return bf16d_ref_decompress_v2(weights, n, payload, payload_bytes, checksum, NULL);
 }

@@ -46,6 +46,7 @@ extern "C" {
 #define REF_ECAPACITY 2
 #define REF_EFORMAT   3
 #define REF_ECHECKSUM 4
+#define REF_EVERSION  7
 
 typedef struct ref_result {
     uint64_t payload_bytes;   /* bytes written, or bytes required on REF_ECAPACITY */
@@ -69,9 +70,35 @@ int bf16d_ref_compress(const uint16_t *src, const uint16_t *dst, uint64_t n,
                        uint8_t *payload, uint64_t capacity, ref_result *res);
 
 /* Apply payload onto weights (old -> new) in place; weights end new on
- * REF_OK and bit-exactly old on every other status. */
+ * REF_OK and bit-exactly old on every other status.  Reads version-1 and
+ * version-2 payloads; the binding of a version-2 payload is not checked. */
 int bf16d_ref_decompress(uint16_t *weights, uint64_t n, const uint8_t *payload,
                          uint64_t payload_bytes, uint64_t checksum);
+
+/* Version 2 ("GPU-accelerated Weight Teleportation", section "Eval, fault
+ * tolerance, and resuming from trained checkpoints", and the NeMo
+ * Delta-Compressed Refit summary: absolute overwrites beside XOR masks,
+ * retry-safe versioning with a joint commit).  The 64 bytes of the version-1
+ * header (with version = 2) are followed by u64 base_version, u64
+ * target_version, u32 flags, u32 0, u64 0; the descriptor table starts at
+ * byte 96.  flags bit 0 (overwrite): every changed element carries its new
+ * value as a 16-bit word right after the position segment (no mantissa
+ * segment; the descriptor's r equals c), and applying it sets the element to
+ * that value.  Records are otherwise those of version 1. */
+#define REF_FLAG_OVERWRITE 1u
+int bf16d_ref_compress_v2(const uint16_t *src, const uint16_t *dst, uint64_t n,
+                          uint64_t base_version, uint64_t target_version, uint32_t flags,
+                          uint8_t *payload, uint64_t capacity, ref_result *res);
+
+/* Apply a version-1 or version-2 payload.  version (may be NULL) is the
+ * receiver's version word: a version-2 payload whose base differs returns
+ * REF_EVERSION with nothing touched; on REF_OK it becomes the target.  An
+ * overwrite payload is built and checked in a copy and written only when the
+ * checksum matches, so the weights end new on REF_OK and untouched
+ * otherwise, whatever mix of old and new values they held at the changed
+ * positions. */
+int bf16d_ref_decompress_v2(uint16_t *weights, uint64_t n, const uint8_t *payload,
+                            uint64_t payload_bytes, uint64_t checksum, uint64_t *version);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,231 @@
+"""Pins for the oracle's version-2 payloads (CPU only): the binding block and
+overwrite records.
+
+The method: changes whose XOR cannot be used are carried as absolute
+overwrites, partial writes are retried through overwrites, and a joint commit
+binds the installed weights to the version the next delta is made from (the
+NeMo Delta-Compressed Refit summary); deltas are kept against versions other
+than the previous one ("GPU-accelerated Weight Teleportation", section "Eval,
+fault tolerance, and resuming from trained checkpoints").
+
+What pins the oracle here, apart from the oracle itself:
+- hand-derived version-2 payloads, byte for byte (tests/golden);
+- an XOR payload bound to versions holds the same descriptors and records as
+  the version-1 payload of the same pair;
+- an overwrite record, read bit by bit in Python, lists exactly the positions
+  where old and new differ (numpy) and the new values there;
+- the overwrite payload length in closed form from those positions;
+- idempotency: the overwrite payload rebuilds the new weights from any mix of
+  old and new values at the changed positions, and from the new weights;
+- the version word: a wrong base touches nothing, success moves it to the
+  target, every failure leaves it and the weights as they were.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_bf16_weight_xor_amd import synth
+from tests import payload_view as pv
+
+
+def _golden_cases():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples_v2.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_worked_example_bytes(case):
+    n = case["n"]
+    old = np.full(n, int(case["old"]["fill"], 16), dtype=np.uint16)
+    new = old.copy()
+    for i, v in case["new_changes"].items():
+        new[int(i)] = int(v, 16)
+    payload, cs, stats = oracle.compress_v2(old, new, case["base"], case["target"],
+                                            overwrite=bool(case["flags"] & 1))
+    h = pv.header(payload)
+    assert h["magic"] == b"BF16DXOR" and h["version"] == 2 and h["block_elems"] == 8192
+    assert h["n"] == n
+    for key in ("n_changed", "n_rare", "pos_bytes", "mant_bytes", "rare_bytes"):
+        assert h[key] == case[key], key
+    b = pv.binding(payload)
+    assert (b["base"], b["target"], b["flags"], b["reserved"]) == (
+        case["base"], case["target"], case["flags"], (0, 0))
+    assert [int(d) for d in pv.descriptors(payload, n)] == [int(d, 16) for d in case["descriptors"]]
+    assert bytes(payload[pv.data_offset(n, 96):]).hex().upper() == case["data_hex"].upper()
+    assert len(payload) == case["payload_bytes"]
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, payload, cs, case["base"]) == (oracle.OK, case["target"])
+    assert np.array_equal(w, new)
+
+
+def _pair(shape, frac, seed, placement="uniform"):
+    s, d = synth.make_pair(shape, frac, synth.MIX_ADVERSARIAL, seed, "cpu", placement)
+    return (synth.bits(s).numpy().astype(np.uint16).reshape(-1),
+            synth.bits(d).numpy().astype(np.uint16).reshape(-1))
+
+
+SHAPES = [((3 * 8192 + 77,), "0.03", 1), ((8191,), "0.6", 2), ((2 * 8192,), "0.001", 3),
+          ((1,), "1.0", 4), ((70001,), "0.2", 5), ((5 * 8192,), "1.0", 6)]
+
+
+@pytest.mark.parametrize("shape,frac,seed", SHAPES)
+def test_bound_xor_payload_is_the_v1_payload_with_a_binding(shape, frac, seed):
+    old, new = _pair(shape, frac, seed)
+    p1, cs1, _ = oracle.compress(old, new)
+    p2, cs2, _ = oracle.compress_v2(old, new, 123, 124)
+    n = old.size
+    assert cs1 == cs2
+    assert bytes(p2[:8]) == bytes(p1[:8]) and bytes(p2[12:64]) == bytes(p1[12:64])
+    assert np.array_equal(pv.descriptors(p1, n), pv.descriptors(p2, n))
+    assert bytes(p2[pv.data_offset(n, 96):]) == bytes(p1[pv.data_offset(n):])
+
+
+@pytest.mark.parametrize("shape,frac,seed", SHAPES)
+def test_overwrite_records_list_the_changed_positions_and_new_values(shape, frac, seed):
+    old, new = _pair(shape, frac, seed)
+    p, cs, stats = oracle.compress_v2(old, new, 5, 6, overwrite=True)
+    n = old.size
+    descs = pv.descriptors(p, n)
+    at = pv.data_offset(n, 96)
+    total = 96 + 4 * len(descs)
+    raw = bytes(p)
+    for b, d in enumerate(descs):
+        L = pv.block_len(n, b)
+        lo = b * 8192
+        want = np.nonzero(old[lo:lo + L] != new[lo:lo + L])[0]
+        c, r, code = pv.split(int(d))
+        assert c == want.size and r == c
+        # the cheaper position encoding, tie to the gap list
+        gaps = np.diff(np.concatenate([[-1], want])) - 1 if want.size else np.zeros(0)
+        w = int(gaps.max()).bit_length() if want.size else 0
+        gap_bytes, bitmap_bytes = -(-(want.size * w) // 8), -(-L // 8)
+        assert code == (15 if bitmap_bytes < gap_bytes else w)
+        length = min(gap_bytes, bitmap_bytes) + 2 * want.size
+        assert pv.record_bytes(int(d), L, overwrite=True) == length
+        pos, vals = pv.overwrite_record(raw[at:at + length], int(d), L)
+        assert pos == want.tolist()
+        assert vals == new[lo + want].tolist()
+        at += length
+        total += length
+    assert at == len(p) == total == stats["payload_bytes"]
+    h = pv.header(p)
+    assert h["n_rare"] == h["n_changed"] == stats["n_changed"] and h["mant_bytes"] == 0
+
+
+@pytest.mark.parametrize("shape,frac,seed", SHAPES)
+def test_overwrite_is_idempotent_over_any_partial_write(shape, frac, seed):
+    old, new = _pair(shape, frac, seed)
+    p, cs, _ = oracle.compress_v2(old, new, 0, 1, overwrite=True)
+    rng = np.random.default_rng(seed)
+    changed = np.nonzero(old != new)[0]
+    starts = [old.copy(), new.copy()]
+    for _ in range(3):                       # a random part of the update written already
+        w = old.copy()
+        done = changed[rng.random(changed.size) < rng.random()]
+        w[done] = new[done]
+        starts.append(w)
+    for w in starts:
+        assert oracle.decompress_v2_inplace(w, p, cs, None) == (oracle.OK, None)
+        assert np.array_equal(w, new)
+
+
+def test_overwrite_never_leaves_a_partial_write():
+    old, new = _pair((3 * 8192 + 5,), "0.05", 11)
+    p, cs, _ = oracle.compress_v2(old, new, 0, 1, overwrite=True)
+    changed = np.nonzero(old != new)[0]
+    unchanged = np.nonzero(old == new)[0]
+    # a receiver that differs at an unchanged position cannot reach the checksum
+    w = old.copy()
+    w[unchanged[7]] ^= 0x0001
+    before = w.copy()
+    assert oracle.decompress_v2_inplace(w, p, cs, 0) == (oracle.ECHECKSUM, 0)
+    assert np.array_equal(w, before)
+    # a wrong checksum on a half-applied receiver leaves it half applied
+    w = old.copy()
+    w[changed[::2]] = new[changed[::2]]
+    before = w.copy()
+    assert oracle.decompress_v2_inplace(w, p, cs ^ 1, 0) == (oracle.ECHECKSUM, 0)
+    assert np.array_equal(w, before)
+    # a malformed record (position padding bit set in a gap-list block)
+    q = p.copy()
+    descs = pv.descriptors(q, old.size)
+    at = pv.data_offset(old.size, 96)
+    for b, d in enumerate(descs):
+        c, r, code = pv.split(int(d))
+        L = pv.block_len(old.size, b)
+        if code not in (0, 15) and (c * code) % 8:
+            q[at + (c * code) // 8] |= 0x80
+            break
+        at += pv.record_bytes(int(d), L, overwrite=True)
+    else:
+        pytest.fail("no gap-list block with position padding")
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, q, cs, 0) == (oracle.EFORMAT, 0)
+    assert np.array_equal(w, old)
+
+
+@pytest.mark.parametrize("overwrite", [False, True])
+def test_the_version_word_moves_only_with_the_weights(overwrite):
+    old, new = _pair((2 * 8192 + 9,), "0.04", 21)
+    p, cs, _ = oracle.compress_v2(old, new, 10, 11, overwrite=overwrite)
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, p, cs, 9) == (oracle.EVERSION, 9)
+    assert np.array_equal(w, old)
+    assert oracle.decompress_v2_inplace(w, p, cs ^ 2, 10) == (oracle.ECHECKSUM, 10)
+    assert np.array_equal(w, old)
+    assert oracle.decompress_v2_inplace(w, p, cs, 10) == (oracle.OK, 11)
+    assert np.array_equal(w, new)
+    # applied again from the new version: refused, untouched
+    assert oracle.decompress_v2_inplace(w, p, cs, 11) == (oracle.EVERSION, 11)
+    assert np.array_equal(w, new)
+    # without a version word the binding is not checked
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, p, cs, None) == (oracle.OK, None)
+    assert np.array_equal(w, new)
+
+
+def test_a_version_1_payload_leaves_the_version_word_alone():
+    old, new = _pair((8192 + 1,), "0.1", 22)
+    p, cs, _ = oracle.compress(old, new)
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, p, cs, 77) == (oracle.OK, 77)
+    assert np.array_equal(w, new)
+
+
+def test_malformed_binding_blocks_are_rejected_before_the_version():
+    old, new = _pair((8192 + 3,), "0.02", 23)
+    for overwrite in (False, True):
+        p, cs, _ = oracle.compress_v2(old, new, 1, 2, overwrite=overwrite)
+        bad = {}
+        bad["flag"] = p.copy(); bad["flag"][80] |= 2
+        bad["reserved32"] = p.copy(); bad["reserved32"][84] = 1
+        bad["reserved64"] = p.copy(); bad["reserved64"][95] = 1
+        bad["version 3"] = p.copy(); bad["version 3"][8] = 3
+        bad["mode"] = p.copy(); bad["mode"][80] ^= 1          # the other record kind
+        bad["short"] = p[:90].copy()
+        for name, q in bad.items():
+            w = old.copy()
+            # a wrong version word too: the format error is reported first
+            assert oracle.decompress_v2_inplace(w, q, cs, 99) == (oracle.EFORMAT, 99), name
+            assert np.array_equal(w, old), name
+
+
+def test_overwrite_descriptor_must_count_one_word_per_change():
+    old, new = _pair((8192,), "0.01", 24)
+    p, cs, _ = oracle.compress_v2(old, new, 1, 2, overwrite=True)
+    d = int(pv.descriptors(p, old.size)[0])
+    c, r, code = pv.split(d)
+    q = p.copy()
+    q[96:100] = np.frombuffer(np.uint32(c | ((r - 1) << 14) | (code << 28)).tobytes(), np.uint8)
+    w = old.copy()
+    assert oracle.decompress_v2_inplace(w, q, cs, 1)[0] == oracle.EFORMAT
+    assert np.array_equal(w, old)
+
+
+def test_compress_v2_rejects_unknown_flags():
+    old, new = _pair((100,), "0.1", 25)
+    st, _, _ = oracle.compress_v2_raw(old, new, 0, 1, flags=2)
+    assert st == oracle.EINVAL
