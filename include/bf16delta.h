@@ -94,10 +94,15 @@ extern "C" {
 #define BF16D_ECHECKSUM 4  /* decompress: rebuilt weights fail the checksum; weights end old */
 #define BF16D_EHIP      5  /* a HIP runtime call failed */
 #define BF16D_ECODEC    6  /* codec race: the frame's codec library is not available here */
+#define BF16D_EVERSION  7  /* decompress: the receiver's version is not the payload's base;
+                              nothing touched */
 
 #define BF16D_BLOCK_ELEMS    8192
 #define BF16D_HEADER_BYTES   64
 #define BF16D_FORMAT_VERSION 1
+#define BF16D_FORMAT_VERSION_BOUND 2   /* version-2 payloads: bound to versions */
+#define BF16D_HEADER_BYTES_BOUND   96
+#define BF16D_BIND_OVERWRITE       1u  /* version 2: records carry absolute values */
 
 /* Per-job outcome, written by the device. 48 bytes. */
 typedef struct bf16d_result {
@@ -210,6 +215,64 @@ int bf16d_delta_decompress(uint16_t *src_inout, uint64_t n,
                            uint64_t checksum,
                            void *workspace, size_t workspace_bytes,
                            bf16d_result *result, hipStream_t stream);
+
+/* Version-2 payloads: bound to versions, optionally with absolute values.
+ *
+ * "GPU-accelerated Weight Teleportation", section "Eval, fault tolerance,
+ * and resuming from trained checkpoints": deltas are also kept against
+ * versions other than the previous one (the last evaluated version, the
+ * engines' base version), so a receiver must be able to tell which version a
+ * payload applies to.  The NeMo Delta-Compressed Refit summary: changes that
+ * cannot be carried as XOR masks travel as absolute overwrites, partial
+ * writes are retried through overwrites, and a joint commit binds the
+ * installed weights to the version the next delta is made from.
+ *
+ * Format version 2: the 64 header bytes of version 1 with version = 2, then
+ *   u64 base_version, u64 target_version, u32 flags, u32 0, u64 0
+ * (96 bytes); the descriptor table starts at byte 96.  Records are those of
+ * version 1, except with flags & BF16D_BIND_OVERWRITE: then every changed
+ * element (old != new) carries its new value as a little-endian u16 right
+ * after the position segment, there is no mantissa segment, the
+ * descriptor's r equals c, and the header counts mant_bytes = 0 and
+ * rare_bytes = 2 * n_changed.  Applying an overwrite record sets each listed
+ * element to its value, so the result is the new tensor whatever mix of old
+ * and new values the listed elements held: a retry after a partial write.
+ * A version-2 payload is at most bf16d_max_payload_bytes(n) + 32 bytes. */
+typedef struct bf16d_binding {
+    uint64_t base_version;    /* the version the receiver's weights must hold */
+    uint64_t target_version;  /* the version they hold after the apply */
+    uint32_t flags;           /* 0 or BF16D_BIND_OVERWRITE */
+    uint32_t reserved;        /* 0 */
+} bf16d_binding;
+
+/* bf16d_compress writing version-2 payloads: bindings[i] (host array) for
+ * job i.  Results are those of bf16d_compress; for an overwrite payload
+ * n_rare counts its words (= n_changed).  Returns BF16D_EINVAL for a NULL
+ * bindings array, unknown flags or a non-zero reserved field. */
+int bf16d_compress_bound(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
+                         uint32_t count, void *workspace, size_t workspace_bytes,
+                         bf16d_result *results, hipStream_t stream);
+
+/* bf16d_decompress with the receiver's version words.
+ *   versions : device memory, 8-byte aligned, count u64: versions[i] is the
+ *              version tensor i holds.  May be NULL: then no binding is
+ *              checked.  It may not overlap the weights, payloads or
+ *              workspace.
+ * Per job, on top of bf16d_decompress:
+ *   - a version-2 payload whose base_version differs from versions[i]:
+ *     BF16D_EVERSION, weights and versions[i] untouched (a malformed header
+ *     or descriptor table still reports BF16D_EFORMAT first);
+ *   - BF16D_OK for a version-2 payload: versions[i] = target_version,
+ *     written together with the weights; on any other status it is kept;
+ *   - a version-1 payload leaves versions[i] alone.
+ * An overwrite payload is verified before anything is written (its checksum
+ * is that of the would-be result) and then written: the weights end new on
+ * BF16D_OK and untouched on any other status.  bf16d_decompress and the
+ * streamed and remapped calls read version-2 payloads too, without checking
+ * the binding. */
+int bf16d_decompress_bound(const bf16d_decompress_job *jobs, uint64_t *versions, uint32_t count,
+                           void *workspace, size_t workspace_bytes, bf16d_result *results,
+                           hipStream_t stream);
 
 /* Remapped apply: the new weights land on a physical layout that differs
  * from the logical tensor the payload was made from.

@@ -23,10 +23,11 @@ from typing import Sequence
 import torch
 
 from . import _native
-from ._native import (OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, BLOCK_ELEMS,
+from ._native import (OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, EVERSION, BLOCK_ELEMS,
                       HEADER_BYTES, CompressJob, DecompressJob, RESULT_BYTES)
 
 FORMAT = "bf16delta_v1"
+BOUND_EXTRA_BYTES = 32   # a version-2 header is 32 bytes longer
 _ALIGN = 256   # payload slots inside an arena start on this boundary
 
 __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_batch",
@@ -113,14 +114,25 @@ class CompressBatch:
     per job."""
 
     def __init__(self, pairs: Sequence[tuple[torch.Tensor, torch.Tensor]],
-                 capacities: Sequence[int] | None = None):
+                 capacities: Sequence[int] | None = None, bindings=None):
+        """bindings: None (version-1 payloads), or per job (base_version,
+        target_version, overwrite) for version-2 payloads (bf16d_compress_bound)."""
         if not pairs:
             raise ValueError("empty batch")
         self.device = pairs[0][0].device
         self.count = len(pairs)
         self.n = [p[0].numel() for p in pairs]
+        self.bindings = None
+        if bindings is not None:
+            if len(bindings) != self.count:
+                raise ValueError("one binding per job")
+            self.bindings = (_native.Binding * self.count)(
+                *[_native.Binding(int(b) & 0xFFFFFFFFFFFFFFFF, int(t) & 0xFFFFFFFFFFFFFFFF,
+                                  _native.BIND_OVERWRITE if ow else 0, 0)
+                  for b, t, ow in bindings])
         if capacities is None:
-            capacities = [max_payload_bytes(n) for n in self.n]
+            extra = BOUND_EXTRA_BYTES if bindings is not None else 0
+            capacities = [max_payload_bytes(n) + extra for n in self.n]
         self.capacity = [int(c) for c in capacities]
         self.offset = []
         at = 0
@@ -146,6 +158,15 @@ class CompressBatch:
     def run(self, events=None) -> None:
         """Enqueue the call.  `events`: optional (before, after) torch.cuda.Event
         pair, recorded around the encode kernel."""
+        if self.bindings is not None:
+            if events is not None:
+                raise ValueError("kernel events are not offered for bound payloads")
+            rc = _native.lib().bf16d_compress_bound(self.jobs, self.bindings, self.count,
+                                                    self.workspace.data_ptr(), self.ws_bytes,
+                                                    self.result_buf.data_ptr(),
+                                                    _stream(self.device))
+            _check_rc(rc, "bf16d_compress_bound")
+            return
         ev = _events(events)
         rc = _native.lib().bf16d_compress_ex(self.jobs, self.count, self.workspace.data_ptr(),
                                              self.ws_bytes, self.result_buf.data_ptr(),
@@ -163,12 +184,23 @@ class DecompressBatch:
     """A prepared batched in-place decompress call over fixed (weights, payload,
     checksum) triples.  `run()` enqueues it on the current stream."""
 
-    def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]]):
+    def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
+                 versions: torch.Tensor | None = None):
+        """versions: None, or the receiver's version words, an int64 tensor of
+        len(items) on the weights' device, checked against version-2 payloads
+        and advanced in place (bf16d_decompress_bound)."""
         if not items:
             raise ValueError("empty batch")
         self.device = items[0][0].device
         self.count = len(items)
         self.items = list(items)
+        self.versions = versions
+        if versions is not None:
+            if (versions.device != self.device or versions.dtype not in (torch.int64,
+                                                                         torch.uint64)
+                    or versions.numel() != self.count or not versions.is_contiguous()):
+                raise TypeError("versions must be a contiguous 64-bit tensor with one word "
+                                "per job on the weights' device")
         n_total = sum(w.numel() for w, _, _ in items)
         self.ws_bytes = workspace_bytes(n_total, self.count)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
@@ -193,6 +225,15 @@ class DecompressBatch:
     def run(self, events=None) -> None:
         """Enqueue the call.  `events`: optional (before, after) torch.cuda.Event
         pair, recorded around the apply kernel."""
+        if self.versions is not None:
+            if events is not None:
+                raise ValueError("kernel events are not offered with version words")
+            rc = _native.lib().bf16d_decompress_bound(self.jobs, self.versions.data_ptr(),
+                                                      self.count, self.workspace.data_ptr(),
+                                                      self.ws_bytes, self.result_buf.data_ptr(),
+                                                      _stream(self.device))
+            _check_rc(rc, "bf16d_decompress_bound")
+            return
         ev = _events(events)
         rc = _native.lib().bf16d_decompress_ex(self.jobs, self.count, self.workspace.data_ptr(),
                                                self.ws_bytes, self.result_buf.data_ptr(),
@@ -342,19 +383,22 @@ def _first_capacity(n: int) -> int:
     return min(max_payload_bytes(n), HEADER_BYTES + 4 * nb + (2 * n) // 8 + 4096)
 
 
-def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]]):
-    """Compress several (src, dst) pairs in one batched call.
+def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]], bindings=None):
+    """Compress several (src, dst) pairs in one batched call.  bindings: None,
+    or per pair (base_version, target_version, overwrite) for version-2
+    payloads.
 
     Returns a list of (payload uint8 tensor, checksum int, stats dict).  The
     payloads are views into one device arena."""
-    caps = [_first_capacity(s.numel()) for s, _ in pairs]
-    batch = CompressBatch(pairs, caps)
+    extra = BOUND_EXTRA_BYTES if bindings is not None else 0
+    caps = [_first_capacity(s.numel()) + extra for s, _ in pairs]
+    batch = CompressBatch(pairs, caps, bindings)
     batch.run()
     res = batch.results()
     short = [j for j, r in enumerate(res) if r["status"] == ECAPACITY]
     if short:
         caps = [res[j]["payload_bytes"] if j in short else caps[j] for j in range(len(pairs))]
-        batch = CompressBatch(pairs, caps)
+        batch = CompressBatch(pairs, caps, bindings)
         batch.run()
         res = batch.results()
     out = []
@@ -365,10 +409,12 @@ def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]]):
     return out
 
 
-def decompress_batch(items: Sequence[tuple[torch.Tensor, torch.Tensor, int]]) -> list[dict]:
-    """Apply several payloads in place in one batched call.  Returns the
-    per-job result dicts, without raising on per-job failures."""
-    batch = DecompressBatch(items)
+def decompress_batch(items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
+                     versions: torch.Tensor | None = None) -> list[dict]:
+    """Apply several payloads in place in one batched call, optionally with the
+    receiver's version words (see DecompressBatch).  Returns the per-job
+    result dicts, without raising on per-job failures."""
+    batch = DecompressBatch(items, versions)
     batch.run()
     return batch.results()
 

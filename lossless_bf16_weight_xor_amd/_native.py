@@ -13,7 +13,8 @@ import torch  # noqa: F401  (loads the HIP runtime the library must share)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta.so")
 
-OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, ECODEC = 0, 1, 2, 3, 4, 5, 6
+OK, EINVAL, ECAPACITY, EFORMAT, ECHECKSUM, EHIP, ECODEC, EVERSION = 0, 1, 2, 3, 4, 5, 6, 7
+BIND_OVERWRITE = 1
 BLOCK_ELEMS = 8192
 HEADER_BYTES = 64
 FORMAT_VERSION = 1
@@ -24,7 +25,7 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress"
             "bf16d_decompress_remapped", "bf16d_workspace_bytes_remapped",
             "bf16d_status_string", "bf16d_format_version", "bf16d_codec_available",
             "bf16d_race_bound", "bf16d_race_compress", "bf16d_race_frame_info",
-            "bf16d_race_decompress")
+            "bf16d_race_decompress", "bf16d_compress_bound", "bf16d_decompress_bound")
 
 CODECS = {"stored": 0, "zstd": 1, "lz4": 2, "lz4hc": 3, "zlib": 4, "brotli": 5, "xz": 6}
 RACE_FRAME_HEADER = 32
@@ -60,6 +61,11 @@ class Segment(ctypes.Structure):
 
 class Remap(ctypes.Structure):
     _fields_ = [("segments", ctypes.POINTER(Segment)), ("count", ctypes.c_uint32)]
+
+
+class Binding(ctypes.Structure):
+    _fields_ = [("base_version", ctypes.c_uint64), ("target_version", ctypes.c_uint64),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class Codec(ctypes.Structure):
@@ -128,6 +134,12 @@ def lib():
         L.bf16d_status_string.restype = ctypes.c_char_p
         L.bf16d_format_version.argtypes = []
         L.bf16d_format_version.restype = ctypes.c_int
+        L.bf16d_compress_bound.argtypes = [ctypes.POINTER(CompressJob), ctypes.POINTER(Binding),
+                                           u32, vp, sz, vp, vp]
+        L.bf16d_compress_bound.restype = ctypes.c_int
+        L.bf16d_decompress_bound.argtypes = [ctypes.POINTER(DecompressJob), vp, u32, vp, sz, vp,
+                                             vp]
+        L.bf16d_decompress_bound.restype = ctypes.c_int
         L.bf16d_codec_available.argtypes = [u32]
         L.bf16d_codec_available.restype = ctypes.c_int
         L.bf16d_race_bound.argtypes = [u64]

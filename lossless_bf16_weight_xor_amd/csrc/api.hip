@@ -109,6 +109,7 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
         dj[j].dtile0 = p.dstart[j];
         dj[j].segs = nullptr;
         dj[j].nsegs = 0;
+        dj[j].version = nullptr;
     }
     std::memcpy(out + (l.block_start - l.jobs), p.bstart.data(), 8 * p.bstart.size());
     std::memcpy(out + (l.dtile_start - l.jobs), p.dstart.data(), 8 * p.dstart.size());
@@ -118,13 +119,15 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
 
 namespace {
 
-// The batched decompress, optionally remapped: checks, job table (and the
-// remap segments after the layout), upload, launch.
-int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps, uint32_t count,
-                    void *workspace, size_t workspace_bytes, bf16d_result *results,
-                    hipStream_t stream, const bf16d_events *events) {
+// The batched decompress, optionally remapped and with the receiver's version
+// words: checks, job table (and the remap segments after the layout), upload,
+// launch.
+int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
+                    uint64_t *versions, uint32_t count, void *workspace, size_t workspace_bytes,
+                    bf16d_result *results, hipStream_t stream, const bf16d_events *events) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
+    if (versions && (reinterpret_cast<uintptr_t>(versions) & 7u) != 0) return BF16D_EINVAL;
     DecompressPrep prep;
     int rc = decompress_prep(jobs, count, prep, remaps);
     if (rc != BF16D_OK) return rc;
@@ -154,10 +157,17 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     }
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + need, true});
+    if (versions)
+        ranges.push_back({reinterpret_cast<uintptr_t>(versions),
+                          reinterpret_cast<uintptr_t>(versions + count), true});
     if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
 
     std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
     decompress_table(jobs, count, prep, l, host.data());
+    if (versions) {
+        auto *dj = reinterpret_cast<DecompressJob *>(host.data());
+        for (uint32_t j = 0; j < count; ++j) dj[j].version = (BF16D_GMEM uint64_t *)(versions + j);
+    }
     std::vector<uint8_t> segs(sizeof(RemapSegment) * nsegs, 0);
     if (nsegs) {
         auto *dj = reinterpret_cast<DecompressJob *>(host.data());
@@ -208,16 +218,20 @@ size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
     return c > d ? c : d;
 }
 
-int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
-                   size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
-    return bf16d_compress_ex(jobs, count, workspace, workspace_bytes, results, stream, nullptr);
-}
+}  // extern "C"
 
-int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
-                      size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
-                      const bf16d_events *events) {
+namespace {
+
+// The batched compress; bindings (may be NULL) make version-2 payloads.
+int compress_call(const bf16d_compress_job *jobs, const bf16d_binding *bindings, uint32_t count,
+                  void *workspace, size_t workspace_bytes, bf16d_result *results,
+                  hipStream_t stream, const bf16d_events *events) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
+    if (bindings)
+        for (uint32_t j = 0; j < count; ++j)
+            if ((bindings[j].flags & ~BF16D_BIND_OVERWRITE) != 0 || bindings[j].reserved != 0)
+                return BF16D_EINVAL;
     std::vector<uint64_t> start(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
     std::vector<Range> ranges;
     ranges.reserve(3 * size_t(count) + 1);
@@ -255,16 +269,54 @@ int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count, void *work
         dj[j].capacity = jobs[j].capacity;
         dj[j].block0 = start[j];
         dj[j].nb = start[j + 1] - start[j];
-        dj[j].pad = 0;
+        dj[j].hdr = bindings ? kHeaderBound : kHeader;
+        dj[j].flags = bindings ? bindings[j].flags : 0;
+        dj[j].base_version = bindings ? bindings[j].base_version : 0;
+        dj[j].target_version = bindings ? bindings[j].target_version : 0;
     }
     std::memcpy(host.data() + (l.block_start - l.jobs), start.data(), 8 * start.size());
     std::memcpy(host.data() + (l.dtile_start - l.jobs), dstart.data(), 8 * dstart.size());
     int rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
+    bool any_overwrite = false;
+    for (uint32_t j = 0; bindings && j < count; ++j)
+        any_overwrite |= (bindings[j].flags & BF16D_BIND_OVERWRITE) != 0;
     return launch_compress(l, static_cast<uint8_t *>(workspace), count, tiles, dtiles, results,
-                           stream, events) == hipSuccess
+                           stream, events, any_overwrite) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bf16d_compress(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
+                   size_t workspace_bytes, bf16d_result *results, hipStream_t stream) {
+    return compress_call(jobs, nullptr, count, workspace, workspace_bytes, results, stream,
+                         nullptr);
+}
+
+int bf16d_compress_ex(const bf16d_compress_job *jobs, uint32_t count, void *workspace,
+                      size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
+                      const bf16d_events *events) {
+    return compress_call(jobs, nullptr, count, workspace, workspace_bytes, results, stream,
+                         events);
+}
+
+int bf16d_compress_bound(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
+                         uint32_t count, void *workspace, size_t workspace_bytes,
+                         bf16d_result *results, hipStream_t stream) {
+    if (!bindings) return BF16D_EINVAL;
+    return compress_call(jobs, bindings, count, workspace, workspace_bytes, results, stream,
+                         nullptr);
+}
+
+int bf16d_decompress_bound(const bf16d_decompress_job *jobs, uint64_t *versions, uint32_t count,
+                           void *workspace, size_t workspace_bytes, bf16d_result *results,
+                           hipStream_t stream) {
+    return decompress_call(jobs, nullptr, versions, count, workspace, workspace_bytes, results,
+                           stream, nullptr);
 }
 
 int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
@@ -275,8 +327,8 @@ int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *wor
 int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,
                         size_t workspace_bytes, bf16d_result *results, hipStream_t stream,
                         const bf16d_events *events) {
-    return decompress_call(jobs, nullptr, count, workspace, workspace_bytes, results, stream,
-                           events);
+    return decompress_call(jobs, nullptr, nullptr, count, workspace, workspace_bytes, results,
+                           stream, events);
 }
 
 size_t bf16d_workspace_bytes_remapped(uint64_t total_n, uint32_t count, uint64_t total_segments) {
@@ -286,8 +338,8 @@ size_t bf16d_workspace_bytes_remapped(uint64_t total_n, uint32_t count, uint64_t
 int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
                               uint32_t count, void *workspace, size_t workspace_bytes,
                               bf16d_result *results, hipStream_t stream) {
-    return decompress_call(jobs, remaps, count, workspace, workspace_bytes, results, stream,
-                           nullptr);
+    return decompress_call(jobs, remaps, nullptr, count, workspace, workspace_bytes, results,
+                           stream, nullptr);
 }
 
 int bf16d_delta_compress(const uint16_t *src, const uint16_t *dst, uint64_t n, uint8_t *payload,
@@ -313,6 +365,7 @@ const char *bf16d_status_string(int status) {
         case BF16D_ECHECKSUM: return "ECHECKSUM: rebuilt weights fail the checksum";
         case BF16D_EHIP: return "EHIP: HIP runtime error";
         case BF16D_ECODEC: return "ECODEC: codec library not available";
+        case BF16D_EVERSION: return "EVERSION: the weights are not the payload's base version";
         default: return "unknown status";
     }
 }

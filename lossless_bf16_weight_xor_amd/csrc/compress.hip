@@ -36,7 +36,12 @@
 //              writes the descriptor.
 //   reencode : for tiles whose record did not fit a slot (dense blocks),
 //              encodes again straight into the payload.
-//   finalize : one workgroup per job; header, checksum and result.
+//   finalize : one thread per job; header, checksum and result.
+//
+// A version-2 payload adds a binding block to the header; an overwrite
+// payload (its flag set) has no mantissa segment and carries the new value
+// of every change as a 16-bit word.  Overwrite tiles take their own compiled
+// instances of the same steps.
 // The slots cost 2 * (record bytes) of extra traffic, about 2% at a 2%
 // change rate.
 #include "internal.hpp"
@@ -128,6 +133,9 @@ struct TileFlags {
 
 // Steps 1-2 for one tile, in registers only: writes x to s_x (each thread
 // touches only its own chunks).  After it returns, o/nw are free.
+//   kOw (an overwrite payload): s_x gets the new values instead, and every
+//   change counts as a word of the word segment (rare flags = changed flags).
+template <bool kOw>
 __device__ __forceinline__ void classify(const TileRef &t, const uint4 (&o)[kChunksPerThread],
                                          const uint4 (&nw)[kChunksPerThread], uint16_t *s_x,
                                          TileFlags &f) {
@@ -144,11 +152,12 @@ __device__ __forceinline__ void classify(const TileRef &t, const uint4 (&o)[kChu
         const uint32_t valid = e0 < t.L ? (t.L - e0 < 8 ? t.L - e0 : 8) : 0;
         const uint4 x = make_uint4(o[i].x ^ nw[i].x, o[i].y ^ nw[i].y, o[i].z ^ nw[i].z,
                                    o[i].w ^ nw[i].w);
-        reinterpret_cast<uint4 *>(s_x)[q] = x;
+        reinterpret_cast<uint4 *>(s_x)[q] = kOw ? nw[i] : x;
         const uint64_t kg = kg0 + i * kRoundKg;
         if (valid > 0) acc += mix64(((uint64_t)nw[i].y << 32 | nw[i].x) ^ kg);
         if (valid > 4) acc += mix64(((uint64_t)nw[i].w << 32 | nw[i].z) ^ (kg + kGamma));
-        const uint32_t c8 = nonzero8(x, 0xFFFFFFFFu), r8 = nonzero8(x, 0xFF80FF80u);
+        const uint32_t c8 = nonzero8(x, 0xFFFFFFFFu);
+        const uint32_t r8 = kOw ? c8 : nonzero8(x, 0xFF80FF80u);
         M |= c8 << (8 * i);
         R |= r8 << (8 * i);
         f.cnt[i] = __popc(c8) | (__popc(r8) << 16);
@@ -160,7 +169,9 @@ __device__ __forceinline__ void classify(const TileRef &t, const uint4 (&o)[kChu
 }
 
 // Step 3: scans in element order (round i, then thread, then slot), the
-// widest gap and the record layout.  Contains two barriers.
+// widest gap and the record layout.  Contains two barriers.  kOw: no
+// mantissa segment.
+template <bool kOw>
 __device__ __forceinline__ void scan(const TileRef &t, const TileFlags &f, EncodeShared &sh,
                                      TileCode &out) {
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -227,14 +238,16 @@ __device__ __forceinline__ void scan(const TileRef &t, const TileFlags &f, Encod
     const uint32_t bitmap_bytes = (t.L + 7) / 8;
     out.code = bitmap_bytes < delta_bytes ? kCodeBitmap : out.w;
     out.pb = out.code == kCodeBitmap ? bitmap_bytes : delta_bytes;
-    out.mb = (7 * c + 7) / 8;
+    out.mb = kOw ? 0u : (7 * c + 7) / 8;
     out.len = out.pb + out.mb + 2 * r;
     out.desc = c | (r << 14) | (out.code << 28);
 }
 
 // Step 4: OR this thread's fields into a zeroed LDS record.  The rare words
-// go in too when kWithRare; otherwise the caller stores them directly.
-template <bool kWithRare>
+// go in too when kWithRare; otherwise the caller stores them directly.  kOw:
+// the words are the new values of every change, and there are no mantissa
+// fields.
+template <bool kWithRare, bool kOw>
 __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
                                           const TileCode &k) {
     const uint32_t tid = threadIdx.x;
@@ -257,7 +270,7 @@ __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
             lds_or_bits(s_rec, j * k.w, 8 * q + s - p1, k.w);
         }
         const uint32_t xs = s_x[8 * q + s];
-        if (!(xs & kExpSign)) {
+        if (!kOw && !(xs & kExpSign)) {
             lds_or_bits(s_rec, mant_bit + 7 * j, xs & kMant, 7);
         } else if (kWithRare) {
             const uint32_t kk = ((uint32_t)(k.Kb >> (16 * i)) & 0xFFFFu) +
@@ -271,7 +284,7 @@ __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
 // One tile, from its loads to its slot.  Whole blocks and the short last
 // block of a tensor are compiled separately, so that all of a whole block's
 // loads are in flight together.
-template <bool kFull>
+template <bool kFull, bool kOw>
 __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16_t *s_x,
                                            uint32_t *s_rec, EncodeShared &sh,
                                            uint8_t *__restrict__ slots,
@@ -287,13 +300,13 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
     init_gap_table(sh);
 
     TileFlags f;
-    classify(tr, o, nw, s_x, f);
+    classify<kOw>(tr, o, nw, s_x, f);
     TileCode k;
-    scan(tr, f, sh, k);   // its barriers also order the clearing above
+    scan<kOw>(tr, f, sh, k);   // its barriers also order the clearing above
 
     const bool fits = k.len <= kSlot;
-    if (fits) or_fields<true>(s_rec, s_x, k);
-    const uint64_t acc = wave_sum(k.acc);
+    if (fits) or_fields<true, kOw>(s_rec, s_x, k);
+    const uint64_t acc = first_lane(wave_sum(k.acc));
     __syncthreads();
 
     if (fits) {
@@ -320,11 +333,20 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
     __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
     __shared__ EncodeShared sh;
     const uint64_t t = blockIdx.x;
-    const TileRef tr = tile_ref(jobs[tile_job[t]], t);
-    if (tr.L == kBlock)
-        encode_one<true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
-    else
-        encode_one<false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+    const CompressJob &job = jobs[tile_job[t]];
+    const TileRef tr = tile_ref(job, t);
+    if (job.flags & kFlagOverwrite) {   // overwrite payloads: their own instances
+        if (tr.L == kBlock)
+            encode_one<true, true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow,
+                                   ctrl);
+        else
+            encode_one<false, true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow,
+                                    ctrl);
+    } else if (tr.L == kBlock) {
+        encode_one<true, false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+    } else {
+        encode_one<false, false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+    }
 }
 
 // ----------------------------------------------------------------- offsets ---
@@ -368,12 +390,13 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
         const uint32_t L = left < kBlock ? (uint32_t)left : kBlock;
         const uint32_t c = d & 0x3FFFu, r = (d >> 14) & 0x3FFFu, code = d >> 28;
         const uint32_t pb = code == kCodeBitmap ? (L + 7) / 8 : (c * code + 7) / 8;
-        lens[k] = pb + (7 * c + 7) / 8 + 2 * r;
+        const uint32_t mb = (job.flags & kFlagOverwrite) ? 0u : (7 * c + 7) / 8;
+        lens[k] = pb + mb + 2 * r;
         mine += lens[k];
         c_sum += c;
         r_sum += r;
         pos_sum += pb;
-        mant_sum += (7 * c + 7) / 8;
+        mant_sum += mb;
         nbm += code == kCodeBitmap;
     }
     uint32_t total;
@@ -395,9 +418,9 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
         const uint64_t b = ld * kDescTile + kDescPerThread * tid + k;
         if (b < job.nb) {
             offsets[job.block0 + b] = off;
-            if (kHeader + 4 * b + 4 <= cap)
-                *reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload + kHeader + 4 * b) = descs[k];
-            const uint64_t rel = kHeader + 4 * job.nb + off;
+            if (job.hdr + 4 * b + 4 <= cap)
+                *reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload + job.hdr + 4 * b) = descs[k];
+            const uint64_t rel = job.hdr + 4 * job.nb + off;
             const uint32_t len = lens[k];
             PlaceEntry e;
             e.dst = job.payload + rel;
@@ -472,10 +495,11 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const PlaceEntry *__res
         for (uint32_t m = 0; m <= kPlaceRounds; ++m) {
             if (256 * m >= sh + len) continue;
             const uint32_t cur = rec[k][m];
-            uint32_t prev = wave_shr1(cur);
-            if (lane == 0)
-                prev = m ? (uint32_t)__builtin_amdgcn_readlane((int)rec[k][m > 0 ? m - 1 : 0], 63)
-                         : 0u;
+            // lane 0 takes the previous round's last dword; read in uniform
+            // control flow (see lane63)
+            const uint32_t carry =
+                m ? (uint32_t)__builtin_amdgcn_readlane((int)rec[k][m > 0 ? m - 1 : 0], 63) : 0u;
+            const uint32_t prev = wave_shr1_fill(cur, carry);
             const uint32_t v = sh ? __builtin_amdgcn_alignbyte(cur, prev, 4 - sh) : cur;
             const uint32_t i = lane + 64 * m;
             if (i < nout) {
@@ -495,6 +519,9 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const PlaceEntry *__res
 // payload now that their offsets are known.  The position and mantissa
 // segments are built in LDS (<= 8192 bytes); the rare words, whole 16-bit
 // words on byte boundaries, are stored directly.
+// kOw: the instance for overwrite payloads (launched only when the call has
+// one); each instance skips the other kind's tiles.
+template <bool kOw>
 __global__ __launch_bounds__(kThreads) void reencode_kernel(
     const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
     const uint32_t *__restrict__ overflow, const uint64_t *__restrict__ offsets,
@@ -508,20 +535,21 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
     for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
         const uint64_t t = overflow[i];
         const CompressJob job = jobs[tile_job[t]];
+        if (((job.flags & kFlagOverwrite) != 0) != kOw) continue;   // uniform
         const TileRef tr = tile_ref(job, t);
         uint4 o[kChunksPerThread], nw[kChunksPerThread];
         load_tile<false>(tr, o, nw);
         for (uint32_t u = tid; u < kPosMantMax / 4 + 4; u += kThreads) s_rec[u] = 0;
         TileFlags f;
-        classify(tr, o, nw, s_x, f);
+        classify<kOw>(tr, o, nw, s_x, f);
         TileCode k;
-        scan(tr, f, sh, k);   // its barriers also order the clearing of s_rec
-        or_fields<false>(s_rec, s_x, k);
+        scan<kOw>(tr, f, sh, k);   // its barriers also order the clearing of s_rec
+        or_fields<false, kOw>(s_rec, s_x, k);
         __syncthreads();
 
         BF16D_GMEM uint8_t *const pay = job.payload;
         const uint64_t cap = job.capacity;
-        const uint64_t D = kHeader + 4 * job.nb + offsets[t];
+        const uint64_t D = job.hdr + 4 * job.nb + offsets[t];
         const uint32_t pm = k.pb + k.mb;
         const uint32_t sh4 = (uint32_t)(D & 3);
         const uint64_t a0 = D - sh4;
@@ -576,14 +604,14 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
     const unsigned long long S = js.csum, c = js.c, r = js.r, pos = js.pos, mant = js.mant,
                              nbm = js.nbm;
     const uint64_t rare = 2 * r;
-    const uint64_t P = kHeader + 4 * job.nb + pos + mant + rare;
+    const uint64_t P = job.hdr + 4 * job.nb + pos + mant + rare;
     const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
     if (status == BF16D_OK) {
         BF16D_GMEM uint32_t *h = reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload);
         BF16D_GMEM uint64_t *h64 = reinterpret_cast<BF16D_GMEM uint64_t *>(job.payload);
         h[0] = kMagicLo;
         h[1] = kMagicHi;
-        h[2] = BF16D_FORMAT_VERSION;
+        h[2] = job.hdr == kHeaderBound ? BF16D_FORMAT_VERSION_BOUND : BF16D_FORMAT_VERSION;
         h[3] = kBlock;
         h64[2] = job.n;
         h64[3] = c;
@@ -591,6 +619,13 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
         h64[5] = pos;
         h64[6] = mant;
         h64[7] = rare;
+        if (job.hdr == kHeaderBound) {   // the binding block
+            h64[8] = job.base_version;
+            h64[9] = job.target_version;
+            h[20] = job.flags;
+            h[21] = 0;
+            h64[11] = 0;
+        }
     }
     bf16d_result res;
     res.status = status;
@@ -605,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
 
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                            uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                           const bf16d_events *events) {
+                           const bf16d_events *events, bool any_overwrite) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const CompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
@@ -638,8 +673,11 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
         const uint64_t per_block = (uint64_t)kWaves * kPlaceTiles;
         place_kernel<<<(uint32_t)((tiles + per_block - 1) / per_block), kThreads, 0, stream>>>(
             place, slots, tiles);
-        reencode_kernel<<<persistent_grid((const void *)reencode_kernel, tiles), kThreads, 0,
-                          stream>>>(jobs, map, overflow, offsets, ctrl);
+        reencode_kernel<false><<<persistent_grid((const void *)reencode_kernel<false>, tiles),
+                                 kThreads, 0, stream>>>(jobs, map, overflow, offsets, ctrl);
+        if (any_overwrite)
+            reencode_kernel<true><<<persistent_grid((const void *)reencode_kernel<true>, tiles),
+                                    kThreads, 0, stream>>>(jobs, map, overflow, offsets, ctrl);
     }
     compress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
         jobs, sums, count, results);

@@ -22,10 +22,20 @@
 //               is canonical.  Then old ^ tile is formed, only the changed
 //               16-byte chunks are written back, and the checksum terms of
 //               the result are accumulated.
-//   finalize  : one workgroup per job; reduces the checksum, compares it,
-//               and writes the result.
+//   finalize  : one thread per job; compares the checksum and writes the
+//               result.
 //   rollback  : the apply kernel again, for the jobs that failed only.  XOR
 //               is its own inverse, so this restores the old weights exactly.
+//
+// Version-2 payloads ("GPU-accelerated Weight Teleportation", section "Eval,
+// fault tolerance, and resuming from trained checkpoints"; the NeMo
+// Delta-Compressed Refit summary): the prepare kernel refuses a payload whose
+// base version is not the receiver's, before anything is touched, and the
+// finalize kernel moves the receiver's version word to the target together
+// with the weights.  An overwrite payload carries absolute values, which
+// applying again cannot undo, so the apply kernel only verifies it (the
+// checksum of the would-be result, no stores) and a commit pass writes it
+// once verified: the weights end new, or untouched.
 #include "internal.hpp"
 
 namespace bf16d {
@@ -55,7 +65,18 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
     const uint32_t j = dtile_job[dt];
     const DecompressJob job = jobs[j];
     const uint64_t ld = dt - job.dtile0;
-    const bool table_ok = job.payload_bytes >= kHeader + 4 * job.nb;
+    // header size and record kind, read before the header is validated (the
+    // prepare kernel rejects the job if they were wrong)
+    uint32_t hdr = kHeader;
+    bool ow = false;
+    if (job.payload_bytes >= kHeaderBound) {
+        BF16D_GMEM const uint32_t *h = reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload);
+        if (h[2] == BF16D_FORMAT_VERSION_BOUND) {
+            hdr = kHeaderBound;
+            ow = (h[20] & kFlagOverwrite) != 0;
+        }
+    }
+    const bool table_ok = job.payload_bytes >= hdr + 4 * job.nb;
 
     uint32_t lens[kDescPerThread];
     uint32_t mine = 0, bad = table_ok ? 0u : 1u;
@@ -66,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
         lens[k] = 0;
         if (!table_ok || d >= job.nb) continue;
         const uint32_t desc =
-            *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + kHeader + 4 * d);
+            *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + hdr + 4 * d);
         const uint32_t L = block_length(job.n, d);
         const uint32_t c = desc & 0x3FFFu, r = (desc >> 14) & 0x3FFFu, code = desc >> 28;
         uint32_t pb;
@@ -77,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
             pb = (c * code + 7) / 8;
             bad |= (code == kCodeInvalid) | (c == 0 && code != 0) | (pb > (L + 7) / 8);
         }
-        bad |= (c > L) | (r > c);
-        const uint32_t mb = (7 * c + 7) / 8;
+        bad |= (c > L) | (r > c) | (ow & (r != c));   // overwrite: one word per change
+        const uint32_t mb = ow ? 0u : (7 * c + 7) / 8;
         lens[k] = pb + mb + 2 * r;
         mine += lens[k];
         c_sum += c;
@@ -133,17 +154,30 @@ __global__ void prepare_kernel(const DecompressJob *__restrict__ jobs,
     const DecompressJob job = jobs[j];
     DecompressState *st = &state[j];
     bool ok = job.payload_bytes >= kHeader;
+    bool bound = false, ow = false, wrong_version = false;
+    uint32_t hdr = kHeader;
     if (ok) {
         BF16D_GMEM const uint32_t *h = reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload);
         BF16D_GMEM const uint64_t *h64 = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload);
-        ok = h[0] == kMagicLo && h[1] == kMagicHi && h[2] == BF16D_FORMAT_VERSION &&
-             h[3] == kBlock && h64[2] == job.n && job.payload_bytes >= kHeader + 4 * job.nb &&
+        bound = h[2] == BF16D_FORMAT_VERSION_BOUND;
+        hdr = bound ? kHeaderBound : kHeader;
+        ok = h[0] == kMagicLo && h[1] == kMagicHi && (bound || h[2] == BF16D_FORMAT_VERSION) &&
+             job.payload_bytes >= hdr;
+        if (ok && bound) {   // the binding block: known flags, zero reserved words
+            ok = (h[20] & ~kFlagOverwrite) == 0 && h[21] == 0 && h64[11] == 0;
+            ow = (h[20] & kFlagOverwrite) != 0;
+        }
+        ok = ok && h[3] == kBlock && h64[2] == job.n && job.payload_bytes >= hdr + 4 * job.nb &&
              st->desc_bad == 0 && st->sum_c == h64[3] && st->sum_r == h64[4] &&
              st->sum_pos == h64[5] && st->sum_mant == h64[6] && 2 * st->sum_r == h64[7] &&
-             kHeader + 4 * job.nb + st->sum_pos + st->sum_mant + 2 * st->sum_r ==
-                 job.payload_bytes;
+             hdr + 4 * job.nb + st->sum_pos + st->sum_mant + 2 * st->sum_r == job.payload_bytes;
+        // the binding: a version-2 payload applies only to its base version
+        wrong_version = ok && bound && job.version && *job.version != h64[8];
     }
-    st->state = ok ? kStateReady : kStateRejected;
+    st->hdr = hdr;
+    st->ow = ow;
+    st->bound = bound;
+    st->state = !ok ? kStateRejected : (wrong_version ? kStateVersion : kStateReady);
 }
 
 // --------------------------------------------------------------------- plan ---
@@ -170,9 +204,10 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
         p.len_room = 0;
         p.job = lo;
         p.block = 0;
-        if (state[lo].state == kStateReady) {
+        const DecompressState &st = state[lo];
+        if (st.state == kStateReady) {
             const uint64_t b = t - job.block0;
-            const uint64_t D = kHeader + 4 * job.nb + offsets[t];
+            const uint64_t D = st.hdr + 4 * job.nb + offsets[t];
             const uint64_t room = job.payload_bytes - D;   // prepare checked D <= payload_bytes
             if (job.nsegs == 0) {
                 p.w = job.weights + b * kBlock;
@@ -186,9 +221,10 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
                 p.w = job.segs[slo].dst + (e - job.segs[slo].first);
             }
             p.rec = job.payload + D;
-            p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + kHeader + 4 * b);
-            p.len_room = block_length(job.n, b) | (uint32_t)(room < 0x3FFFFu ? room : 0x3FFFFu)
-                                                      << 14;
+            p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + st.hdr + 4 * b);
+            p.len_room = block_length(job.n, b) |
+                         (uint32_t)(room < kRoomCap ? room : kRoomCap) << 14 |
+                         (st.ow ? kPlanOverwrite : 0u);
             p.block = (uint32_t)b;
         }
         plan[t] = p;
@@ -275,7 +311,7 @@ __device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe, uint32_t tid)
     g.r = (pe.desc >> 14) & 0x3FFFu;
     g.code = pe.desc >> 28;
     g.pb = g.code == kCodeBitmap ? (g.L + 7) / 8 : (g.c * g.code + 7) / 8;
-    g.mb = (7 * g.c + 7) / 8;
+    g.mb = (pe.len_room & kPlanOverwrite) ? 0u : (7 * g.c + 7) / 8;   // overwrite: none
     g.len = g.pb + g.mb + 2 * g.r;
     g.lead = (uint32_t)((uintptr_t)pe.rec & 15);
     g.stage = tid < kStageChunks && 16 * tid < g.lead + g.len;
@@ -290,7 +326,7 @@ __device__ __forceinline__ TileGeom tile_geom(const ApplyPlan &pe, uint32_t tid)
 // payload's end.
 __device__ __forceinline__ uint4 load_record_word(const ApplyPlan &pe, uint32_t tid) {
     const TileGeom g = tile_geom(pe, tid);
-    const uint32_t room = g.lead + (pe.len_room >> 14);
+    const uint32_t room = g.lead + ((pe.len_room >> 14) & kRoomCap);
     if (g.L == 0 || g.len == 0 || room < 16) return make_uint4(0, 0, 0, 0);
     // threads past the record reload its last word (the same cache line), so
     // the window costs no HBM traffic beyond the record
@@ -303,7 +339,7 @@ __device__ __forceinline__ uint4 load_record_word(const ApplyPlan &pe, uint32_t 
 
 __device__ __forceinline__ uint4 fix_record_word(const ApplyPlan &pe, uint4 rv, uint32_t tid) {
     const TileGeom g = tile_geom(pe, tid);
-    const uint32_t room = g.lead + (pe.len_room >> 14);
+    const uint32_t room = g.lead + ((pe.len_room >> 14) & kRoomCap);
     if (g.L == 0 || !g.stage || 16 * tid + 16 <= room) return rv;
     BF16D_GMEM const uint8_t *win = pe.rec - g.lead;
     uint32_t w[4] = {0, 0, 0, 0};
@@ -341,8 +377,11 @@ __device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv,
 // [t*F, t*F + F), reads them from one window of three (gaps) and two
 // (mantissas) LDS dwords, keeps them in registers, and writes the XOR of
 // every changed element into s_x.  Returns this thread's share of `bad`.
+// kOw (an overwrite record): no mantissa fields; every change takes the next
+// word, its new value, which goes to s_x as it is.
 constexpr uint32_t kFastFields = 4;
 
+template <bool kOw>
 __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint32_t c,
                                                       uint32_t r, uint32_t w, uint32_t L,
                                                       uint32_t mant0, uint32_t rare0,
@@ -361,8 +400,10 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
         g0 = rb.lds[gd];
         g1 = rb.lds[gd + 1];
         g2 = rb.lds[gd + 2];
-        m0 = rb.lds[md];
-        m1 = rb.lds[md + 1];
+        if (!kOw) {
+            m0 = rb.lds[md];
+            m1 = rb.lds[md + 1];
+        }
     }
     const uint32_t gmask = (1u << w) - 1;
     uint32_t gk[kFastFields], mk[kFastFields];
@@ -371,7 +412,8 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
     for (uint32_t k = 0; k < kFastFields; ++k) {
         gk[k] = window_bits(g0, g1, g2, gsh + k * w) & gmask;
         const uint32_t mp = msh + 7 * k;
-        mk[k] = (mp < 32 ? __builtin_amdgcn_alignbit(m1, m0, mp) : m1 >> (mp - 32)) & kMant;
+        mk[k] = kOw ? 0u : (mp < 32 ? __builtin_amdgcn_alignbit(m1, m0, mp) : m1 >> (mp - 32)) &
+                               kMant;
         if (k < nf) {
             sum_g1 += gk[k] + 1;
             esc += mk[k] == 0;
@@ -386,8 +428,9 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
     const uint32_t e_wave = __popcll(e1) + 2 * __popcll(e2) + 4 * __popcll(e4);
     const uint32_t inc_g = wave_incl_add(sum_g1);
     const uint32_t top_wave = __ballot(top) != 0;
+    const uint32_t tot_g = lane63(inc_g);   // outside the branch below: see lane63
     if (lane == 0) {
-        sa.a[wave] = lane63(inc_g);
+        sa.a[wave] = tot_g;
         sa.b[wave] = e_wave;
         sa.c[wave] = top_wave;
     }
@@ -414,7 +457,7 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
             if (x == 0) {
                 if (e < r) {
                     x = rb.get_staged(rare0 + 16 * e, 16);
-                    bad |= (x & kExpSign) == 0;
+                    if (!kOw) bad |= (x & kExpSign) == 0;
                 } else {
                     bad = 1;
                 }
@@ -434,13 +477,20 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
 //   record window, loaded by the caller before this call so that its latency
 //   overlaps the decode; it is written to s_raw once this tile's record has
 //   been read.
-//   kRollback: undo a previous pass (same decode, no checksum).
-template <bool kRollback>
+//   kPass: kPassApply (XOR, store, checksum), kPassRollback (XOR again, store,
+//   no checksum), kPassVerify (overwrite record: checksum of the result, no
+//   store), kPassCommit (overwrite record: store, no checksum).
+enum : int { kPassApply = 0, kPassRollback = 1, kPassVerify = 2, kPassCommit = 3 };
+
+template <int kPass>
 __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o)[kChunksPerThread],
                                             uint64_t tile, const ApplyPlan &next, uint4 rv_next,
                                             DecompressState *__restrict__ state,
                                             uint64_t *__restrict__ partial, uint16_t *s_x,
                                             uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
+    constexpr bool kOw = kPass == kPassVerify || kPass == kPassCommit;
+    constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify;
+    constexpr bool kStore = kPass != kPassVerify;
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const TileGeom g = tile_geom(pe, tid);
     const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
@@ -448,7 +498,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     RecordBits rb;
     rb.lds = s_raw;
     rb.win = pe.rec - g.lead;
-    rb.room = g.lead + (pe.len_room >> 14);
+    rb.room = g.lead + ((pe.len_room >> 14) & kRoomCap);
     rb.rb0 = 8 * g.lead;
 
     // ---- decode the record into s_x, checking that it is canonical ----
@@ -458,10 +508,17 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     const uint32_t mant0 = 8 * pb, rare0 = 8 * (pb + mb);
     uint32_t bad = 0;
     if (changed) {
-        __syncthreads();   // record staged; s_x clear
+        // overwrite: the tile starts as the current weights, and the decode
+        // writes the new values over them
+        if (kOw) {
+#pragma unroll
+            for (uint32_t i = 0; i < kChunksPerThread; ++i)
+                reinterpret_cast<uint4 *>(s_x)[tid + kThreads * i] = o[i];
+        }
+        __syncthreads();   // record staged; s_x clear (overwrite: s_x = the weights)
         if (code != kCodeBitmap && c <= kFastFields * kThreads &&
             g.lead + g.len + 12 <= 4 * kStageWords) {
-            bad = decode_delta_fast(rb, c, r, code, L, mant0, rare0, s_x, sa, tid);
+            bad = decode_delta_fast<kOw>(rb, c, r, code, L, mant0, rare0, s_x, sa, tid);
             if (tid == 0 && 8 * pb > c * code)               // position padding
                 bad |= rb.get(c * code, 8 * pb - c * code) != 0;
         } else if (code == kCodeBitmap) {
@@ -479,9 +536,10 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
             const uint32_t pop = __popc(word);
             const uint32_t last1 = word ? lo + 32 - __clz(word) : 0;   // last position + 1
             const uint32_t inc_pop = wave_incl_add(pop), inc_last = wave_incl_max(last1);
+            const uint32_t tot_pop = lane63(inc_pop), tot_last = lane63(inc_last);
             if (lane == 0) {
-                sa.a[wave] = lane63(inc_pop);
-                sa.b[wave] = lane63(inc_last);
+                sa.a[wave] = tot_pop;
+                sa.b[wave] = tot_last;
             }
             __syncthreads();
             uint32_t rank0 = inc_pop - pop, prev1 = wave_shr1(inc_last), total = 0;
@@ -502,14 +560,15 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     bits &= bits - 1;
                     maxg = umax32(maxg, p - p1);
                     p1 = p + 1;
-                    esc += rb.get(mant0 + 7 * jj, 7) == 0;
+                    esc += kOw ? 1u : (rb.get(mant0 + 7 * jj, 7) == 0);
                     ++jj;
                 }
             }
             const uint32_t inc_esc = wave_incl_add(esc), wmax = lane63(wave_incl_max(maxg));
+            const uint32_t tot_esc = lane63(inc_esc);
             __syncthreads();   // sa.a / sa.b reads done
             if (lane == 0) {
-                sa.a[wave] = lane63(inc_esc);
+                sa.a[wave] = tot_esc;
                 sa.c[wave] = wmax;
             }
             __syncthreads();
@@ -526,11 +585,11 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
             while (bits) {
                 const uint32_t p = lo + __ffs(bits) - 1;
                 bits &= bits - 1;
-                uint32_t x = rb.get(mant0 + 7 * jj, 7);
+                uint32_t x = kOw ? 0u : rb.get(mant0 + 7 * jj, 7);
                 if (x == 0) {
                     if (e < r) {
                         x = rb.get(rare0 + 16 * e, 16);
-                        bad |= (x & kExpSign) == 0;
+                        if (!kOw) bad |= (x & kExpSign) == 0;
                     } else {
                         bad = 1;
                     }
@@ -550,13 +609,14 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                 const uint32_t g = w ? rb.get(jj * w, w) : 0;
                 sum_g1 += g + 1;
                 maxg = umax32(maxg, g);
-                esc += rb.get(mant0 + 7 * jj, 7) == 0;
+                esc += kOw ? 1u : (rb.get(mant0 + 7 * jj, 7) == 0);
             }
             const uint32_t inc_g = wave_incl_add(sum_g1), inc_e = wave_incl_add(esc);
             const uint32_t wmax = lane63(wave_incl_max(maxg));
+            const uint32_t tot_g = lane63(inc_g), tot_e = lane63(inc_e);
             if (lane == 0) {
-                sa.a[wave] = lane63(inc_g);
-                sa.b[wave] = lane63(inc_e);
+                sa.a[wave] = tot_g;
+                sa.b[wave] = tot_e;
                 sa.c[wave] = wmax;
             }
             __syncthreads();
@@ -579,11 +639,11 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                 const uint32_t g = w ? rb.get(jj * w, w) : 0;
                 run += g + 1;
                 const uint32_t p = run - 1;
-                uint32_t x = rb.get(mant0 + 7 * jj, 7);
+                uint32_t x = kOw ? 0u : rb.get(mant0 + 7 * jj, 7);
                 if (x == 0) {
                     if (e < r) {
                         x = rb.get(rare0 + 16 * e, 16);
-                        bad |= (x & kExpSign) == 0;
+                        if (!kOw) bad |= (x & kExpSign) == 0;
                     } else {
                         bad = 1;
                     }
@@ -612,10 +672,25 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
         const uint32_t q = tid + kThreads * i;
         const uint32_t e0 = 8 * q;
         const uint32_t valid = e0 < L ? (L - e0 < 8 ? L - e0 : 8) : 0;
-        const uint4 t = changed ? reinterpret_cast<const uint4 *>(s_x)[q] : make_uint4(0, 0, 0, 0);
-        const bool dirty = (t.x | t.y | t.z | t.w) != 0;
         uint4 nw = o[i];
-        if (dirty) {
+        if (kOw) {   // the tile holds the result itself
+            const uint4 t = changed ? reinterpret_cast<const uint4 *>(s_x)[q] : nw;
+            const bool dirty = ((t.x ^ nw.x) | (t.y ^ nw.y) | (t.z ^ nw.z) | (t.w ^ nw.w)) != 0;
+            if (changed) reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(0, 0, 0, 0);
+            if (dirty && !bad) {
+                nw = t;
+                BF16D_GMEM uint16_t *dstp = pe.w + e0;
+                if (!kStore) {
+                    // verify: the result is only summed
+                } else if (valid == 8) {
+                    *reinterpret_cast<BF16D_GMEM uint4 *>(dstp) = nw;
+                } else {
+                    for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
+                }
+            }
+        } else if (const uint4 t = changed ? reinterpret_cast<const uint4 *>(s_x)[q]
+                                           : make_uint4(0, 0, 0, 0);
+                   (t.x | t.y | t.z | t.w) != 0) {   // dirty
             // tid >> 16 is 0; written so the zero is not one more register
             // held across the persistent loop
             const uint32_t z = tid >> 16;
@@ -630,14 +705,14 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                 }
             }
         }
-        if (!kRollback) {
+        if (kSum) {
             if (valid > 0) acc += mix64(((uint64_t)nw.y << 32 | nw.x) ^ kg);
             if (valid > 4) acc += mix64(((uint64_t)nw.w << 32 | nw.z) ^ (kg + gamma));
             kg += round_kg;
         }
     }
-    if (!kRollback) {
-        acc = wave_sum(acc);
+    if (kSum) {
+        acc = first_lane(wave_sum(acc));
         if (lane == 0) partial[kWaves * tile + wave] = acc;
         if (tid == 0 && bad) atomicOr(&state[pe.job].block_bad, 1u);
     }
@@ -647,7 +722,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
 // s_raw) from its weight loads to its stores, with the next tile's record
 // word loaded meanwhile.  Whole blocks and the short last block of a tensor
 // are compiled separately (see load_old).
-template <bool kRollback, bool kFull>
+template <int kPass, bool kFull>
 __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &pn, uint64_t t,
                                           DecompressState *__restrict__ state,
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
@@ -655,18 +730,18 @@ __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &
     uint4 o[kChunksPerThread];
     load_old<kFull>(pc, o, tid);
     const uint4 rv_next = fix_record_word(pn, load_record_word(pn, tid), tid);
-    finish_tile<kRollback>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa, tid);
+    finish_tile<kPass>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa, tid);
 }
 
-// A persistent pass over the tiles (the rollback); workgroup g takes tiles
+// A persistent pass over the tiles (rollback and commit); workgroup g takes tiles
 // g, g + G, g + 2G, ...  While a tile is decoded, its old weights and the next tile's
 // record word are in flight, and the plan entry of the tile after that has
 // been requested; the next tile's record is staged in LDS as soon as this
 // one's has been read, so its decode can start at once.  LDS is kept at
 // 20 KiB so that 8 workgroups (8 waves per SIMD) fit on a CU.
-//   kRollback = false: every tile of every job that passed its checks.
-//   kRollback = true : only the tiles of jobs marked for rollback.
-template <bool kRollback>
+//   kPassRollback: only the tiles of jobs marked for rollback.
+//   kPassCommit  : only the tiles of overwrite jobs that passed verification.
+template <int kPass>
 __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
                                            DecompressState *__restrict__ state,
                                            uint64_t *__restrict__ partial, uint64_t tiles) {
@@ -683,7 +758,10 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
     auto fetch = [&](uint64_t u) -> ApplyPlan {
         if (u >= tiles) return none;
         ApplyPlan p = plan[u];
-        if (kRollback && (p.len_room & 0x3FFFu) && state[p.job].rollback == 0) p = none;
+        if (p.len_room & 0x3FFFu) {
+            const DecompressState &st = state[p.job];
+            if ((kPass == kPassRollback ? st.rollback : st.commit) == 0) p = none;
+        }
         return p;
     };
     for (uint32_t u = threadIdx.x; u < kBlock / 8; u += kThreads)
@@ -703,9 +781,9 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
         const ApplyPlan pnn = fetch(t + 2 * G);
         const uint32_t L = pc.len_room & 0x3FFFu;
         if (L == kBlock)
-            pass_step<kRollback, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+            pass_step<kPass, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
         else if (L != 0)
-            pass_step<kRollback, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+            pass_step<kPass, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
         else   // a skipped tile: nothing reads its record
             stage_record_word(pn, fix_record_word(pn, load_record_word(pn, tid), tid), s_raw, tid);
         t += G;
@@ -719,7 +797,7 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
 // and the short last block of a tensor are compiled separately (see
 // load_old), so that the wave waits only for the record word before the
 // decode while the weight loads stay in flight.
-template <bool kFull>
+template <bool kFull, bool kOw>
 __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
                                           DecompressState *__restrict__ state,
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
@@ -730,16 +808,17 @@ __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
     load_old<kFull>(pe, o, tid);
     rv = fix_record_word(pe, rv, tid);
     if (pe.desc & 0x3FFFu) {   // changed elements: the decode needs a clear tile
-        for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
-            reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+        if (!kOw)   // (an overwrite tile is filled with the weights instead)
+            for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
+                reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
         stage_record_word(pe, rv, s_raw, tid);
     }
     ApplyPlan none;
     none.w = nullptr;
     none.rec = nullptr;
     none.desc = none.len_room = none.job = none.block = 0;
-    finish_tile<false>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x, s_raw,
-                       sa, tid);
+    finish_tile<kOw ? kPassVerify : kPassApply>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state,
+                                                partial, s_x, s_raw, sa, tid);
 }
 
 // The apply pass: one workgroup per tile, 8 workgroups per CU (20 KiB of
@@ -757,17 +836,33 @@ void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restric
     const uint64_t tile = blockIdx.x;
     const ApplyPlan pe = plan[tile];
     const uint32_t L = pe.len_room & 0x3FFFu;
-    if (L == kBlock)
-        apply_one<true>(pe, tile, state, partial, s_x, s_raw, sa);
-    else if (L != 0)   // 0: the job was rejected
-        apply_one<false>(pe, tile, state, partial, s_x, s_raw, sa);
+    if (pe.len_room & kPlanOverwrite) {   // overwrite records: verified here, written later
+        if (L == kBlock)
+            apply_one<true, true>(pe, tile, state, partial, s_x, s_raw, sa);
+        else if (L != 0)
+            apply_one<false, true>(pe, tile, state, partial, s_x, s_raw, sa);
+    } else if (L == kBlock) {
+        apply_one<true, false>(pe, tile, state, partial, s_x, s_raw, sa);
+    } else if (L != 0) {   // 0: the job was rejected
+        apply_one<false, false>(pe, tile, state, partial, s_x, s_raw, sa);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void rollback_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
                      const Control *__restrict__ ctrl, uint64_t tiles) {
     if (ctrl->any_rollback == 0) return;
-    apply_pass<true>(plan, state, nullptr, tiles);
+    apply_pass<kPassRollback>(plan, state, nullptr, tiles);
+}
+
+// Overwrite payloads that passed verification: the same decode again, now
+// storing.  Absolute values cannot be undone by applying them twice, so they
+// are written only once the whole result is known to be right.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void commit_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
+                   const Control *__restrict__ ctrl, uint64_t tiles) {
+    if (ctrl->any_commit == 0) return;
+    apply_pass<kPassCommit>(plan, state, nullptr, tiles);
 }
 
 // ------------------------------------------------------------- checksum sum ---
@@ -811,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
     res.reserved = 0;
     res.payload_bytes = job.payload_bytes;
     if (!ready) {
-        res.status = BF16D_EFORMAT;
+        res.status = st->state == kStateVersion ? BF16D_EVERSION : BF16D_EFORMAT;
         res.checksum = 0;
         res.n_changed = res.n_rare = res.n_bitmap_blocks = 0;
     } else {
@@ -822,10 +917,19 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
         res.n_changed = st->sum_c;
         res.n_rare = st->sum_r;
         res.n_bitmap_blocks = st->n_bitmap;
-        if (res.status != BF16D_OK) {
+        if (st->ow) {
+            // overwrite: nothing was written yet; the commit pass writes it
+            if (res.status == BF16D_OK) {
+                st->commit = 1;
+                atomicOr(&ctrl->any_commit, 1u);
+            }
+        } else if (res.status != BF16D_OK) {
             st->rollback = 1;
             atomicOr(&ctrl->any_rollback, 1u);
         }
+        // the joint commit: the version word moves to the target with the weights
+        if (res.status == BF16D_OK && st->bound && job.version)
+            *job.version = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload)[9];
     }
     results[j] = res;
 }
@@ -872,6 +976,8 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     decompress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
         jobs, state, sums, ctrl, count, results);
     if (tiles) {
+        commit_kernel<<<persistent_grid((const void *)commit_kernel, tiles), kThreads, 0,
+                        stream>>>(plan, state, ctrl, tiles);
         rollback_kernel<<<persistent_grid((const void *)rollback_kernel, tiles), kThreads, 0,
                           stream>>>(plan, state, ctrl, tiles);
     }

@@ -14,7 +14,11 @@ namespace bf16d {
 
 // ---- format constants (bf16delta_v1) ---------------------------------------
 constexpr uint32_t kBlock = BF16D_BLOCK_ELEMS;            // elements per block
-constexpr uint32_t kHeader = BF16D_HEADER_BYTES;          // header bytes
+constexpr uint32_t kHeader = BF16D_HEADER_BYTES;          // header bytes (version 1)
+// version 2: the version-1 header fields, then the binding block
+// (u64 base_version, u64 target_version, u32 flags, u32 0, u64 0)
+constexpr uint32_t kHeaderBound = BF16D_HEADER_BYTES_BOUND;   // 96
+constexpr uint32_t kFlagOverwrite = BF16D_BIND_OVERWRITE;     // records carry new values
 constexpr uint32_t kCodeBitmap = 15;
 constexpr uint32_t kCodeInvalid = 14;
 constexpr uint32_t kExpSign = 0xFF80u;                   // sign + exponent bits of a bf16
@@ -62,10 +66,12 @@ struct alignas(64) CompressJob {
     uint64_t capacity;
     uint64_t block0;   // first global tile index of this job
     uint64_t nb;       // blocks of this job
-    uint64_t pad;
+    uint32_t hdr;      // header bytes: kHeader (version 1) or kHeaderBound (version 2)
+    uint32_t flags;    // version 2: kFlagOverwrite or 0
+    uint64_t base_version, target_version;   // version 2 binding
 };
 
-enum JobState : uint32_t { kStateReady = 1, kStateRejected = 2 };
+enum JobState : uint32_t { kStateReady = 1, kStateRejected = 2, kStateVersion = 3 };
 
 // one segment of a remapped tensor: logical elements [first, first + count)
 // live at dst (first is block-aligned)
@@ -86,6 +92,7 @@ struct alignas(64) DecompressJob {
     uint64_t dtile0;   // first global descriptor-scan tile index
     BF16D_GMEM const RemapSegment *segs;   // remapped: the job's segments; else nullptr
     uint32_t nsegs;             // 0: no remap, the weights pointer is used
+    BF16D_GMEM uint64_t *version;   // the receiver's version word, or nullptr
 };
 
 // per-job device state of a decompress call (zeroed by the setup kernel)
@@ -95,6 +102,10 @@ struct alignas(64) DecompressState {
     uint32_t state;        // JobState, set by the prepare kernel
     uint32_t block_bad;    // a block record failed its checks
     uint32_t rollback;     // the apply pass must be undone
+    uint32_t commit;       // overwrite payload verified: the commit pass writes it
+    uint32_t hdr;          // header bytes of the payload (set by the prepare kernel)
+    uint32_t ow;           // an overwrite payload
+    uint32_t bound;        // a version-2 payload
 };
 
 // decompress: everything the apply pass needs about one tile, gathered once
@@ -104,11 +115,14 @@ struct alignas(32) ApplyPlan {
     BF16D_GMEM const uint8_t *rec;   // first byte of the block's record
     uint32_t desc;        // the block's descriptor
     uint32_t len_room;    // block length (bits 0..13; 0 = skip the tile) | payload bytes
-                          // left from `rec`, capped at 2^18 - 1 (bits 14..31)
+                          // left from `rec`, capped at 2^17 - 1 (bits 14..30) |
+                          // kPlanOverwrite (bit 31): an overwrite record
     uint32_t job;
     uint32_t block;       // block index within the job
 };
 static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
+constexpr uint32_t kPlanOverwrite = 1u << 31;
+constexpr uint32_t kRoomCap = (1u << 17) - 1;
 
 // per-job sums (zeroed at the start of a call), accumulated with one atomic
 // per job and scan tile of 2048 blocks: the checksum sum S (both directions,
@@ -134,7 +148,8 @@ struct alignas(64) Control {
     uint32_t dticket;         // dynamic tile ids for the descriptor-scan look-back
     uint32_t any_rollback;    // decompress: some job must be rolled back
     uint32_t overflow_count;  // compress: tiles whose record exceeded a slot
-    uint32_t pad[12];
+    uint32_t any_commit;      // decompress: some overwrite payload is to be written
+    uint32_t pad[11];
 };
 
 // Workspace layout, computed identically by every entry point.
@@ -200,14 +215,17 @@ __device__ __forceinline__ T wave_sum(T v) {
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
     return v;
 }
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        T o = __shfl_xor(v, d, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+// The value lane 0 holds, as a wave-uniform (scalar) value, read where the
+// whole wave is active: a value the wave has just reduced can then be stored
+// by one lane without the reduction moving into that lane's branch.
+__device__ __forceinline__ uint32_t first_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ uint64_t first_lane(uint64_t v) {
+    return (uint64_t)first_lane((uint32_t)v) | (uint64_t)first_lane((uint32_t)(v >> 32)) << 32;
+}
+__device__ __forceinline__ unsigned long long first_lane(unsigned long long v) {
+    return first_lane((uint64_t)v);
 }
 
 // Block-wide sum over kThreads threads; every thread gets the total.
@@ -215,24 +233,12 @@ __device__ __forceinline__ T wave_max(T v) {
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T *s_tmp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum(v);
-    if (lane == 0) s_tmp[wave] = v;
+    const T w = first_lane(wave_sum(v));
+    if (lane == 0) s_tmp[wave] = w;
     __syncthreads();
     T t = 0;
 #pragma unroll
-    for (int w = 0; w < (int)kWaves; ++w) t += s_tmp[w];
-    __syncthreads();
-    return t;
-}
-template <typename T>
-__device__ __forceinline__ T block_max(T v, T *s_tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_max(v);
-    if (lane == 0) s_tmp[wave] = v;
-    __syncthreads();
-    T t = s_tmp[0];
-#pragma unroll
-    for (int w = 1; w < (int)kWaves; ++w) t = s_tmp[w] > t ? s_tmp[w] : t;
+    for (int w2 = 0; w2 < (int)kWaves; ++w2) t += s_tmp[w2];
     __syncthreads();
     return t;
 }
@@ -258,24 +264,6 @@ __device__ __forceinline__ T block_exclusive_sum(T v, T *s_tmp, T &total) {
     __syncthreads();
     total = all;
     return before + inc - v;
-}
-
-// Block-wide exclusive prefix max in thread order (identity `lowest`).
-__device__ __forceinline__ int block_exclusive_max(int v, int lowest, int *s_tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = o > inc ? o : inc;
-    }
-    int excl = __shfl_up(inc, 1, 64);
-    if (lane == 0) excl = lowest;
-    if (lane == 63) s_tmp[wave] = inc;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) excl = s_tmp[w] > excl ? s_tmp[w] : excl;
-    __syncthreads();
-    return excl;
 }
 
 // ---- wave64 DPP scans (GFX9 row_shr / row_bcast / wave_shr) -------------------
@@ -319,11 +307,20 @@ __device__ __forceinline__ uint32_t row_incl_max(uint32_t v) {
     v = umax32(v, dpp_src<0x118>(v));
     return v;
 }
+// Cross-lane reads (readlane_u32, lane63, the DPP scans) belong in control
+// flow that the whole wave executes.  Inside a branch only some lanes take
+// (`if (lane == 0)`), the compiler may compute the operand for the active
+// lanes only, and the read then returns another lane's stale value: take the
+// value before the branch and use it inside.
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, uint32_t lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
 }
 // value of the previous lane (0 for lane 0)
 __device__ __forceinline__ uint32_t wave_shr1(uint32_t v) { return dpp_src<0x138>(v); }
+// value of the previous lane, `fill` for lane 0 (one DPP move, no lane test)
+__device__ __forceinline__ uint32_t wave_shr1_fill(uint32_t v, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, 0x138, 0xf, 0xf, false);
+}
 __device__ __forceinline__ uint32_t lane63(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
@@ -379,7 +376,7 @@ __device__ __forceinline__ uint64_t look_back(uint64_t *status, uint64_t tile, u
 #pragma unroll
         for (int k = 0; k < kLookDepth; ++k)
             if (k < stop_k || (k == stop_k && lane <= stop_lane)) mine += v[k] & kValueMask;
-        excl += wave_sum(mine);
+        excl += first_lane(wave_sum(mine));   // wave-uniform, whatever the caller's branch
         if (stop_k < kLookDepth) return excl;
         pred -= 64 * kLookDepth;
     }
@@ -485,7 +482,7 @@ void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint
 void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                            uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                           const bf16d_events *events);
+                           const bf16d_events *events, bool any_overwrite);
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream,
                              const bf16d_events *events);

@@ -174,3 +174,26 @@ def test_remapped_arguments_are_rejected_before_any_gpu_work(native):
     assert call([(0, 8192, A + 8), (8192, 2 * 8192, B)]) == E        # dst alignment
     assert call([(0, 8192, A), (8192, 2 * 8192, A + 4096)]) == E     # segments overlap
     assert call([(0, 8192, A), (8192, 2 * 8192, None)]) == E         # no destination
+
+
+def test_bound_arguments_are_rejected_before_any_gpu_work(native):
+    lib = native.lib()
+    assert ctypes.sizeof(native.Binding) == 24
+    ws = ctypes.create_string_buffer(1 << 16)
+    jobs = (native.CompressJob * 1)(native.CompressJob(None, None, 0, None, 0))
+    res = ctypes.create_string_buffer(64)
+    ws_ptr = (ctypes.addressof(ws) + 15) // 16 * 16
+    # no bindings array
+    assert lib.bf16d_compress_bound(jobs, None, 1, ws_ptr, 1 << 15, ctypes.addressof(res),
+                                    None) == native.EINVAL
+    for flags, reserved in ((2, 0), (1 | 4, 0), (0, 1)):
+        b = (native.Binding * 1)(native.Binding(0, 1, flags, reserved))
+        assert lib.bf16d_compress_bound(jobs, b, 1, ws_ptr, 1 << 15, ctypes.addressof(res),
+                                        None) == native.EINVAL, (flags, reserved)
+    dj = (native.DecompressJob * 1)(native.DecompressJob(None, 0, None, 0, 0))
+    # version words must be 8-byte aligned and may not overlap the workspace
+    assert lib.bf16d_decompress_bound(dj, ws_ptr + 3, 1, ws_ptr, 1 << 15, ctypes.addressof(res),
+                                      None) == native.EINVAL
+    assert lib.bf16d_decompress_bound(dj, ws_ptr + 64, 1, ws_ptr, 1 << 15,
+                                      ctypes.addressof(res), None) == native.EINVAL
+    assert native.status_string(native.EVERSION).startswith("EVERSION")
