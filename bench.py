@@ -23,6 +23,8 @@ Reported:
               timed with events recorded around it on its stream
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
+  bound_overwrite : the same pair as version-2 overwrite payloads (absolute
+              values, verified then written, version words committed)
   codec_race : the host race of general-purpose codecs over every payload,
               and the payload % of the weights after it
   streamed_receiver : the same decompress with the payloads in pinned host
@@ -265,6 +267,56 @@ def remapped(bd, names, shapes, pairs, payloads, cs_new, cs_old, steps):
             "gbps_weights": round(2 * n / t / 1e9, 2)}
 
 
+def bound_overwrite(bd, pairs, steps):
+    """Version-2 payloads of the same checkpoint pair in overwrite form (each
+    change carries its new value; the apply is verified, then written), bound
+    from version 1 to 2, applied with the receiver's version words.  Reports
+    the payload size and whole-call times beside the XOR path's."""
+    n = sum(s.numel() for s, _ in pairs)
+    binds = [(1, 2, True)] * len(pairs)
+    caps = [bd._first_capacity(s.numel()) + bd.BOUND_EXTRA_BYTES for s, _ in pairs]
+    comp = bd.CompressBatch(pairs, caps, binds)
+    comp.run()
+    res = comp.results()
+    if any(r["status"] != bd.OK for r in res):
+        comp = bd.CompressBatch(pairs, [r["payload_bytes"] for r in res], binds)
+        comp.run()
+        res = comp.results()
+    assert all(r["status"] == bd.OK for r in res), "overwrite compress failed"
+    P = sum(r["payload_bytes"] for r in res)
+    recv = [s.clone() for s, _ in pairs]
+    ver = torch.ones(len(pairs), dtype=torch.int64, device=pairs[0][0].device)
+    items = [(w, comp.payload(j, r["payload_bytes"]), r["checksum"])
+             for j, (w, r) in enumerate(zip(recv, res))]
+    dec = bd.DecompressBatch(items, ver)
+    t_c, t_d = [], []
+    for i in range(steps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        comp.run()
+        e[1].record()
+        for w, (s, _) in zip(recv, pairs):
+            w.copy_(s)
+        ver.fill_(1)
+        e[2].record()
+        dec.run()
+        e[3].record()
+        torch.cuda.synchronize()
+        assert all(r["status"] == bd.OK for r in dec.results()), "overwrite decompress failed"
+        assert ver.cpu().tolist() == [2] * len(pairs), "version words not committed"
+        if i:
+            t_c.append(e[0].elapsed_time(e[1]) / 1e3)
+            t_d.append(e[2].elapsed_time(e[3]) / 1e3)
+    for w, (_, d) in zip(recv, pairs):
+        assert torch.equal(w.view(torch.int16), d.view(torch.int16)), "overwrite not bit-exact"
+    tc, td = float(np.median(t_c)), float(np.median(t_d))
+    del recv, dec, comp
+    return {"payload_bytes": P, "payload_pct_of_orig": round(100 * P / (2 * n), 4),
+            "compress_ms": round(1e3 * tc, 4), "compress_gbps_weights": round(2 * n / tc / 1e9, 2),
+            "decompress_ms": round(1e3 * td, 4),
+            "decompress_gbps_weights": round(2 * n / td / 1e9, 2)}
+
+
 def cpu_baseline(pairs, gpu_payloads, budget_s: float):
     """The CPU oracle, single-threaded, timed on a bounded sample of the
     workload's tensors, walking from the last tensor back.  Each oracle
@@ -321,6 +373,8 @@ def main():
                     help="skip the streamed receiver (payloads in pinned host memory)")
     ap.add_argument("--no-remapped", action="store_true",
                     help="skip the remapped apply (gate/up paired in groups of 64 rows)")
+    ap.add_argument("--no-bound", action="store_true",
+                    help="skip the version-2 overwrite payloads")
     ap.add_argument("--no-race", action="store_true",
                     help="skip the host codec race over the payloads")
     ap.add_argument("--race-threads", type=int, default=16,
@@ -446,6 +500,10 @@ def main():
         remap_info = remapped(bd, names, [sp.shape for sp in specs], pairs, payloads, cs_new,
                               cs_old, 4)
 
+    bound_info = None
+    if not args.no_bound:
+        bound_info = bound_overwrite(bd, pairs, 3)
+
     race_info = None
     if not args.no_race:
         race_info = codec_race(bd, payloads, max(1, min(args.race_threads, os.cpu_count() or 1)))
@@ -496,6 +554,7 @@ def main():
                                 "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,
+        "bound_overwrite": bound_info,
         "codec_race": race_info,
         "cpu_baseline": cpu,
     }

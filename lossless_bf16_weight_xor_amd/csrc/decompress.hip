@@ -381,12 +381,14 @@ __device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv,
 // word, its new value, which goes to s_x as it is.
 constexpr uint32_t kFastFields = 4;
 
-template <bool kOw>
+//   kDirect: each value is stored straight to its weight (the commit of a
+//   verified overwrite record) instead of into s_x.
+template <bool kOw, bool kDirect>
 __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint32_t c,
                                                       uint32_t r, uint32_t w, uint32_t L,
                                                       uint32_t mant0, uint32_t rare0,
                                                       uint16_t *s_x, ApplyShared &sa,
-                                                      uint32_t tid) {
+                                                      uint32_t tid, BF16D_GMEM uint16_t *wts) {
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const uint32_t F = (c + kThreads - 1) / kThreads;
     const uint32_t jb = tid * F < c ? tid * F : c;
@@ -463,7 +465,12 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
                 }
                 ++e;
             }
-            if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
+            if (p >= L)
+                bad = 1;
+            else if (kDirect)
+                wts[p] = (uint16_t)x;
+            else
+                s_x[p] = (uint16_t)x;
         }
     }
     return bad;
@@ -491,6 +498,9 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     constexpr bool kOw = kPass == kPassVerify || kPass == kPassCommit;
     constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify;
     constexpr bool kStore = kPass != kPassVerify;
+    // the commit writes each verified value at its position: absolute values
+    // need neither the old weights nor the tile
+    constexpr bool kDirect = kPass == kPassCommit;
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const TileGeom g = tile_geom(pe, tid);
     const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
@@ -510,7 +520,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     if (changed) {
         // overwrite: the tile starts as the current weights, and the decode
         // writes the new values over them
-        if (kOw) {
+        if (kOw && !kDirect) {
 #pragma unroll
             for (uint32_t i = 0; i < kChunksPerThread; ++i)
                 reinterpret_cast<uint4 *>(s_x)[tid + kThreads * i] = o[i];
@@ -518,7 +528,8 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
         __syncthreads();   // record staged; s_x clear (overwrite: s_x = the weights)
         if (code != kCodeBitmap && c <= kFastFields * kThreads &&
             g.lead + g.len + 12 <= 4 * kStageWords) {
-            bad = decode_delta_fast<kOw>(rb, c, r, code, L, mant0, rare0, s_x, sa, tid);
+            bad = decode_delta_fast<kOw, kDirect>(rb, c, r, code, L, mant0, rare0, s_x, sa, tid,
+                                                  pe.w);
             if (tid == 0 && 8 * pb > c * code)               // position padding
                 bad |= rb.get(c * code, 8 * pb - c * code) != 0;
         } else if (code == kCodeBitmap) {
@@ -595,7 +606,10 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     }
                     ++e;
                 }
-                s_x[p] = (uint16_t)x;
+                if (kDirect)
+                    pe.w[p] = (uint16_t)x;
+                else
+                    s_x[p] = (uint16_t)x;
                 ++jj;
             }
         } else {
@@ -649,7 +663,12 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     }
                     ++e;
                 }
-                if (p < L) s_x[p] = (uint16_t)x; else bad = 1;
+                if (p >= L)
+                    bad = 1;
+                else if (kDirect)
+                    pe.w[p] = (uint16_t)x;
+                else
+                    s_x[p] = (uint16_t)x;
             }
             if (tid == 0 && 8 * pb > c * w)                  // position padding
                 bad |= rb.get(c * w, 8 * pb - c * w) != 0;
@@ -659,6 +678,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
         bad = block_any(bad, sa, tid);   // s_x complete; every read of s_raw done
     }
     stage_record_word(next, rv_next, s_raw, tid);
+    if (kDirect) return;   // the values are written; the tile was not used
 
     // ---- new = old ^ tile; store only changed chunks; clear the tile ----
     uint64_t acc = 0;
@@ -728,7 +748,12 @@ __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
                                           uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
     uint4 o[kChunksPerThread];
-    load_old<kFull>(pc, o, tid);
+    if (kPass == kPassCommit) {   // writes values only: the old weights are not read
+#pragma unroll
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) o[i] = make_uint4(0, 0, 0, 0);
+    } else {
+        load_old<kFull>(pc, o, tid);
+    }
     const uint4 rv_next = fix_record_word(pn, load_record_word(pn, tid), tid);
     finish_tile<kPass>(pc, o, t, pn, rv_next, state, partial, s_x, s_raw, sa, tid);
 }
