@@ -354,3 +354,31 @@ def page_example(seed: int = 0):
     src = torch.randn((1024, 1024), generator=gen, dtype=torch.bfloat16)
     noise = torch.randn((1024, 1024), generator=gen, dtype=torch.bfloat16)
     return src, src + 1e-3 * noise
+
+
+# ------------------------------------------------------ the largest sizes ---
+
+def huge_pair(n: int, seed: int, device):
+    """A pair for the largest-size checks, built in chunks so no index
+    permutation of n elements is needed: old ~ N(0, 0.02) in bf16, and every
+    element of new differs from old.  Element i's change flips mantissa bits
+    (a non-zero 7-bit pattern drawn per element); when i % 3 == 0 it also
+    flips the lowest exponent bit, and when i % 97 == 0 the sign bit too.
+    Returns (old, new) as flat bfloat16 tensors."""
+    gen = generator(seed, device)
+    old = torch.empty(n, dtype=torch.bfloat16, device=device)
+    new = torch.empty(n, dtype=torch.bfloat16, device=device)
+    step = 1 << 28
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        o = normal_bf16((b - a,), gen, device)
+        idx = torch.arange(a, b, device=device, dtype=torch.int64)
+        x = torch.randint(1, 128, (b - a,), generator=gen, device=device, dtype=torch.int32)
+        x = x | torch.where(idx % 3 == 0, 0x0080, 0).to(torch.int32)
+        x = x | torch.where(idx % 97 == 0, 0x8000, 0).to(torch.int32)
+        ob = o.view(torch.int16).to(torch.int32) & 0xFFFF
+        nb = (ob ^ x).to(torch.int16)
+        old[a:b] = o
+        new[a:b] = nb.view(torch.bfloat16)
+        del o, idx, x, ob, nb
+    return old, new

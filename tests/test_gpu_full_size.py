@@ -119,3 +119,50 @@ def test_config5_70b_half_model_sampled_and_properties():
     log("  reverse payloads identical")
     _apply_in_place_and_compare(pairs, comp, res)
     log("  round trip bit-exact")
+
+
+def test_tensor_beyond_four_billion_elements():
+    """One tensor of 2^32 + 12345 elements with every element changed and a
+    third of them rare: its payload passes 4 GiB, so block indices, record
+    offsets and the payload arena all need 64 bits.  The head and the tail
+    blocks are compared with the oracle run on those blocks alone (a block's
+    record depends only on its own elements); the whole tensor by the round
+    trip and by the payload depending only on the mask."""
+    n = (1 << 32) + 12345
+    log(f"case tensor of {n} elements, all changed")
+    src, dst = synth.huge_pair(n, 77, DEV)
+    pairs = [(src, dst)]
+    comp, res = _compress_like_bench(pairs)
+    r = res[0]
+    assert r["n_changed"] == n
+    # rare: i % 3 == 0, plus i % 97 == 0 among the others
+    assert r["n_rare"] == -(-n // 3) + (-(-n // 97) - -(-n // 291))
+    P = r["payload_bytes"]
+    assert P > (1 << 32), P
+    payload = comp.payload(0, P)
+    nb = -(-n // 8192)
+    desc = payload[64:64 + 4 * nb].cpu().numpy().view("<u4").astype(np.int64)
+    c, rr, code = desc & 0x3FFF, (desc >> 14) & 0x3FFF, desc >> 28
+    L = np.full(nb, 8192, np.int64)
+    L[-1] = n - 8192 * (nb - 1)
+    pb = np.where(code == 15, (L + 7) // 8, (c * np.where(code == 15, 0, code) + 7) // 8)
+    lens = pb + (7 * c + 7) // 8 + 2 * rr
+    starts = 64 + 4 * nb + np.concatenate([[0], np.cumsum(lens)[:-1]])
+    assert starts[-1] + lens[-1] == P
+    for name, b0, b1 in (("head", 0, 3), ("tail", nb - 3, nb)):
+        lo, hi = 8192 * b0, min(n, 8192 * b1)
+        ref, ref_cs, _ = oracle.compress(to_u16(src[lo:hi]), to_u16(dst[lo:hi]))
+        k = b1 - b0
+        assert np.array_equal(desc[b0:b1], ref[64:64 + 4 * k].view("<u4").astype(np.int64)), name
+        got = payload[int(starts[b0]):int(starts[b1 - 1] + lens[b1 - 1])].cpu().numpy()
+        assert_same_bytes(got, ref[64 + 4 * k:], f"{name} records")
+    log("  head and tail blocks agree with the oracle")
+    rev = bd.CompressBatch([(dst, src)], [P])
+    rev.run()
+    rres = rev.results()
+    assert rres[0]["status"] == bd.OK and rres[0]["payload_bytes"] == P
+    assert torch.equal(rev.payload(0, P), payload)
+    del rev
+    log("  reverse payload identical")
+    _apply_in_place_and_compare(pairs, comp, res)
+    log("  round trip bit-exact")
