@@ -84,3 +84,29 @@ def test_remapped_failure_leaves_the_physical_layout_old():
         assert res[j]["status"] == oracle.decompress_inplace(w, payload.cpu().numpy(), cs)
         assert res[j]["status"] != bd.OK
     assert torch.equal(fused.view(torch.int16), old.view(torch.int16))
+
+
+@pytest.mark.parametrize("overwrite", [False, True])
+def test_remapped_apply_of_version_2_payloads(overwrite):
+    """Bound payloads through the remapped call (the binding is not checked
+    there): overwrite records are verified on the physical layout and then
+    written at their remapped positions."""
+    log(f"case remapped version-2 overwrite={overwrite}")
+    R, C = 512, 128
+    (g0, g1) = synth.make_pair((R, C), "0.3", synth.MIX_ADVERSARIAL, 6100, DEV)
+    (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_ADVERSARIAL, 6101, DEV)
+    out = bd.compress_batch([(g0.reshape(-1), g1.reshape(-1)), (u0.reshape(-1), u1.reshape(-1))],
+                            [(1, 2, overwrite), (1, 2, overwrite)])
+    fused = _paired(g0, u0)
+    want = _paired(g1, u1)
+    items = [((R * C, _segments(fused, 0, R, C)), out[0][0], out[0][1]),
+             ((R * C, _segments(fused, 1, R, C)), out[1][0], out[1][1])]
+    res = bd.decompress_remapped(items)
+    assert [r["status"] for r in res] == [bd.OK, bd.OK]
+    assert torch.equal(fused.view(torch.int16), want.view(torch.int16))
+    # a wrong checksum on an overwrite payload leaves the fused layout untouched
+    before = fused.clone()
+    items[0] = (items[0][0], out[0][0], out[0][1] ^ 1)
+    res = bd.decompress_remapped(items[:1])
+    assert res[0]["status"] == bd.ECHECKSUM
+    assert torch.equal(fused.view(torch.int16), before.view(torch.int16))

@@ -101,3 +101,26 @@ def test_raced_payloads_stream_into_the_receiver():
     assert [r["status"] for r in res] == [bd.OK] * len(pairs)
     for w, (_, d) in zip(recv, pairs):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16))
+
+
+def test_streamed_groups_mix_xor_and_overwrite_payloads():
+    """Version-1 XOR payloads and version-2 overwrite payloads in the same
+    groups: each group's commit pass writes its verified overwrite jobs."""
+    log("case streamed mixed versions")
+    shapes = [(3 * 8192 + 77,), (8192,), (70001,), (2 * 8192,), (12345,), (4096, 64)]
+    pairs = [tuple(t.reshape(-1) for t in synth.make_pair(sh, r, synth.MIX_ADVERSARIAL,
+                                                          2100 + i, DEV))
+             for i, (sh, r) in enumerate(zip(shapes, ["0.03", "0.6", "0.02", "1.0", "0.1",
+                                                      "0.3"]))]
+    payloads, checksums = [], []
+    for j, (s, d) in enumerate(pairs):
+        binds = [(0, 1, True)] if j % 2 else None
+        p, cs, _ = bd.compress_batch([(s, d)], binds)[0]
+        payloads.append(p.cpu().pin_memory())
+        checksums.append(cs)
+    checksums[5] ^= 1                       # an overwrite job that must stay untouched
+    recv, res = _run(pairs, payloads, checksums, [2, 3, 1])
+    assert [r["status"] for r in res] == [bd.OK] * 5 + [bd.ECHECKSUM]
+    for j, (w, (s, d)) in enumerate(zip(recv, pairs)):
+        ref = s if j == 5 else d
+        assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"tensor {j}"
