@@ -6,14 +6,16 @@
 // then checks them against the trainer's checksum ("Every byte counts: ARCv3
 // and the case for cross-region RL", section "Deep dive into ARCv3").
 //
-// Kernels of one batched call, in stream order:
+// Kernels of one batched call, in stream order (six launches):
+//   setup     : clears the call's state and builds the descriptor-tile -> job
+//               map.
 //   desc_scan : validates every descriptor and builds the block offset table
 //               (the exclusive sum of record sizes within each job).  It uses
 //               the same decoupled look-back as the encoder, over tiles of
-//               2048 descriptors.
-//   prepare   : one thread per job; checks the header against the arguments
-//               and against the descriptor sums.  A job that fails is
-//               rejected before any weight is touched.
+//               2048 descriptors.  Its last workgroup then checks each job's
+//               header against the arguments and the descriptor sums; a job
+//               that fails is rejected before any weight is touched.
+//   plan      : one entry per block: its weight and record addresses.
 //   apply     : one workgroup per 8192-element block.  The block's old
 //               weights are loaded into registers first, so HBM latency
 //               overlaps the decode; occupancy (up to 6 workgroups per CU)
@@ -22,19 +24,21 @@
 //               is canonical.  Then old ^ tile is formed, only the changed
 //               16-byte chunks are written back, and the checksum terms of
 //               the result are accumulated.
-//   finalize  : one thread per job; compares the checksum and writes the
-//               result.
-//   rollback  : the apply kernel again, for the jobs that failed only.  XOR
-//               is its own inverse, so this restores the old weights exactly.
+//   sum       : adds up each job's checksum terms; its last workgroup
+//               compares every job's checksum and writes the results.
+//   fixup     : the apply pass again, for the failed jobs only (XOR is its
+//               own inverse, so this restores the old weights exactly) and for
+//               verified overwrite payloads; it exits at once when there is
+//               neither.
 //
 // Version-2 payloads ("GPU-accelerated Weight Teleportation", section "Eval,
 // fault tolerance, and resuming from trained checkpoints"; the NeMo
-// Delta-Compressed Refit summary): the prepare kernel refuses a payload whose
+// Delta-Compressed Refit summary): the header check refuses a payload whose
 // base version is not the receiver's, before anything is touched, and the
-// finalize kernel moves the receiver's version word to the target together
+// checksum step moves the receiver's version word to the target together
 // with the weights.  An overwrite payload carries absolute values, which
 // applying again cannot undo, so the apply kernel only verifies it (the
-// checksum of the would-be result, no stores) and a commit pass writes it
+// checksum of the would-be result, no stores) and the fix-up pass writes it
 // once verified: the weights end new, or untouched.
 #include "internal.hpp"
 
@@ -46,11 +50,50 @@ __device__ __forceinline__ uint32_t block_length(uint64_t n, uint64_t b) {
     return left < kBlock ? (uint32_t)left : kBlock;
 }
 
+// ------------------------------------------------------------------ prepare ---
+// Job j's header against its arguments and its descriptor sums (read with
+// device-scope loads: the scan's last workgroup runs this right after the
+// other workgroups' atomics).
+__device__ void prepare_job(const DecompressJob *__restrict__ jobs,
+                            DecompressState *__restrict__ state, uint32_t j) {
+    const DecompressJob job = jobs[j];
+    DecompressState *st = &state[j];
+    const unsigned long long sum_c = ld_agent(&st->sum_c), sum_r = ld_agent(&st->sum_r),
+                             sum_pos = ld_agent(&st->sum_pos),
+                             sum_mant = ld_agent(&st->sum_mant);
+    const uint32_t desc_bad = ld_agent(&st->desc_bad);
+    bool ok = job.payload_bytes >= kHeader;
+    bool bound = false, ow = false, wrong_version = false;
+    uint32_t hdr = kHeader;
+    if (ok) {
+        BF16D_GMEM const uint32_t *h = reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload);
+        BF16D_GMEM const uint64_t *h64 = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload);
+        bound = h[2] == BF16D_FORMAT_VERSION_BOUND;
+        hdr = bound ? kHeaderBound : kHeader;
+        ok = h[0] == kMagicLo && h[1] == kMagicHi && (bound || h[2] == BF16D_FORMAT_VERSION) &&
+             job.payload_bytes >= hdr;
+        if (ok && bound) {   // the binding block: known flags, zero reserved words
+            ok = (h[20] & ~kFlagOverwrite) == 0 && h[21] == 0 && h64[11] == 0;
+            ow = (h[20] & kFlagOverwrite) != 0;
+        }
+        ok = ok && h[3] == kBlock && h64[2] == job.n && job.payload_bytes >= hdr + 4 * job.nb &&
+             desc_bad == 0 && sum_c == h64[3] && sum_r == h64[4] && sum_pos == h64[5] &&
+             sum_mant == h64[6] && 2 * sum_r == h64[7] &&
+             hdr + 4 * job.nb + sum_pos + sum_mant + 2 * sum_r == job.payload_bytes;
+        // the binding: a version-2 payload applies only to its base version
+        wrong_version = ok && bound && job.version && *job.version != h64[8];
+    }
+    st->hdr = hdr;
+    st->ow = ow;
+    st->bound = bound;
+    st->state = !ok ? kStateRejected : (wrong_version ? kStateVersion : kStateReady);
+}
+
 // ---------------------------------------------------------------- desc_scan ---
 __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
     const DecompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
     uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets,
-    DecompressState *__restrict__ state, Control *__restrict__ ctrl) {
+    DecompressState *__restrict__ state, Control *__restrict__ ctrl, uint32_t count) {
     __shared__ uint32_t s_tmp32[kWaves];
     __shared__ unsigned long long s_tmp64[kWaves];
     __shared__ uint32_t s_dt;
@@ -66,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
     const DecompressJob job = jobs[j];
     const uint64_t ld = dt - job.dtile0;
     // header size and record kind, read before the header is validated (the
-    // prepare kernel rejects the job if they were wrong)
+    // header check rejects the job if they were wrong)
     uint32_t hdr = kHeader;
     bool ow = false;
     if (job.payload_bytes >= kHeaderBound) {
@@ -135,49 +178,25 @@ __global__ __launch_bounds__(kThreads) void desc_scan_kernel(
     mant_sum = block_sum(mant_sum, s_tmp64);
     nbm = block_sum(nbm, s_tmp64);
     const uint32_t any_bad = __syncthreads_or(bad);
+    uint64_t dep = 0;
     if (tid == 0) {
         DecompressState *st = &state[j];
-        atomicAdd(&st->sum_c, c_sum);
-        atomicAdd(&st->sum_r, r_sum);
-        atomicAdd(&st->sum_pos, pos_sum);
-        atomicAdd(&st->sum_mant, mant_sum);
-        atomicAdd(&st->n_bitmap, nbm);
-        if (any_bad) atomicOr(&st->desc_bad, 1u);
+        dep = atomicAdd(&st->sum_c, c_sum) ^ atomicAdd(&st->sum_r, r_sum) ^
+              atomicAdd(&st->sum_pos, pos_sum) ^ atomicAdd(&st->sum_mant, mant_sum) ^
+              atomicAdd(&st->n_bitmap, nbm);
+        if (any_bad) dep ^= atomicOr(&st->desc_bad, 1u);
     }
+    // the last workgroup to finish checks every job's header against the sums
+    if (last_workgroup(&ctrl->scan_done, dep))
+        for (uint32_t jj = tid; jj < count; jj += kThreads) prepare_job(jobs, state, jj);
 }
 
-// ------------------------------------------------------------------ prepare ---
+// For calls without descriptors (every tensor empty); otherwise the scan's
+// last workgroup prepares the jobs.
 __global__ void prepare_kernel(const DecompressJob *__restrict__ jobs,
                                DecompressState *__restrict__ state, uint32_t count) {
     const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= count) return;
-    const DecompressJob job = jobs[j];
-    DecompressState *st = &state[j];
-    bool ok = job.payload_bytes >= kHeader;
-    bool bound = false, ow = false, wrong_version = false;
-    uint32_t hdr = kHeader;
-    if (ok) {
-        BF16D_GMEM const uint32_t *h = reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload);
-        BF16D_GMEM const uint64_t *h64 = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload);
-        bound = h[2] == BF16D_FORMAT_VERSION_BOUND;
-        hdr = bound ? kHeaderBound : kHeader;
-        ok = h[0] == kMagicLo && h[1] == kMagicHi && (bound || h[2] == BF16D_FORMAT_VERSION) &&
-             job.payload_bytes >= hdr;
-        if (ok && bound) {   // the binding block: known flags, zero reserved words
-            ok = (h[20] & ~kFlagOverwrite) == 0 && h[21] == 0 && h64[11] == 0;
-            ow = (h[20] & kFlagOverwrite) != 0;
-        }
-        ok = ok && h[3] == kBlock && h64[2] == job.n && job.payload_bytes >= hdr + 4 * job.nb &&
-             st->desc_bad == 0 && st->sum_c == h64[3] && st->sum_r == h64[4] &&
-             st->sum_pos == h64[5] && st->sum_mant == h64[6] && 2 * st->sum_r == h64[7] &&
-             hdr + 4 * job.nb + st->sum_pos + st->sum_mant + 2 * st->sum_r == job.payload_bytes;
-        // the binding: a version-2 payload applies only to its base version
-        wrong_version = ok && bound && job.version && *job.version != h64[8];
-    }
-    st->hdr = hdr;
-    st->ow = ow;
-    st->bound = bound;
-    st->state = !ok ? kStateRejected : (wrong_version ? kStateVersion : kStateReady);
+    if (j < count) prepare_job(jobs, state, j);
 }
 
 // --------------------------------------------------------------------- plan ---
@@ -764,10 +783,10 @@ __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &
 // been requested; the next tile's record is staged in LDS as soon as this
 // one's has been read, so its decode can start at once.  LDS is kept at
 // 20 KiB so that 8 workgroups (8 waves per SIMD) fit on a CU.
-//   kPassRollback: only the tiles of jobs marked for rollback.
-//   kPassCommit  : only the tiles of overwrite jobs that passed verification.
-template <int kPass>
-__device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
+// It visits the tiles of jobs marked for rollback (an XOR pass again) and of
+// overwrite jobs that passed verification (their values written); the tile's
+// plan entry says which.
+__device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
                                            DecompressState *__restrict__ state,
                                            uint64_t *__restrict__ partial, uint64_t tiles) {
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];        // dense XOR tile
@@ -785,7 +804,7 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
         ApplyPlan p = plan[u];
         if (p.len_room & 0x3FFFu) {
             const DecompressState &st = state[p.job];
-            if ((kPass == kPassRollback ? st.rollback : st.commit) == 0) p = none;
+            if ((st.rollback | st.commit) == 0) p = none;
         }
         return p;
     };
@@ -805,10 +824,15 @@ __device__ __forceinline__ void apply_pass(const ApplyPlan *__restrict__ plan,
         asm volatile("" : "+v"(tid));
         const ApplyPlan pnn = fetch(t + 2 * G);
         const uint32_t L = pc.len_room & 0x3FFFu;
-        if (L == kBlock)
-            pass_step<kPass, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        const bool ow = (pc.len_room & kPlanOverwrite) != 0;
+        if (L == kBlock && ow)
+            pass_step<kPassCommit, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        else if (L == kBlock)
+            pass_step<kPassRollback, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        else if (L != 0 && ow)
+            pass_step<kPassCommit, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
         else if (L != 0)
-            pass_step<kPass, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+            pass_step<kPassRollback, false>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
         else   // a skipped tile: nothing reads its record
             stage_record_word(pn, fix_record_word(pn, load_record_word(pn, tid), tid), s_raw, tid);
         t += G;
@@ -873,60 +897,30 @@ void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restric
     }
 }
 
+// After the finalize step: the rollback of failed XOR jobs (applying the same
+// mask again restores the old weights exactly) and the writing of verified
+// overwrite payloads, in one persistent pass that exits at once when there
+// is neither.  Absolute values cannot be undone by applying them twice, so
+// they are written only once the whole result is known to be right.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
-void rollback_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
-                     const Control *__restrict__ ctrl, uint64_t tiles) {
-    if (ctrl->any_rollback == 0) return;
-    apply_pass<kPassRollback>(plan, state, nullptr, tiles);
-}
-
-// Overwrite payloads that passed verification: the same decode again, now
-// storing.  Absolute values cannot be undone by applying them twice, so they
-// are written only once the whole result is known to be right.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
-void commit_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
-                   const Control *__restrict__ ctrl, uint64_t tiles) {
-    if (ctrl->any_commit == 0) return;
-    apply_pass<kPassCommit>(plan, state, nullptr, tiles);
-}
-
-// ------------------------------------------------------------- checksum sum ---
-// The checksum sum S of every job that was applied: one workgroup per 2048
-// blocks (the descriptor-scan tiles) sums its blocks' per-wave partials and
-// adds them to the job's total with one atomic (exact mod 2^64 in any order).
-__global__ __launch_bounds__(kThreads) void sum_partials_kernel(
-    const DecompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
-    const DecompressState *__restrict__ state, const uint64_t *__restrict__ partial,
-    JobSums *__restrict__ sums) {
-    __shared__ unsigned long long s_tmp[kWaves];
-    const uint64_t dt = blockIdx.x;
-    const uint32_t j = dtile_job[dt];
-    if (state[j].state != kStateReady) return;   // uniform: nothing was applied
-    const DecompressJob &job = jobs[j];
-    const uint64_t ld = dt - job.dtile0;
-    unsigned long long S = 0;
-#pragma unroll
-    for (uint32_t k = 0; k < kDescPerThread; ++k) {
-        const uint64_t b = ld * kDescTile + kDescPerThread * threadIdx.x + k;
-        if (b < job.nb)
-#pragma unroll
-            for (uint32_t w = 0; w < kWaves; ++w) S += partial[kWaves * (job.block0 + b) + w];
-    }
-    S = block_sum(S, s_tmp);
-    if (threadIdx.x == 0) atomicAdd(&sums[j].csum, S);
+void fixup_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
+                  const Control *__restrict__ ctrl, uint64_t tiles) {
+    if ((ctrl->any_rollback | ctrl->any_commit) == 0) return;
+    fixup_pass(plan, state, nullptr, tiles);
 }
 
 // ----------------------------------------------------------------- finalize ---
-__global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
-    const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
-    const JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
-    bf16d_result *__restrict__ results) {
-    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= count) return;
+// Job j's checksum comparison, status and result.  The sums are read with
+// device-scope loads: the checksum kernel's last workgroup runs this right
+// after the other workgroups' atomics.
+__device__ void finalize_job(const DecompressJob *__restrict__ jobs,
+                             DecompressState *__restrict__ state,
+                             const JobSums *__restrict__ sums, Control *__restrict__ ctrl,
+                             bf16d_result *__restrict__ results, uint32_t j) {
     const DecompressJob job = jobs[j];
     DecompressState *st = &state[j];
     const bool ready = st->state == kStateReady;
-    const unsigned long long S = sums[j].csum;
+    const unsigned long long S = ld_agent(&sums[j].csum);
     bf16d_result res;
     res.reserved = 0;
     res.payload_bytes = job.payload_bytes;
@@ -936,14 +930,14 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
         res.n_changed = res.n_rare = res.n_bitmap_blocks = 0;
     } else {
         const uint64_t cs = mix64(S ^ job.n);
-        res.status = st->block_bad ? BF16D_EFORMAT
-                                   : (cs != job.checksum ? BF16D_ECHECKSUM : BF16D_OK);
+        res.status = ld_agent(&st->block_bad) ? BF16D_EFORMAT
+                                              : (cs != job.checksum ? BF16D_ECHECKSUM : BF16D_OK);
         res.checksum = cs;
         res.n_changed = st->sum_c;
         res.n_rare = st->sum_r;
         res.n_bitmap_blocks = st->n_bitmap;
         if (st->ow) {
-            // overwrite: nothing was written yet; the commit pass writes it
+            // overwrite: nothing was written yet; the fix-up pass writes it
             if (res.status == BF16D_OK) {
                 st->commit = 1;
                 atomicOr(&ctrl->any_commit, 1u);
@@ -957,6 +951,50 @@ __global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
             *job.version = reinterpret_cast<BF16D_GMEM const uint64_t *>(job.payload)[9];
     }
     results[j] = res;
+}
+
+// For calls without tiles; otherwise the checksum kernel's last workgroup
+// finalizes the jobs.
+__global__ __launch_bounds__(kThreads) void decompress_finalize_kernel(
+    const DecompressJob *__restrict__ jobs, DecompressState *__restrict__ state,
+    const JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
+    bf16d_result *__restrict__ results) {
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < count) finalize_job(jobs, state, sums, ctrl, results, j);
+}
+
+// ------------------------------------------------------------- checksum sum ---
+// The checksum sum S of every job that was applied: one workgroup per 2048
+// blocks (the descriptor-scan tiles) sums its blocks' per-wave partials and
+// adds them to the job's total with one atomic (exact mod 2^64 in any order).
+// The last workgroup to finish then finalizes every job.
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(
+    const DecompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
+    DecompressState *__restrict__ state, const uint64_t *__restrict__ partial,
+    JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
+    bf16d_result *__restrict__ results) {
+    __shared__ unsigned long long s_tmp[kWaves];
+    const uint64_t dt = blockIdx.x;
+    const uint32_t j = dtile_job[dt];
+    uint64_t dep = 0;
+    if (state[j].state == kStateReady) {   // uniform; otherwise nothing was applied
+        const DecompressJob &job = jobs[j];
+        const uint64_t ld = dt - job.dtile0;
+        unsigned long long S = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kDescPerThread; ++k) {
+            const uint64_t b = ld * kDescTile + kDescPerThread * threadIdx.x + k;
+            if (b < job.nb)
+#pragma unroll
+                for (uint32_t w = 0; w < kWaves; ++w)
+                    S += partial[kWaves * (job.block0 + b) + w];
+        }
+        S = block_sum(S, s_tmp);
+        if (threadIdx.x == 0) dep = atomicAdd(&sums[j].csum, S);
+    }
+    if (last_workgroup(&ctrl->sum_done, dep))
+        for (uint32_t jj = threadIdx.x; jj < count; jj += kThreads)
+            finalize_job(jobs, state, sums, ctrl, results, jj);
 }
 
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
@@ -974,18 +1012,25 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     auto *state = reinterpret_cast<DecompressState *>(ws + l.state);
     auto *plan = reinterpret_cast<ApplyPlan *>(ws + l.plan);
 
-    launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
-    launch_zero_words(reinterpret_cast<uint32_t *>(state),
-                      sizeof(DecompressState) / 4 * (uint64_t)count, stream);
-    launch_zero_words(reinterpret_cast<uint32_t *>(sums), sizeof(JobSums) / 4 * (uint64_t)count,
-                      stream);
-    if (dtiles) {
-        launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
+    SetupArgs sa{};
+    sa.zero[0] = reinterpret_cast<uint32_t *>(ctrl);
+    sa.zero_words[0] = sizeof(Control) / 4;
+    sa.zero[1] = reinterpret_cast<uint32_t *>(state);
+    sa.zero_words[1] = sizeof(DecompressState) / 4 * (uint64_t)count;
+    sa.zero[2] = reinterpret_cast<uint32_t *>(sums);
+    sa.zero_words[2] = sizeof(JobSums) / 4 * (uint64_t)count;
+    sa.start[0] = dstart;
+    sa.map[0] = dmap;
+    sa.status[0] = dstatus;
+    sa.tiles[0] = dtiles;
+    sa.count = count;
+    launch_setup(sa, stream);
+    if (dtiles)   // its last workgroup also prepares the jobs
         desc_scan_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(jobs, dmap, dstatus, offsets,
-                                                                    state, ctrl);
-    }
-    prepare_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(jobs, state,
-                                                                               count);
+                                                                    state, ctrl, count);
+    else
+        prepare_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(jobs, state,
+                                                                                   count);
     if (tiles) {
         const uint64_t g = (tiles + kThreads - 1) / kThreads;
         plan_kernel<<<(uint32_t)(g < 4096 ? g : 4096), kThreads, 0, stream>>>(
@@ -995,16 +1040,14 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
         apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(plan, state, partial);
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
-        sum_partials_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(jobs, dmap, state,
-                                                                       partial, sums);
-    }
-    decompress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
-        jobs, state, sums, ctrl, count, results);
-    if (tiles) {
-        commit_kernel<<<persistent_grid((const void *)commit_kernel, tiles), kThreads, 0,
-                        stream>>>(plan, state, ctrl, tiles);
-        rollback_kernel<<<persistent_grid((const void *)rollback_kernel, tiles), kThreads, 0,
-                          stream>>>(plan, state, ctrl, tiles);
+        // its last workgroup also finalizes the jobs
+        sum_partials_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
+            jobs, dmap, state, partial, sums, ctrl, count, results);
+        fixup_kernel<<<persistent_grid((const void *)fixup_kernel, tiles), kThreads, 0, stream>>>(
+            plan, state, ctrl, tiles);
+    } else {
+        decompress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+            jobs, state, sums, ctrl, count, results);
     }
     return hipGetLastError();
 }

@@ -149,7 +149,20 @@ struct alignas(64) Control {
     uint32_t any_rollback;    // decompress: some job must be rolled back
     uint32_t overflow_count;  // compress: tiles whose record exceeded a slot
     uint32_t any_commit;      // decompress: some overwrite payload is to be written
-    uint32_t pad[11];
+    uint32_t scan_done;       // workgroups of the descriptor/offset scan that have finished
+    uint32_t sum_done;        // decompress: workgroups of the checksum sum that have finished
+    uint32_t pad[9];
+};
+
+// Set-up of a batched call in one launch: zero fills and tile -> job maps.
+struct SetupArgs {
+    uint32_t *zero[3];            // ranges to clear (may be null)
+    uint64_t zero_words[3];
+    const uint64_t *start[2];     // job start tables of the maps
+    uint32_t *map[2];             // map[m][t] = j with start[m][j] <= t < start[m][j + 1]
+    uint64_t *status[2];          // cleared alongside map[m] (may be null)
+    uint64_t tiles[2];
+    uint32_t count;
 };
 
 // Workspace layout, computed identically by every entry point.
@@ -204,6 +217,30 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
 
 __device__ __forceinline__ uint64_t ld_acquire_agent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Counts the workgroups of a grid as they finish; true in the last one.
+// Workgroups hand results to it only through device-scope atomics, which the
+// last workgroup reads with device-scope loads.  `dep` is the XOR of the
+// values the calling thread's atomics returned (0 in threads that made
+// none): the count waits for them to come back, so they are done before the
+// last workgroup can look.  No fence is used: on this chip a device-scope
+// fence writes back and invalidates the XCD's whole L2, for every workgroup.
+// Every thread must call it (it contains barriers).
+__device__ __forceinline__ bool last_workgroup(uint32_t *done, uint64_t dep) {
+    __shared__ bool s_last;
+    asm volatile("" ::"v"(dep) : "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 gridDim.x - 1;
+    __syncthreads();
+    return s_last;
 }
 __device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -477,6 +514,7 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
 
 // workgroups of a persistent kernel: as many as fit on the device at once
 uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds = 0);
+void launch_setup(const SetupArgs &a, hipStream_t stream);
 void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
                       uint64_t tiles, hipStream_t stream);
 void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
