@@ -25,18 +25,19 @@
 // Placing records needs each record's byte offset: the exclusive sum of the
 // sizes of the job's earlier records.  Computing that inside the streaming
 // pass would stall it on a cross-workgroup look-back.  So the work is split:
+//   setup    : clears the call's sums and builds the tile -> job maps.
 //   encode   : one workgroup per tile, no inter-workgroup waits.  Reads old
 //              and new once.  Writes each record (if <= kSlot bytes) to a
 //              fixed per-tile slot in the workspace, plus its descriptor and
 //              checksum partials; larger records are listed for re-encoding.
 //   offsets  : a decoupled look-back scan (Merrill and Garland, "Single-pass
 //              Parallel Prefix Scan with Decoupled Look-back", 2016) over the
-//              record sizes of each job: the stream offsets.
-//   place    : one wave per tile copies its slot to the record's offset and
-//              writes the descriptor.
+//              record sizes of each job: the stream offsets.  It writes
+//              the descriptor table, and its last workgroup writes each
+//              job's header, checksum and result.
+//   place    : each wave copies four tiles' slots to their records' offsets.
 //   reencode : for tiles whose record did not fit a slot (dense blocks),
 //              encodes again straight into the payload.
-//   finalize : one thread per job; header, checksum and result.
 //
 // A version-2 payload adds a binding block to the header; an overwrite
 // payload (its flag set) has no mantissa segment and carries the new value
@@ -349,6 +350,62 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
     }
 }
 
+// ---------------------------------------------------------------- finalize ---
+// Job j's header, checksum and result.  The sums are read with device-scope
+// loads: the offsets kernel's last workgroup runs this right after the other
+// workgroups' atomics.
+__device__ void finalize_job(const CompressJob *__restrict__ jobs,
+                             const JobSums *__restrict__ sums,
+                             bf16d_result *__restrict__ results, uint32_t j) {
+    const CompressJob job = jobs[j];
+    const JobSums *js = &sums[j];
+    const unsigned long long S = ld_agent(&js->csum), c = ld_agent(&js->c), r = ld_agent(&js->r),
+                             pos = ld_agent(&js->pos), mant = ld_agent(&js->mant),
+                             nbm = ld_agent(&js->nbm);
+    const uint64_t rare = 2 * r;
+    const uint64_t P = job.hdr + 4 * job.nb + pos + mant + rare;
+    const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
+    if (status == BF16D_OK) {
+        BF16D_GMEM uint32_t *h = reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload);
+        BF16D_GMEM uint64_t *h64 = reinterpret_cast<BF16D_GMEM uint64_t *>(job.payload);
+        h[0] = kMagicLo;
+        h[1] = kMagicHi;
+        h[2] = job.hdr == kHeaderBound ? BF16D_FORMAT_VERSION_BOUND : BF16D_FORMAT_VERSION;
+        h[3] = kBlock;
+        h64[2] = job.n;
+        h64[3] = c;
+        h64[4] = r;
+        h64[5] = pos;
+        h64[6] = mant;
+        h64[7] = rare;
+        if (job.hdr == kHeaderBound) {   // the binding block
+            h64[8] = job.base_version;
+            h64[9] = job.target_version;
+            h[20] = job.flags;
+            h[21] = 0;
+            h64[11] = 0;
+        }
+    }
+    bf16d_result res;
+    res.status = status;
+    res.reserved = 0;
+    res.payload_bytes = P;
+    res.checksum = mix64(S ^ job.n);
+    res.n_changed = c;
+    res.n_rare = r;
+    res.n_bitmap_blocks = nbm;
+    results[j] = res;
+}
+
+// For calls without tiles (every tensor empty); otherwise the offsets
+// kernel's last workgroup finalizes the jobs.
+__global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
+    const CompressJob *__restrict__ jobs, const JobSums *__restrict__ sums, uint32_t count,
+    bf16d_result *__restrict__ results) {
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < count) finalize_job(jobs, sums, results, j);
+}
+
 // ----------------------------------------------------------------- offsets ---
 // Record offsets within each job: exclusive sum of record sizes over the
 // job's tiles, by tiles of kDescTile descriptors with a decoupled look-back.
@@ -357,7 +414,8 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     const uint64_t *__restrict__ dstart, const uint32_t *__restrict__ desc,
     uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets,
     PlaceEntry *__restrict__ place, const uint64_t *__restrict__ partial,
-    JobSums *__restrict__ sums, Control *__restrict__ ctrl) {
+    JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
+    bf16d_result *__restrict__ results) {
     __shared__ uint32_t s_tmp[kWaves];
     __shared__ unsigned long long s_tmp64[kWaves];
     __shared__ uint32_t s_dt;
@@ -438,14 +496,14 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     mant_sum = block_sum(mant_sum, s_tmp64);
     nbm = block_sum(nbm, s_tmp64);
     S = block_sum(S, s_tmp64);
-    if (tid == 0) {
-        atomicAdd(&sums[j].csum, S);   // exact mod 2^64, in any order
-        atomicAdd(&sums[j].c, c_sum);
-        atomicAdd(&sums[j].r, r_sum);
-        atomicAdd(&sums[j].pos, pos_sum);
-        atomicAdd(&sums[j].mant, mant_sum);
-        atomicAdd(&sums[j].nbm, nbm);
-    }
+    uint64_t dep = 0;
+    if (tid == 0)   // exact mod 2^64, in any order
+        dep = atomicAdd(&sums[j].csum, S) ^ atomicAdd(&sums[j].c, c_sum) ^
+              atomicAdd(&sums[j].r, r_sum) ^ atomicAdd(&sums[j].pos, pos_sum) ^
+              atomicAdd(&sums[j].mant, mant_sum) ^ atomicAdd(&sums[j].nbm, nbm);
+    // the last workgroup to finish writes every job's header and result
+    if (last_workgroup(&ctrl->scan_done, dep))
+        for (uint32_t jj = tid; jj < count; jj += kThreads) finalize_job(jobs, sums, results, jj);
 }
 
 // ------------------------------------------------------------------- place ---
@@ -592,52 +650,6 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(
     }
 }
 
-// ---------------------------------------------------------------- finalize ---
-// One thread per job: header, checksum and result.
-__global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
-    const CompressJob *__restrict__ jobs, const JobSums *__restrict__ sums, uint32_t count,
-    bf16d_result *__restrict__ results) {
-    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= count) return;
-    const CompressJob job = jobs[j];
-    const JobSums js = sums[j];
-    const unsigned long long S = js.csum, c = js.c, r = js.r, pos = js.pos, mant = js.mant,
-                             nbm = js.nbm;
-    const uint64_t rare = 2 * r;
-    const uint64_t P = job.hdr + 4 * job.nb + pos + mant + rare;
-    const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
-    if (status == BF16D_OK) {
-        BF16D_GMEM uint32_t *h = reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload);
-        BF16D_GMEM uint64_t *h64 = reinterpret_cast<BF16D_GMEM uint64_t *>(job.payload);
-        h[0] = kMagicLo;
-        h[1] = kMagicHi;
-        h[2] = job.hdr == kHeaderBound ? BF16D_FORMAT_VERSION_BOUND : BF16D_FORMAT_VERSION;
-        h[3] = kBlock;
-        h64[2] = job.n;
-        h64[3] = c;
-        h64[4] = r;
-        h64[5] = pos;
-        h64[6] = mant;
-        h64[7] = rare;
-        if (job.hdr == kHeaderBound) {   // the binding block
-            h64[8] = job.base_version;
-            h64[9] = job.target_version;
-            h[20] = job.flags;
-            h[21] = 0;
-            h64[11] = 0;
-        }
-    }
-    bf16d_result res;
-    res.status = status;
-    res.reserved = 0;
-    res.payload_bytes = P;
-    res.checksum = mix64(S ^ job.n);
-    res.n_changed = c;
-    res.n_rare = r;
-    res.n_bitmap_blocks = nbm;
-    results[j] = res;
-}
-
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                            uint64_t dtiles, bf16d_result *results, hipStream_t stream,
                            const bf16d_events *events, bool any_overwrite) {
@@ -656,20 +668,31 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     auto *overflow = reinterpret_cast<uint32_t *>(ws + l.overflow);
     auto *place = reinterpret_cast<PlaceEntry *>(ws + l.plan);
 
-    launch_zero_words(reinterpret_cast<uint32_t *>(ctrl), sizeof(Control) / 4, stream);
-    launch_zero_words(reinterpret_cast<uint32_t *>(sums), sizeof(JobSums) / 4 * (uint64_t)count,
-                      stream);
+    SetupArgs sa{};
+    sa.zero[0] = reinterpret_cast<uint32_t *>(ctrl);
+    sa.zero_words[0] = sizeof(Control) / 4;
+    sa.zero[1] = reinterpret_cast<uint32_t *>(sums);
+    sa.zero_words[1] = sizeof(JobSums) / 4 * (uint64_t)count;
+    sa.start[0] = bstart;
+    sa.map[0] = map;
+    sa.tiles[0] = tiles;
+    sa.start[1] = dstart;
+    sa.map[1] = dmap;
+    sa.status[1] = dstatus;
+    sa.tiles[1] = dtiles;
+    sa.count = count;
+    launch_setup(sa, stream);
     if (tiles) {
-        launch_map_tiles(bstart, count, map, nullptr, tiles, stream);
-        launch_map_tiles(dstart, count, dmap, dstatus, dtiles, stream);
         if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
             return hipErrorInvalidValue;
         encode_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, slots, desc, partial,
                                                                 overflow, ctrl);
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
+        // its last workgroup also writes the headers and results
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
-            jobs, dmap, dstart, desc, dstatus, offsets, place, partial, sums, ctrl);
+            jobs, dmap, dstart, desc, dstatus, offsets, place, partial, sums, ctrl, count,
+            results);
         const uint64_t per_block = (uint64_t)kWaves * kPlaceTiles;
         place_kernel<<<(uint32_t)((tiles + per_block - 1) / per_block), kThreads, 0, stream>>>(
             place, slots, tiles);
@@ -678,9 +701,10 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
         if (any_overwrite)
             reencode_kernel<true><<<persistent_grid((const void *)reencode_kernel<true>, tiles),
                                     kThreads, 0, stream>>>(jobs, map, overflow, offsets, ctrl);
+    } else {
+        compress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+            jobs, sums, count, results);
     }
-    compress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
-        jobs, sums, count, results);
     return hipGetLastError();
 }
 

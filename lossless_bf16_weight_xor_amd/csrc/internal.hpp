@@ -515,9 +515,6 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
 // workgroups of a persistent kernel: as many as fit on the device at once
 uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds = 0);
 void launch_setup(const SetupArgs &a, hipStream_t stream);
-void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
-                      uint64_t tiles, hipStream_t stream);
-void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream);
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                            uint64_t dtiles, bf16d_result *results, hipStream_t stream,
                            const bf16d_events *events, bool any_overwrite);

@@ -7,29 +7,9 @@
 
 namespace bf16d {
 
-// map[t] = j with start[j] <= t < start[j+1]; optionally clears status[t]
-__global__ void map_tiles_kernel(const uint64_t *__restrict__ start, uint32_t count,
-                                 uint32_t *__restrict__ map, uint64_t *__restrict__ status,
-                                 uint64_t tiles) {
-    for (uint64_t t = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; t < tiles;
-         t += (uint64_t)gridDim.x * blockDim.x) {
-        uint32_t lo = 0, hi = count;   // invariant: start[lo] <= t < start[hi]
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (start[mid] <= t) lo = mid; else hi = mid;
-        }
-        map[t] = lo;
-        if (status) status[t] = 0;
-    }
-}
-
-__global__ void zero_words_kernel(uint32_t *__restrict__ p, uint64_t words) {
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
-         i += (uint64_t)gridDim.x * blockDim.x)
-        p[i] = 0;
-}
-
-// The zero fills and tile maps of one call, in one launch.
+// The zero fills and tile maps of one call, in one launch: map[m][t] = j
+// with start[m][j] <= t < start[m][j + 1] (a binary search of the job start
+// table), and status[m][t] cleared alongside when given.
 __global__ void setup_kernel(SetupArgs a) {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     const uint64_t i0 = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
@@ -74,15 +54,6 @@ void launch_setup(const SetupArgs &a, hipStream_t stream) {
     for (int z = 0; z < 3; ++z) items = a.zero_words[z] > items ? a.zero_words[z] : items;
     for (int m = 0; m < 2; ++m) items = a.tiles[m] > items ? a.tiles[m] : items;
     setup_kernel<<<grid_for(items), kThreads, 0, stream>>>(a);
-}
-
-void launch_map_tiles(const uint64_t *start, uint32_t count, uint32_t *map, uint64_t *status,
-                      uint64_t tiles, hipStream_t stream) {
-    map_tiles_kernel<<<grid_for(tiles), kThreads, 0, stream>>>(start, count, map, status, tiles);
-}
-
-void launch_zero_words(uint32_t *p, uint64_t words, hipStream_t stream) {
-    zero_words_kernel<<<grid_for(words), kThreads, 0, stream>>>(p, words);
 }
 
 }  // namespace bf16d
