@@ -21,6 +21,9 @@ Reported:
   decompress: GB/s of weights, and % of HBM peak on algorithmic bytes (2n + P + 2c)
   roofline  : the encode kernel (the dominant kernel of a step) against 8 TB/s,
               timed with events recorded around it on its stream
+  achievable: the read ceiling of the encoder's access pattern (a probe
+              kernel that only reads), over old and new and over old alone,
+              and each main kernel's fraction of it
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
   bound_overwrite : the same pair as version-2 overwrite payloads (absolute
@@ -317,6 +320,33 @@ def bound_overwrite(bd, pairs, steps):
             "decompress_gbps_weights": round(2 * n / td / 1e9, 2)}
 
 
+def read_ceiling(bd, n, dev, steps):
+    """The read ceiling of the encoder's access pattern (bf16d_probe_read: one
+    workgroup per 8192-element block, 16-byte loads, nothing else) over two
+    flat n-element arrays, as the encoder reads old and new, and over one, as
+    the apply pass reads old.  Their contents do not matter."""
+    a = torch.empty(n, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.empty(1, dtype=torch.int64, device=dev)
+    full = n // 8192 * 8192
+    out = {}
+    for key, arrays in (("read2", (a, b)), ("read1", (a, None))):
+        bd.probe_read(*arrays, sink=sink)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            bd.probe_read(*arrays, sink=sink)
+        ev[1].record()
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) / 1e3 / steps
+        nbytes = (2 if arrays[1] is not None else 1) * 2 * full
+        out[key] = {"bytes": nbytes, "ms": round(1e3 * t, 4), "gbps": round(nbytes / t / 1e9, 2),
+                    "pct_of_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBPS, 2)}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(pairs, gpu_payloads, budget_s: float):
     """The CPU oracle, single-threaded, timed on a bounded sample of the
     workload's tensors, walking from the last tensor back.  Each oracle
@@ -379,6 +409,8 @@ def main():
                     help="skip the host codec race over the payloads")
     ap.add_argument("--race-threads", type=int, default=16,
                     help="CPU threads of the codec race (capped at the host's cores)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the read-ceiling probe (bf16d_probe_read)")
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -511,6 +543,18 @@ def main():
         log(f"codec race: {race_info['raced_bytes']} B "
             f"({race_info['payload_pct_after_race']}% of orig) in {race_info['race_s']} s")
 
+    # last of the GPU measurements: it frees two checkpoint-sized buffers, and
+    # a large free slows the streamed receiver's copies for some seconds
+    ceiling = None
+    if not args.no_probe:
+        ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2))
+        ceiling["encode_kernel_frac_of_read2"] = round(comp_alg / t_enc / 1e9 /
+                                                       ceiling["read2"]["gbps"], 4)
+        ceiling["apply_kernel_frac_of_read1"] = round(dec_alg / t_app / 1e9 /
+                                                      ceiling["read1"]["gbps"], 4)
+        log(f"read ceiling: {ceiling['read2']['gbps']} GB/s over two arrays, "
+            f"{ceiling['read1']['gbps']} GB/s over one")
+
     gpu_payloads = [None] * len(pairs)
     cpu = None
     if args.cpu_budget > 0:
@@ -552,6 +596,7 @@ def main():
                                 "achieved": round(dec_alg / t_app / 1e9, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
+        "achievable": ceiling,
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,
         "bound_overwrite": bound_info,

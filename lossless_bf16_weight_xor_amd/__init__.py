@@ -34,7 +34,7 @@ __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_b
            "CompressBatch", "DecompressBatch", "StreamedDecompress", "RemappedBatch",
            "decompress_remapped", "race_compress", "race_decompress", "codec_available",
            "RaceFrame", "DEFAULT_RACE", "FormatError", "ChecksumError",
-           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
+           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT", "probe_read"]
 
 
 class FormatError(ValueError):
@@ -374,6 +374,27 @@ def decompress_remapped(items) -> list[dict]:
     batch = RemappedBatch(items)
     batch.run()
     return batch.results()
+
+
+_PROBE_KEY = 0x9E3779B97F4A7C15   # the probe stores only if its fold equals this
+
+
+def probe_read(a: torch.Tensor, b: torch.Tensor | None = None,
+               sink: torch.Tensor | None = None) -> None:
+    """Measurement aid: read a (and b) with the encoder's access pattern and
+    nothing else, enqueued on the current stream (`bf16d_probe_read`)."""
+    pa = _weights_ptr(a, "a")
+    pb = 0
+    if b is not None:
+        pb = _weights_ptr(b, "b")
+        if b.device != a.device or b.numel() < a.numel():
+            raise ValueError("b must be on a's device and hold at least as many elements")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int64, device=a.device)
+    if sink.device != a.device or sink.dtype != torch.int64 or sink.numel() < 1:
+        raise ValueError("sink must be an int64 tensor on a's device")
+    _check_rc(_native.lib().bf16d_probe_read(pa, pb, a.numel(), sink.data_ptr(), _PROBE_KEY,
+                                             _stream(a.device)), "bf16d_probe_read")
 
 
 def _first_capacity(n: int) -> int:

@@ -1,0 +1,60 @@
+// probe.hip -- a measurement aid, not a step of the method.
+//
+// The encoder's whole-block access pattern with nothing else: one workgroup
+// of 256 threads per 8192-element block, four 16-byte loads per thread from
+// each array, all in flight together.  Its time is the read ceiling of that
+// pattern on the device, against which the encoder (both checkpoints) and
+// the apply pass (one) are compared; the published HBM peak stays the
+// roofline.
+#include "internal.hpp"
+
+namespace bf16d {
+
+// Plain pointers in the signature (an address-space qualifier there would
+// give the kernel a different name in the host and device passes); they are
+// made global inside.
+template <bool kTwo>
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint16_t *__restrict__ pa,
+                                                              const uint16_t *__restrict__ pb,
+                                                              uint64_t *__restrict__ sink,
+                                                              uint64_t key) {
+    auto *a = (BF16D_GMEM const uint16_t *)pa;
+    auto *b = (BF16D_GMEM const uint16_t *)pb;
+    const uint64_t base = (uint64_t)blockIdx.x * kBlock;
+    uint4 x[kChunksPerThread], y[kChunksPerThread];
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint64_t e0 = base + 8 * (threadIdx.x + kThreads * i);
+        x[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(a + e0);
+        y[i] = make_uint4(0, 0, 0, 0);
+        if constexpr (kTwo) y[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(b + e0);
+    }
+    uint64_t acc = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i)
+        acc += ((uint64_t)(x[i].x ^ y[i].x) << 32 | (x[i].y ^ y[i].y)) +
+               ((uint64_t)(x[i].z ^ y[i].z) << 32 | (x[i].w ^ y[i].w));
+    // keeps the loads: the store happens only if the fold hits the caller's key
+    if (acc == key) sink[0] = acc;
+}
+
+int probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink, uint64_t key,
+               hipStream_t stream) {
+    const uint64_t blocks = n / kBlock;
+    if (!a || !sink || ((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sink & 7) ||
+        blocks > 0x7FFFFFFFull)
+        return BF16D_EINVAL;
+    if (blocks == 0) return BF16D_OK;
+    if (b)
+        probe_read_kernel<true><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, b, sink, key);
+    else
+        probe_read_kernel<false><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, b, sink, key);
+    return hipGetLastError() == hipSuccess ? BF16D_OK : BF16D_EHIP;
+}
+
+}  // namespace bf16d
+
+extern "C" int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink,
+                                uint64_t key, hipStream_t stream) {
+    return bf16d::probe_read(a, b, n, sink, key, stream);
+}

@@ -44,6 +44,23 @@ def test_every_declared_symbol_is_exported(native):
     assert set(native.EXPORTED) == set(_declared_functions())
 
 
+def test_no_kernel_takes_an_address_space_qualified_parameter():
+    """A kernel's name must be the same in the host and device passes.  The
+    global-memory qualifier is empty in the host pass, so a kernel parameter
+    carrying it would give the device kernel a name the host never registers
+    (the launch then fails with a missing-symbol abort)."""
+    csrc = os.path.join(ROOT, "lossless_bf16_weight_xor_amd", "csrc")
+    kernels = 0
+    for f in sorted(os.listdir(csrc)):
+        if not f.endswith(".hip"):
+            continue
+        text = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, f)).read())
+        for m in re.finditer(r"__global__[^;{]*?\b(\w+)\s*\(([^)]*)\)\s*\{", text):
+            kernels += 1
+            assert "BF16D_GMEM" not in m.group(2), f"{f}: kernel {m.group(1)}"
+    assert kernels >= 10
+
+
 def test_struct_sizes_match_the_header(native):
     assert ctypes.sizeof(native.Result) == 48
     assert ctypes.sizeof(native.CompressJob) == 40
