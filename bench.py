@@ -40,6 +40,7 @@ Only one GPU is used; --gpus above 1 is refused.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -90,7 +91,6 @@ def generate(workload: str, device, limit=None):
 
 
 def kernel_source_hash() -> str:
-    import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -357,36 +357,53 @@ def cpu_baseline(pairs, gpu_payloads, budget_s: float):
     n_done = 0
     names = []
     mismatches = 0
-    for j in range(len(pairs) - 1, -1, -1):
-        src, dst = pairs[j]
-        a = synth.bits(src).cpu().numpy().astype(np.uint16)
-        b = synth.bits(dst).cpu().numpy().astype(np.uint16)
-        t0 = time.perf_counter()
-        payload, cs, _ = oracle.compress(a, b)
-        t1 = time.perf_counter()
-        w = a.copy()
-        st = oracle.decompress_inplace(w, payload, cs)
-        t2 = time.perf_counter()
-        assert st == oracle.OK and np.array_equal(w, b)
-        got = gpu_payloads[j]
-        if got is not None and not (got.size == payload.size and np.array_equal(got, payload)):
-            mismatches += 1
-        t_c += t1 - t0
-        t_d += t2 - t1
-        n_done += a.size
-        names.append(j)
-        if t_c + t_d > budget_s:
-            break
+    # one core, as the oracle's single thread would use anyway; restored after
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    os.sched_setaffinity(0, {core})
+    try:
+        for j in range(len(pairs) - 1, -1, -1):
+            src, dst = pairs[j]
+            a = synth.bits(src).cpu().numpy().astype(np.uint16)
+            b = synth.bits(dst).cpu().numpy().astype(np.uint16)
+            t0 = time.perf_counter()
+            payload, cs, _ = oracle.compress(a, b)
+            t1 = time.perf_counter()
+            w = a.copy()
+            st = oracle.decompress_inplace(w, payload, cs)
+            t2 = time.perf_counter()
+            assert st == oracle.OK and np.array_equal(w, b)
+            got = gpu_payloads[j]
+            if got is not None and not (got.size == payload.size and np.array_equal(got, payload)):
+                mismatches += 1
+            t_c += t1 - t0
+            t_d += t2 - t1
+            n_done += a.size
+            names.append(j)
+            if t_c + t_d > budget_s:
+                break
+    finally:
+        os.sched_setaffinity(0, saved)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": round(2 * n_done / (t_c + t_d) / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"{len(names)} of {len(pairs)} tensors ({2 * n_done / 1e9:.3f} GB of BF16 "
-                  f"weights), compress + decompress, single-threaded C oracle",
+                  f"weights), compress + decompress, single-threaded C oracle pinned to one core",
         "compress_gbps": round(2 * n_done / t_c / 1e9, 4),
         "decompress_gbps": round(2 * n_done / t_d / 1e9, 4),
         "payload_mismatches_vs_gpu": mismatches,
+        "cpu_model": cpu_model,
+        "cores_available": len(saved),
     }
 
 
@@ -501,8 +518,11 @@ def main():
         ref = d if expect_new else s
         assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "receiver not bit-exact"
 
+    def durations(a, b):
+        return [evs[i][a].elapsed_time(evs[i][b]) / 1e3 for i in range(args.steps)]
+
     def avg(a, b):
-        return float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)])) / 1e3
+        return float(np.mean(durations(a, b)))
 
     tc, td = avg(0, 3), avg(3, 6)            # whole calls
     t_enc, t_app = avg(1, 2), avg(4, 5)      # their main kernels
@@ -579,11 +599,17 @@ def main():
                    "weights_bytes": w_bytes, "parallelism": "single GPU"},
         "compress": {"gbps_weights": round(w_bytes / tc / 1e9, 2),
                      "hbm_pct": round(100 * comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 2),
-                     "ms": round(1e3 * tc, 4), "encode_kernel_ms": round(1e3 * t_enc, 4),
+                     "ms": round(1e3 * tc, 4),
+                     "ms_median": round(1e3 * float(np.median(durations(0, 3))), 4),
+                     "ms_min": round(1e3 * min(durations(0, 3)), 4),
+                     "encode_kernel_ms": round(1e3 * t_enc, 4),
                      "algorithmic_bytes": comp_alg},
         "decompress": {"gbps_weights": round(w_bytes / td / 1e9, 2),
                        "hbm_pct": round(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS, 2),
-                       "ms": round(1e3 * td, 4), "apply_kernel_ms": round(1e3 * t_app, 4),
+                       "ms": round(1e3 * td, 4),
+                       "ms_median": round(1e3 * float(np.median(durations(3, 6))), 4),
+                       "ms_min": round(1e3 * min(durations(3, 6)), 4),
+                       "apply_kernel_ms": round(1e3 * t_app, 4),
                        "algorithmic_bytes": dec_alg},
         "payload_pct_of_orig": round(100 * payload_total / w_bytes, 4),
         "payload_bytes": payload_total,
@@ -602,6 +628,10 @@ def main():
         "bound_overwrite": bound_info,
         "codec_race": race_info,
         "cpu_baseline": cpu,
+        "env": {"torch": torch.__version__, "hip": torch.version.hip,
+                "device": torch.cuda.get_device_name(dev),
+                "checksums_sha256": hashlib.sha256(
+                    np.array(cs_new, dtype=np.uint64).tobytes()).hexdigest()},
     }
     print(json.dumps(out), flush=True)
 
