@@ -98,9 +98,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(elements: int):
     """HBM bytes per encode launch from the committed counter summary, or None
-    if there is none or the kernel sources changed since it was taken."""
+    if there is none, it was taken on another workload (element count), or the
+    kernel sources changed since it was taken."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     fields = {}
@@ -110,6 +111,8 @@ def measured_traffic():
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
     if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    if fields.get("elements_per_call") != str(elements):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -617,7 +620,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "encode_kernel",
                      "achieved": round(comp_alg / t_enc / 1e9, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(comp_alg / t_enc / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(n_total)},
         "roofline_decompress": {"bound": "hbm", "kernel": "apply_kernel",
                                 "achieved": round(dec_alg / t_app / 1e9, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
