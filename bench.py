@@ -31,8 +31,10 @@ Reported:
   codec_race : the host race of general-purpose codecs over every payload,
               and the payload % of the weights after it
   streamed_receiver : the same decompress with the payloads in pinned host
-              memory, copied in layer by layer while the previous layer is
-              applied (PCIe-inclusive; context, not `value`)
+              memory, copied in layer by layer while earlier layers are
+              applied, through a ring of three device slots with the copies
+              on two streams (and two slots on one stream, for comparison);
+              PCIe-inclusive, context, not `value`
   cpu_baseline : the CPU oracle on a bounded sample of the same workload
 
 Only one GPU is used; --gpus above 1 is refused.
@@ -134,15 +136,18 @@ def layer_groups(names, layers_per_group=1):
     return [sum(units[i:i + layers_per_group]) for i in range(0, len(units), layers_per_group)]
 
 
-def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_group):
+def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_group, slots,
+             copies):
     """The streamed receiver: payloads in pinned host memory, applied layer by
-    layer through two device slots while the next layer's payloads are copied
-    in.  Reported next to the device-resident numbers, never as `value`."""
+    layer through a ring of `slots` device slots while the next layers'
+    payloads are copied in.  Reported next to the device-resident numbers,
+    never as `value`."""
     dev = pairs[0][0].device
     host = bd.StreamedDecompress.pin_packed([p.cpu() for p in payloads])
     groups = layer_groups(names, layers_per_group)
     recv = [s.clone() for s, _ in pairs]
-    sd = bd.StreamedDecompress(list(zip(recv, host, cs_new)), groups)
+    sd = bd.StreamedDecompress(list(zip(recv, host, cs_new)), groups, slots=slots,
+                               copy_streams=copies)
     # the host-to-device copy of every payload byte on its own
     P = sum(h.numel() for h in host)
     flat = torch.empty(P, dtype=torch.uint8).pin_memory()
@@ -178,7 +183,9 @@ def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_g
     ts, th = float(np.median(t_str)), float(np.median(t_h2d))
     slot = sd.slot_bytes
     del recv, sd, dbuf
-    return {"layers_per_group": layers_per_group, "groups": len(groups), "slot_bytes": slot,
+    return {"layers_per_group": layers_per_group, "groups": len(groups), "slots": slots,
+            "copy_streams": copies,
+            "slot_bytes": slot,
             "ms": round(1e3 * ts, 4),
             "gbps_weights_pcie_inclusive": round(2 * n / ts / 1e9, 2),
             "h2d_payload_ms": round(1e3 * th, 4), "h2d_gbps": round(P / th / 1e9, 2),
@@ -545,8 +552,9 @@ def main():
 
     stream_info = None
     if not args.no_streamed:
-        stream_info = [streamed(bd, names, pairs, payloads, cs_new, cs_old, 5, td, lpg)
-                       for lpg in (1, 4)]
+        stream_info = [streamed(bd, names, pairs, payloads, cs_new, cs_old, 5, td, lpg, slots,
+                                copies)
+                       for lpg, slots, copies in ((1, 3, 2), (4, 3, 2), (1, 2, 1))]
 
     remap_info = None
     if not args.no_remapped:

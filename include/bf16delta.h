@@ -331,8 +331,11 @@ int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_rema
  * device slots, one group of tensors (a layer) at a time, so that the copy
  * of one group overlaps the in-place apply of the previous one and only two
  * groups' payloads are ever on the device.  Here the copies are host-to-
- * device DMA transfers on `copy`, and the applies are bf16d_decompress
- * calls on `compute`.
+ * device DMA transfers on `copy`, the applies are bf16d_decompress calls on
+ * `compute`, and the slots form a ring of `slots` (two or more): with two,
+ * every copy waits for the apply just before it, so each cross-stream wait
+ * lands on the copies' critical path; three give the copies one group of
+ * slack.
  *
  * One tensor of such a call:
  *   weights       : device, 16-byte aligned, n elements (as in
@@ -354,19 +357,27 @@ typedef struct bf16d_stream_job {
 /* Apply `count` host-resident payloads in place, streamed in `groups`
  * groups.  Group g holds jobs [group_end[g-1], group_end[g]) (group_end[-1]
  * is 0); group_end must increase strictly and end at count.
- *   staging      : device, 16-byte aligned, 2 * slot_bytes bytes: slot 0 at
- *                  staging, slot 1 at staging + slot_bytes.  slot_bytes must be
- *                  a multiple of 16.  Group g's payloads are packed into slot
- *                  g % 2, each at a 16-byte boundary; every group must fit.
+ *   staging      : device, 16-byte aligned, slots * slot_bytes bytes: slot k
+ *                  at staging + k * slot_bytes.  slot_bytes must be a
+ *                  multiple of 16, and 2 <= slots <= 64.  Group g's payloads
+ *                  are packed into slot g % slots, each at a 16-byte
+ *                  boundary; every group must fit.  The copy of group g
+ *                  waits for the apply of group g - slots.
  *   workspace    : device, 16-byte aligned, at least
  *                  bf16d_workspace_bytes(sum of n, count) bytes; one
  *                  workspace serves every group, in stream order.
  *   results      : results[j] for job j, as in bf16d_decompress.
- *   compute      : stream of the applies; the call's work on `copy` starts
- *                  only after the work enqueued on `compute` before the call,
- *                  and results are valid once `compute` has completed.
- *   copy         : stream of the copies (may equal `compute`, which makes the
- *                  pipeline serial).  Both streams must be of the same device.
+ *   compute      : stream of the applies; the call's work on the copy streams
+ *                  starts only after the work enqueued on `compute` before
+ *                  the call, and results are valid once `compute` has
+ *                  completed.
+ *   copy         : copy_streams streams (1 to 8, host array) for the copies;
+ *                  group g's copy goes on copy[g % copy_streams].  Each
+ *                  host-to-device transfer has a fixed cost of its own
+ *                  (about 10 us, more with the event that follows it), which
+ *                  two streams hide behind each other's transfers.  A copy
+ *                  stream may equal `compute` (that makes the pipeline
+ *                  serial).  All streams must be of the same device.
  * Consecutive payloads of a group that lie in host memory exactly as they are
  * packed in the slot (each at the next 16-byte boundary after the previous
  * one) are copied with a single transfer, padding included.
@@ -375,10 +386,10 @@ typedef struct bf16d_stream_job {
  * those of bf16d_decompress; a failed job does not affect the others. */
 int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
                               const uint32_t *group_end, uint32_t groups,
-                              void *staging, size_t slot_bytes,
+                              void *staging, size_t slot_bytes, uint32_t slots,
                               void *workspace, size_t workspace_bytes,
-                              bf16d_result *results,
-                              hipStream_t compute, hipStream_t copy);
+                              bf16d_result *results, hipStream_t compute,
+                              const hipStream_t *copy, uint32_t copy_streams);
 
 /* Codec race (host only): general-purpose compression of payloads.
  *

@@ -246,18 +246,27 @@ class DecompressBatch:
 
 class StreamedDecompress:
     """A prepared streamed receiver (bf16d_decompress_streamed): payloads in
-    pinned host memory, applied in place group by group through two device
-    slots, the copies on a stream of their own.
+    pinned host memory, applied in place group by group through a ring of
+    device slots, the copies on a stream of their own.
 
     items  : (weights device tensor, payload host uint8 tensor, checksum);
              pin the payloads (torch's pin_memory) for the copies to overlap.
     groups : number of jobs in each group, in order (for a model, a layer).
+    slots  : device slots in the ring (2 to 64); with 3 the copies do not
+             wait on the apply just before them.
+    copy_streams : streams the groups' copies alternate over (1 to 8); with
+             2 each transfer's fixed cost hides behind the other's transfer.
     The device slots are sized for the largest group."""
 
     def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
-                 groups: Sequence[int]):
+                 groups: Sequence[int], slots: int = 3, copy_streams: int = 2):
         if not items or not groups or sum(groups) != len(items) or min(groups) <= 0:
             raise ValueError("groups must be positive and cover every item")
+        if not 2 <= slots <= 64:
+            raise ValueError("slots must be between 2 and 64")
+        if not 1 <= copy_streams <= 8:
+            raise ValueError("copy_streams must be between 1 and 8")
+        self.slots = slots
         self.device = items[0][0].device
         self.count = len(items)
         self.items = list(items)   # keep the tensors alive
@@ -277,12 +286,14 @@ class StreamedDecompress:
         self.groups = len(ends)
         self.group_end = (ctypes.c_uint32 * self.groups)(*ends)
         self.slot_bytes = pad16(slot)
-        self.staging = torch.empty(2 * self.slot_bytes, dtype=torch.uint8, device=self.device)
+        self.staging = torch.empty(slots * self.slot_bytes, dtype=torch.uint8,
+                                   device=self.device)
         self.ws_bytes = workspace_bytes(sum(w.numel() for w, _, _ in items), self.count)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
                                       device=self.device)
-        self.copy_stream = torch.cuda.Stream(device=self.device)
+        self.copy_streams = [torch.cuda.Stream(device=self.device) for _ in range(copy_streams)]
+        self._copy = (ctypes.c_void_p * copy_streams)(*[c.cuda_stream for c in self.copy_streams])
 
     @staticmethod
     def pin_packed(payloads: Sequence[torch.Tensor]) -> list[torch.Tensor]:
@@ -301,11 +312,11 @@ class StreamedDecompress:
         return out
 
     def run(self) -> None:
-        """Enqueue the call on the current stream (copies on self.copy_stream)."""
+        """Enqueue the call on the current stream (copies on self.copy_streams)."""
         rc = _native.lib().bf16d_decompress_streamed(
             self.jobs, self.count, self.group_end, self.groups, self.staging.data_ptr(),
-            self.slot_bytes, self.workspace.data_ptr(), self.ws_bytes,
-            self.result_buf.data_ptr(), _stream(self.device), self.copy_stream.cuda_stream)
+            self.slot_bytes, self.slots, self.workspace.data_ptr(), self.ws_bytes,
+            self.result_buf.data_ptr(), _stream(self.device), self._copy, len(self.copy_streams))
         _check_rc(rc, "bf16d_decompress_streamed")
 
     def results(self) -> list[dict]:

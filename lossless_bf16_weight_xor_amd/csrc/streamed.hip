@@ -1,14 +1,20 @@
 // streamed.hip -- the streamed receiver: host-resident payloads applied in
-// place group by group through two device slots.
+// place group by group through a ring of device slots.
 //
 // The double-buffered pipeline of "GPU-accelerated Weight Teleportation",
 // sections "Overlapping DE and SM" and "Assembling the weight teleporter",
-// on MI355X: the DMA engines copy group g's payloads into slot g % 2 on the
-// copy stream while the CUs apply group g - 1 from the other slot on the
+// on MI355X: the DMA engines copy group g's payloads into slot g % S on the
+// copy stream while the CUs apply earlier groups from the other slots on the
 // compute stream.  Events order each copy after the apply that last read its
-// slot, and each apply after its copy.  Everything is validated before any
-// work is enqueued.
+// slot, and each apply after its copy.  With S = 2 a copy waits for the apply
+// just before it, and every cross-stream wait (tens of microseconds) lands
+// on the copies' critical path; a third slot gives the copies a whole group
+// of slack.  Each transfer also has a fixed cost of its own (about 10 us,
+// 18 us with the event after it); the groups' copies alternate over the
+// caller's copy streams, so one engine's set-up overlaps another's
+// transfer.  Everything is validated before any work is enqueued.
 #include <algorithm>
+#include <cstdint>
 #include <vector>
 
 #include "internal.hpp"
@@ -24,7 +30,7 @@ struct Span {
     uintptr_t lo, hi;
 };
 
-// The device ranges written by the call (weights, both slots, workspace) may
+// The device ranges written by the call (weights, the slots, workspace) may
 // not overlap.
 bool spans_disjoint(std::vector<Span> v) {
     v.erase(std::remove_if(v.begin(), v.end(), [](const Span &s) { return s.hi <= s.lo; }),
@@ -35,19 +41,23 @@ bool spans_disjoint(std::vector<Span> v) {
     return true;
 }
 
+constexpr uint32_t kMaxSlots = 64;
+constexpr uint32_t kMaxCopyStreams = 8;
+
 struct Events {
-    hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, applied[2] = {nullptr, nullptr};
+    hipEvent_t start = nullptr;
+    std::vector<hipEvent_t> copied, applied;
     bool ok = true;
-    Events() {
+    explicit Events(uint32_t slots) : copied(slots, nullptr), applied(slots, nullptr) {
         ok = hipEventCreateWithFlags(&start, hipEventDisableTiming) == hipSuccess;
-        for (int s = 0; s < 2 && ok; ++s)
+        for (uint32_t s = 0; s < slots && ok; ++s)
             ok = hipEventCreateWithFlags(&copied[s], hipEventDisableTiming) == hipSuccess &&
                  hipEventCreateWithFlags(&applied[s], hipEventDisableTiming) == hipSuccess;
     }
     ~Events() {
         // an event still pending in a stream is released once it completes
         if (start) (void)hipEventDestroy(start);
-        for (int s = 0; s < 2; ++s) {
+        for (size_t s = 0; s < copied.size(); ++s) {
             if (copied[s]) (void)hipEventDestroy(copied[s]);
             if (applied[s]) (void)hipEventDestroy(applied[s]);
         }
@@ -58,12 +68,15 @@ struct Events {
 
 extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
                                          const uint32_t *group_end, uint32_t groups,
-                                         void *staging, size_t slot_bytes, void *workspace,
-                                         size_t workspace_bytes, bf16d_result *results,
-                                         hipStream_t compute, hipStream_t copy) {
+                                         void *staging, size_t slot_bytes, uint32_t slots,
+                                         void *workspace, size_t workspace_bytes,
+                                         bf16d_result *results, hipStream_t compute,
+                                         const hipStream_t *copy, uint32_t copy_streams) {
     if (!jobs || count == 0 || !group_end || groups == 0 || groups > count || !staging ||
-        !aligned16(staging) || slot_bytes == 0 || slot_bytes % 16 != 0 || !workspace ||
-        !aligned16(workspace) || !results)
+        !aligned16(staging) || slot_bytes == 0 || slot_bytes % 16 != 0 || slots < 2 ||
+        slots > kMaxSlots || slot_bytes > SIZE_MAX / slots || !workspace ||
+        !aligned16(workspace) || !results || !copy || copy_streams == 0 ||
+        copy_streams > kMaxCopyStreams)
         return BF16D_EINVAL;
     // groups partition [0, count) in order; each group's payloads fit a slot.
     // Each group's decompress jobs point into its slot.
@@ -75,7 +88,7 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
     for (uint32_t g = 0; g < groups; ++g) {
         const uint32_t end = group_end[g];
         if (end <= first || end > count || (g + 1 == groups && end != count)) return BF16D_EINVAL;
-        uint8_t *slot = static_cast<uint8_t *>(staging) + (g % 2) * slot_bytes;
+        uint8_t *slot = static_cast<uint8_t *>(staging) + (g % slots) * slot_bytes;
         uint64_t packed = 0;
         for (uint32_t j = first; j < end; ++j) {
             const bf16d_stream_job &J = jobs[j];
@@ -110,7 +123,7 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
     const size_t need = base + tables;
     if (workspace_bytes < need) return BF16D_EINVAL;
     spans.push_back({reinterpret_cast<uintptr_t>(staging),
-                     reinterpret_cast<uintptr_t>(staging) + 2 * slot_bytes});
+                     reinterpret_cast<uintptr_t>(staging) + slots * slot_bytes});
     spans.push_back({reinterpret_cast<uintptr_t>(workspace),
                      reinterpret_cast<uintptr_t>(workspace) + need});
     if (!spans_disjoint(spans)) return BF16D_EINVAL;
@@ -127,7 +140,7 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
         first = end;
     }
 
-    Events ev;
+    Events ev(slots);
     if (!ev.ok) return BF16D_EHIP;
     auto fail = [](hipError_t e) { return e != hipSuccess; };
     auto *ws = static_cast<uint8_t *>(workspace);
@@ -136,14 +149,17 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
     // caller's earlier work on the compute stream
     if (fail(hipMemcpyAsync(ws + base, host.data(), host.size(), hipMemcpyHostToDevice,
                             compute)) ||
-        fail(hipEventRecord(ev.start, compute)) || fail(hipStreamWaitEvent(copy, ev.start, 0)))
+        fail(hipEventRecord(ev.start, compute)))
         return BF16D_EHIP;
+    for (uint32_t c = 0; c < copy_streams; ++c)
+        if (fail(hipStreamWaitEvent(copy[c], ev.start, 0))) return BF16D_EHIP;
     first = 0;
     for (uint32_t g = 0; g < groups; ++g) {
-        const uint32_t end = group_end[g], s = g % 2;
+        const uint32_t end = group_end[g], s = g % slots;
+        hipStream_t cs = copy[g % copy_streams];
         uint8_t *slot = static_cast<uint8_t *>(staging) + s * slot_bytes;
-        // the slot is free once the apply of group g - 2 has read it
-        if (g >= 2 && fail(hipStreamWaitEvent(copy, ev.applied[s], 0))) return BF16D_EHIP;
+        // the slot is free once the apply of group g - slots has read it
+        if (g >= slots && fail(hipStreamWaitEvent(cs, ev.applied[s], 0))) return BF16D_EHIP;
         // one copy per run of payloads that lie in host memory exactly as
         // they are packed in the slot (the padding between them then comes
         // along; nothing reads it)
@@ -158,11 +174,11 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
                 ++k;
             const uint64_t bytes = offset[k - 1] - offset[j] + jobs[k - 1].payload_bytes;
             if (fail(hipMemcpyAsync(slot + offset[j], jobs[j].payload, bytes,
-                                    hipMemcpyHostToDevice, copy)))
+                                    hipMemcpyHostToDevice, cs)))
                 return BF16D_EHIP;
             j = k;
         }
-        if (fail(hipEventRecord(ev.copied[s], copy)) ||
+        if (fail(hipEventRecord(ev.copied[s], cs)) ||
             fail(hipStreamWaitEvent(compute, ev.copied[s], 0)) ||
             fail(launch_decompress(lay[g], ws, end - first, prep[g].tiles, prep[g].dtiles,
                                    results + first, compute, nullptr)) ||

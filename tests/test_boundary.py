@@ -135,11 +135,14 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
     jobs = (native.StreamJob * 2)(native.StreamJob(w0, 100, ctypes.addressof(payload), 64, 0),
                                   native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
 
-    def call(jobs=jobs, count=2, ends=(1, 2), staging=staging, slot=4096, ws=ws, ws_bytes=WS,
-             results=ctypes.addressof(res)):
+    copies = (ctypes.c_void_p * 2)(None, None)
+
+    def call(jobs=jobs, count=2, ends=(1, 2), staging=staging, slot=4096, slots=2, ws=ws,
+             ws_bytes=WS, results=ctypes.addressof(res), copy=copies, n_copy=1):
         ge = (ctypes.c_uint32 * max(1, len(ends)))(*ends) if ends is not None else None
         return lib.bf16d_decompress_streamed(jobs, count, ge, len(ends) if ends else 0, staging,
-                                             slot, ws, ws_bytes, results, None, None)
+                                             slot, slots, ws, ws_bytes, results, None, copy,
+                                             n_copy)
 
     E = native.EINVAL
     assert call(count=0) == E
@@ -154,6 +157,13 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
     assert call(ws_bytes=16) == E               # workspace too small
     assert call(results=None) == E
     assert call(staging=w0 + 64) == E           # staging overlaps the weights
+    assert call(slots=1) == E                   # a ring needs two slots at least
+    assert call(slots=65) == E                  # and at most 64
+    assert call(copy=None) == E                 # no copy streams
+    assert call(n_copy=0) == E
+    assert call(n_copy=9) == E                  # at most 8
+    # the third slot of a ring of three overlaps the second job's weights
+    assert call(staging=w1 - 2 * 4096 - 16, slots=3) == E
     bad = (native.StreamJob * 2)(native.StreamJob(w0 + 2, 100, ctypes.addressof(payload), 64, 0),
                                  native.StreamJob(w1, 100, ctypes.addressof(payload), 64, 0))
     assert call(jobs=bad) == E                  # weights alignment

@@ -1,5 +1,5 @@
 """GPU tests of the streamed receiver (bf16d_decompress_streamed): host-resident
-payloads applied in place group by group through two device slots.
+payloads applied in place group by group through a ring of device slots.
 
 The payloads come from the GPU compressor, whose bytes the other parity tests
 pin to the oracle; here the streamed apply must rebuild every tensor bit for
@@ -31,23 +31,25 @@ def _make(seed0=500):
     return pairs, payloads, checksums
 
 
-def _run(pairs, payloads, checksums, groups):
+def _run(pairs, payloads, checksums, groups, slots=3, copy_streams=2):
     recv = [s.clone() for s, _ in pairs]
-    sd = bd.StreamedDecompress(list(zip(recv, payloads, checksums)), groups)
+    sd = bd.StreamedDecompress(list(zip(recv, payloads, checksums)), groups, slots=slots,
+                               copy_streams=copy_streams)
     sd.run()
     return recv, sd.results()
 
 
+@pytest.mark.parametrize("slots,copies", [(2, 1), (3, 2), (5, 3)])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("groups", [[3, 1, 4, 4], [1] * 12, [12], [5, 7]])
-def test_streamed_apply_rebuilds_every_tensor(groups, packed):
+def test_streamed_apply_rebuilds_every_tensor(groups, packed, slots, copies):
     """packed: all payloads in one pinned buffer at 16-byte boundaries, so each
     group goes over in one transfer; otherwise one pinned tensor each."""
-    log(f"case streamed groups={groups} packed={packed}")
+    log(f"case streamed groups={groups} packed={packed} slots={slots} copies={copies}")
     pairs, payloads, checksums = _make()
     if packed:
         payloads = bd.StreamedDecompress.pin_packed(payloads)
-    recv, res = _run(pairs, payloads, checksums, groups)
+    recv, res = _run(pairs, payloads, checksums, groups, slots, copies)
     assert [r["status"] for r in res] == [bd.OK] * len(pairs)
     for j, (w, (_, d)) in enumerate(zip(recv, pairs)):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16)), f"tensor {j}"
@@ -72,15 +74,17 @@ def test_streamed_failures_match_the_oracle():
     assert all(res[j]["status"] == bd.OK for j in (0, 1, 3, 4, 6, 7, 8, 10, 11))
 
 
-def test_streamed_many_groups_reuse_both_slots_in_turn():
-    """40 one-tensor groups: each slot is refilled 20 times, so every copy
-    waits for the apply two groups back."""
-    log("case streamed 40 groups")
+@pytest.mark.parametrize("slots,copies", [(2, 1), (2, 2), (3, 2), (3, 4)])
+def test_streamed_many_groups_reuse_the_slots_in_turn(slots, copies):
+    """40 one-tensor groups: each slot is refilled 40 / slots times, so every
+    copy waits for the apply `slots` groups back, on whichever copy stream
+    its group falls to."""
+    log(f"case streamed 40 groups slots={slots} copies={copies}")
     pairs = [synth.make_pair((8192 * (1 + i % 3) + i,), "0.05", synth.MIX_DEFAULT, 1300 + i, DEV)
              for i in range(40)]
     out = bd.compress_batch(pairs)
     payloads = [p.cpu().pin_memory() for p, _, _ in out]
-    recv, res = _run(pairs, payloads, [cs for _, cs, _ in out], [1] * 40)
+    recv, res = _run(pairs, payloads, [cs for _, cs, _ in out], [1] * 40, slots, copies)
     assert all(r["status"] == bd.OK for r in res)
     for w, (_, d) in zip(recv, pairs):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16))
