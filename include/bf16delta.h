@@ -62,7 +62,7 @@
  *   - src, dst, weights, payload and workspace are device pointers and must
  *     be 16-byte aligned.
  *   - `results` must be memory the device can write: device memory, or
- *     pinned host memory.
+ *     pinned host memory.  It may not overlap any buffer the call writes.
  *   - `stream` is a HIP stream; NULL means the null stream.  All device work
  *     is enqueued on it, and results[] is valid once the stream has
  *     completed.

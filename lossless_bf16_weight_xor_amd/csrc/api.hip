@@ -139,7 +139,7 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     const size_t need = nsegs ? seg_at + sizeof(RemapSegment) * nsegs : l.total;
     if (workspace_bytes < need) return BF16D_EINVAL;
     std::vector<Range> ranges;
-    ranges.reserve(2 * size_t(count) + nsegs + 1);
+    ranges.reserve(2 * size_t(count) + nsegs + 3);
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_decompress_job &J = jobs[j];
         if (remaps && remaps[j].count > 0) {
@@ -157,6 +157,8 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     }
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + need, true});
+    ranges.push_back({reinterpret_cast<uintptr_t>(results),
+                      reinterpret_cast<uintptr_t>(results + count), true});
     if (versions)
         ranges.push_back({reinterpret_cast<uintptr_t>(versions),
                           reinterpret_cast<uintptr_t>(versions + count), true});
@@ -234,7 +236,7 @@ int compress_call(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
                 return BF16D_EINVAL;
     std::vector<uint64_t> start(size_t(count) + 1, 0), dstart(size_t(count) + 1, 0);
     std::vector<Range> ranges;
-    ranges.reserve(3 * size_t(count) + 1);
+    ranges.reserve(3 * size_t(count) + 2);
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_compress_job &J = jobs[j];
         if (J.n > 0 && (!J.src || !J.dst || !aligned16(J.src) || !aligned16(J.dst)))
@@ -256,6 +258,8 @@ int compress_call(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
     if (workspace_bytes < l.total) return BF16D_EINVAL;
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + l.total, true});
+    ranges.push_back({reinterpret_cast<uintptr_t>(results),
+                      reinterpret_cast<uintptr_t>(results + count), true});
     if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
 
     // job table, block starts and scan-tile starts, laid out as in the workspace

@@ -30,8 +30,8 @@ struct Span {
     uintptr_t lo, hi;
 };
 
-// The device ranges written by the call (weights, the slots, workspace) may
-// not overlap.
+// The device ranges written by the call (weights, the slots, workspace,
+// results) may not overlap.
 bool spans_disjoint(std::vector<Span> v) {
     v.erase(std::remove_if(v.begin(), v.end(), [](const Span &s) { return s.hi <= s.lo; }),
             v.end());
@@ -83,7 +83,7 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
     std::vector<bf16d_decompress_job> dj(count);
     std::vector<uint64_t> offset(count, 0);
     std::vector<Span> spans;
-    spans.reserve(size_t(count) + 3);
+    spans.reserve(size_t(count) + 4);
     uint32_t first = 0;
     for (uint32_t g = 0; g < groups; ++g) {
         const uint32_t end = group_end[g];
@@ -126,6 +126,8 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
                      reinterpret_cast<uintptr_t>(staging) + slots * slot_bytes});
     spans.push_back({reinterpret_cast<uintptr_t>(workspace),
                      reinterpret_cast<uintptr_t>(workspace) + need});
+    spans.push_back({reinterpret_cast<uintptr_t>(results),
+                     reinterpret_cast<uintptr_t>(results + count)});
     if (!spans_disjoint(spans)) return BF16D_EINVAL;
     std::vector<uint8_t> host(tables, 0);
     first = 0;

@@ -110,6 +110,18 @@ def test_invalid_arguments_are_rejected_before_any_gpu_work(native):
     djob = native.DecompressJob(ws_ptr, 64, ws_ptr + 64, 64, 0)
     assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, 1 << 14,
                                 ctypes.addressof(res), None) == native.EINVAL
+    # results overlapping a buffer the call writes (otherwise valid calls: the
+    # workspace is large enough, so only the overlap refuses them)
+    need = lib.bf16d_workspace_bytes(16, 1)
+    assert need <= (1 << 16) - 16384
+    job = native.CompressJob(ws_ptr, ws_ptr + 64, 16, ws_ptr + 128, 128)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, need,
+                              ws_ptr + 8192 + 64, None) == native.EINVAL      # in the workspace
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, need,
+                              ws_ptr + 160, None) == native.EINVAL            # in the payload
+    djob = native.DecompressJob(ws_ptr, 16, ws_ptr + 128, 64, 0)
+    assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, need,
+                                ws_ptr + 16, None) == native.EINVAL          # in the weights
 
 
 def test_python_api_refuses_cpu_tensors(native):
@@ -157,6 +169,7 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
     assert call(ws_bytes=16) == E               # workspace too small
     assert call(results=None) == E
     assert call(staging=w0 + 64) == E           # staging overlaps the weights
+    assert call(results=ws + 64) == E           # results inside the workspace
     assert call(slots=1) == E                   # a ring needs two slots at least
     assert call(slots=65) == E                  # and at most 64
     assert call(copy=None) == E                 # no copy streams
