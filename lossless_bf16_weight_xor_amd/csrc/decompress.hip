@@ -395,7 +395,8 @@ __device__ __forceinline__ void stage_record_word(const ApplyPlan &pe, uint4 rv,
 // whose record lies wholly in the staged window: thread t owns fields
 // [t*F, t*F + F), reads them from one window of three (gaps) and two
 // (mantissas) LDS dwords, keeps them in registers, and writes the XOR of
-// every changed element into s_x.  Returns this thread's share of `bad`.
+// every changed element into s_x.  Up to 256 fields, wave 0 does it alone
+// (lane t owns [t*F, t*F + F)).  Returns this thread's share of `bad`.
 // kOw (an overwrite record): no mantissa fields; every change takes the next
 // word, its new value, which goes to s_x as it is.
 constexpr uint32_t kFastFields = 4;
@@ -409,8 +410,14 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
                                                       uint16_t *s_x, ApplyShared &sa,
                                                       uint32_t tid, BF16D_GMEM uint16_t *wts) {
     const uint32_t lane = tid & 63, wave = tid >> 6;
-    const uint32_t F = (c + kThreads - 1) / kThreads;
-    const uint32_t jb = tid * F < c ? tid * F : c;
+    // A sparse block (at most 256 fields) is decoded by wave 0 alone: its
+    // scans stay within the wave, with no exchange of totals between waves
+    // and no barrier; the other waves have nothing to do here.
+    const bool one = c <= 64 * kFastFields;   // uniform
+    if (one && wave != 0) return 0;
+    const uint32_t idx = one ? lane : tid, n_threads = one ? 64u : kThreads;
+    const uint32_t F = (c + n_threads - 1) / n_threads;
+    const uint32_t jb = idx * F < c ? idx * F : c;
     const uint32_t nf = (jb + F < c ? jb + F : c) - jb;
     uint32_t g0 = 0, g1 = 0, g2 = 0, m0 = 0, m1 = 0, gsh = 0, msh = 0;
     if (nf) {
@@ -450,23 +457,26 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
     const uint32_t inc_g = wave_incl_add(sum_g1);
     const uint32_t top_wave = __ballot(top) != 0;
     const uint32_t tot_g = lane63(inc_g);   // outside the branch below: see lane63
-    if (lane == 0) {
-        sa.a[wave] = tot_g;
-        sa.b[wave] = e_wave;
-        sa.c[wave] = top_wave;
-    }
-    __syncthreads();
     uint32_t run = inc_g - sum_g1, e = e_lane;
-    uint32_t total_g1 = 0, esc_total = 0, any_top = 0;
-#pragma unroll
-    for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
-        if (w2 < wave) {
-            run += sa.a[w2];
-            e += sa.b[w2];
+    uint32_t total_g1 = tot_g, esc_total = e_wave, any_top = top_wave;
+    if (!one) {   // every wave has fields: add up the waves' totals
+        if (lane == 0) {
+            sa.a[wave] = tot_g;
+            sa.b[wave] = e_wave;
+            sa.c[wave] = top_wave;
         }
-        total_g1 += sa.a[w2];
-        esc_total += sa.b[w2];
-        any_top |= sa.c[w2];
+        __syncthreads();
+        total_g1 = esc_total = any_top = 0;
+#pragma unroll
+        for (uint32_t w2 = 0; w2 < kWaves; ++w2) {
+            if (w2 < wave) {
+                run += sa.a[w2];
+                e += sa.b[w2];
+            }
+            total_g1 += sa.a[w2];
+            esc_total += sa.b[w2];
+            any_top |= sa.c[w2];
+        }
     }
     uint32_t bad = (total_g1 - 1 >= L) | (esc_total != r) | (any_top == 0);
 #pragma unroll
