@@ -59,6 +59,9 @@ METRIC = "compress / decompress GB/s of BF16 weights (% of HBM peak); payload % 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "encode_kernel_7b_traffic.txt")
 KERNEL_SOURCES = ("lossless_bf16_weight_xor_amd/csrc/compress.hip",
                   "lossless_bf16_weight_xor_amd/csrc/internal.hpp")
+APPLY_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "apply_kernel_7b_traffic.txt")
+APPLY_SOURCES = ("lossless_bf16_weight_xor_amd/csrc/decompress.hip",
+                 "lossless_bf16_weight_xor_amd/csrc/internal.hpp")
 
 
 def log(msg):
@@ -92,27 +95,27 @@ def generate(workload: str, device, limit=None):
     return names, pairs, desc
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(elements: int):
-    """HBM bytes per encode launch from the committed counter summary, or None
-    if there is none, it was taken on another workload (element count), or the
-    kernel sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+def measured_traffic(elements: int, profile=TRAFFIC_PROFILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of a kernel (the encoder by default) from its
+    committed counter summary, or None if there is none, it was taken on
+    another workload (element count), or the kernel sources changed since."""
+    if not os.path.exists(profile):
         return None
     fields = {}
-    with open(TRAFFIC_PROFILE) as f:
+    with open(profile) as f:
         for line in f:
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != kernel_source_hash():
+    if fields.get("source_sha256") != kernel_source_hash(sources):
         return None
     if fields.get("elements_per_call") != str(elements):
         return None
@@ -649,7 +652,9 @@ def main():
         "roofline_decompress": {"bound": "hbm", "kernel": "apply_kernel",
                                 "achieved": round(dec_alg / t_app / 1e9, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4)},
+                                "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4),
+                                "traffic": measured_traffic(n_total, APPLY_TRAFFIC_PROFILE,
+                                                            APPLY_SOURCES)},
         "achievable": ceiling,
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,
