@@ -86,6 +86,12 @@ def generate(workload: str, device, limit=None):
         it = synth.config5(device, limit=limit)
         desc = ("one-GPU share of a 70B-shaped model: 40 of 80 layers (hidden 8192, FFN 28672, "
                 "GQA 64q/8kv, head_dim 128, 360 tensors); 1% uniform changes, 95/4.5/0.5")
+    elif workload.startswith("c3-") and workload[3:] in synth.C3_RATES:
+        rate = workload[3:]
+        src, dst = synth.config3(device, rate)
+        it = [("tensor", src, dst)]
+        desc = (f"one 1-D BF16 tensor of 536,870,912 elements (1 GiB), {float(rate) * 100:g}% "
+                "uniform changes, 95/4.5/0.5")
     else:
         raise SystemExit(f"unknown workload {workload}")
     names, pairs = [], []
@@ -425,7 +431,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="7b", choices=["7b", "70b-half"])
+    ap.add_argument("--workload", default="7b",
+                    choices=["7b", "70b-half"] + ["c3-" + r for r in ("0.00085", "0.01", "0.03",
+                                                                      "0.05")],
+                    help="7b (the default), the 70B half-model share, or one 1 GiB tensor at a "
+                         "change rate (c3-<rate>)")
     ap.add_argument("--limit", type=int, default=None, help="first N tensors only (debug)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")
@@ -554,7 +564,7 @@ def main():
         del a, b
 
     remap_info = None
-    if not args.no_remapped:
+    if not args.no_remapped and args.workload in ("7b", "70b-half"):
         from lossless_bf16_weight_xor_amd import synth
         specs = synth.seven_b_specs() if args.workload == "7b" else synth.config5_specs()
         remap_info = remapped(bd, names, [sp.shape for sp in specs], pairs, payloads, cs_new,
