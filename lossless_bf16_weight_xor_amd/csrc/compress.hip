@@ -333,7 +333,7 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
     __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
     __shared__ EncodeShared sh;
-    const uint64_t t = blockIdx.x;
+    const uint64_t t = xcd_tile(blockIdx.x, gridDim.x);
     const CompressJob &job = jobs[tile_job[t]];
     const TileRef tr = tile_ref(job, t);
     if (job.flags & kFlagOverwrite) {   // overwrite payloads: their own instances

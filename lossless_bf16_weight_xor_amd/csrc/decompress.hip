@@ -892,7 +892,7 @@ void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restric
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];        // dense XOR tile
     __shared__ __attribute__((aligned(16))) uint32_t s_raw[kStageWords];  // staged record
     __shared__ ApplyShared sa;
-    const uint64_t tile = blockIdx.x;
+    const uint64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const ApplyPlan pe = plan[tile];
     const uint32_t L = pe.len_room & 0x3FFFu;
     if (pe.len_room & kPlanOverwrite) {   // overwrite records: verified here, written later

@@ -224,6 +224,17 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
 __device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Workgroup b of a launch runs on XCD b % 8 (workgroups are dispatched to
+// the XCDs in turn).  A one-workgroup-per-tile kernel maps b to a tile so
+// that each XCD takes a contiguous range (XCD x: q + (x < r) tiles from
+// x*q + min(x, r), q = tiles / 8, r = tiles % 8): neighbouring tiles, and
+// the lines of per-tile tables they share, stay in one L2.  A bijection on
+// [0, tiles) whatever the dispatch order.
+__device__ __forceinline__ uint64_t xcd_tile(uint64_t b, uint64_t tiles) {
+    const uint64_t q = tiles >> 3, r = tiles & 7, x = b & 7, y = b >> 3;
+    return x * q + (x < r ? x : r) + y;
+}
+
 // Counts the workgroups of a grid as they finish; true in the last one.
 // Workgroups hand results to it only through device-scope atomics, which the
 // last workgroup reads with device-scope loads.  `dep` is the XOR of the
