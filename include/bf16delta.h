@@ -331,8 +331,9 @@ int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_rema
  * device slots, one group of tensors (a layer) at a time, so that the copy
  * of one group overlaps the in-place apply of the previous one and only two
  * groups' payloads are ever on the device.  Here the copies are host-to-
- * device DMA transfers on `copy`, the applies are bf16d_decompress calls on
- * `compute`, and the slots form a ring of `slots` (two or more): with two,
+ * device DMA transfers on the copy streams, the applies are
+ * bf16d_decompress calls on `compute`, and the slots form a ring of `slots`
+ * (two or more): with two,
  * every copy waits for the apply just before it, so each cross-stream wait
  * lands on the copies' critical path; three give the copies one group of
  * slack.
