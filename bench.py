@@ -569,10 +569,21 @@ def main():
         specs = synth.seven_b_specs() if args.workload == "7b" else synth.config5_specs()
         remap_info = remapped(bd, names, [sp.shape for sp in specs], pairs, payloads, cs_new,
                               cs_old, 4)
+        # the same payloads and changes: the algorithmic bytes of the plain decompress
+        remap_info["hbm_pct"] = round(100 * dec_alg / (remap_info["ms"] / 1e3) / 1e9 /
+                                      HBM_PEAK_GBPS, 2)
 
     bound_info = None
     if not args.no_bound:
         bound_info = bound_overwrite(bd, pairs, 3)
+        # algorithmic bytes with the overwrite payload: 4n + P to compress,
+        # 2n + P + 2c to decompress (the same changes)
+        P_ow = bound_info["payload_bytes"]
+        bound_info["compress_hbm_pct"] = round(
+            100 * (4 * n_total + P_ow) / (bound_info["compress_ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 2)
+        bound_info["decompress_hbm_pct"] = round(
+            100 * (2 * n_total + P_ow + 2 * n_changed) / (bound_info["decompress_ms"] / 1e3) / 1e9
+            / HBM_PEAK_GBPS, 2)
 
     race_info = None
     if not args.no_race:
