@@ -163,6 +163,35 @@ def test_batched_call_matches_per_tensor_oracle():
         assert torch.equal(w.view(torch.int16), dst.view(torch.int16)), j
 
 
+def test_thousands_of_tiny_jobs_in_one_call():
+    """3000 tensors of 0..300 elements (every tenth one empty) in one call:
+    the per-job passes of the descriptor scan and checksum sum run many
+    rounds over a workgroup's threads, and most tiles are ragged."""
+    log("case 3000 tiny jobs")
+    rng = np.random.default_rng(77)
+    sizes = rng.integers(1, 301, size=3000)
+    sizes[::10] = 0
+    rates = ["0", "0.02", "0.2", "1"]
+    pairs = []
+    for j, n in enumerate(sizes):
+        if n == 0:
+            s = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+            pairs.append((s, s.clone()))
+        else:
+            s, d = pair((int(n),), rates[j % 4], synth.MIX_ADVERSARIAL, 7000 + j, "cpu")
+            pairs.append((s.to(DEV), d.to(DEV)))
+    out = compress_batch(pairs)
+    for j, ((src, dst), (payload, cs, _)) in enumerate(zip(pairs, out)):
+        ref_payload, ref_cs, _ = oracle_of(src, dst)
+        assert cs == ref_cs, j
+        assert_same_bytes(payload_np(payload), ref_payload, f"tiny job {j}")
+    ws = [s.clone() for s, _ in pairs]
+    res = decompress_batch([(w, p, cs) for w, (p, cs, _) in zip(ws, out)])
+    for j, (w, (_, dst), r) in enumerate(zip(ws, pairs, res)):
+        assert r["status"] == OK, j
+        assert torch.equal(w.view(torch.int16), dst.view(torch.int16)), j
+
+
 def test_capacity_too_small_reports_the_exact_size():
     src, dst = pair((5 * 8192,), "0.3", synth.MIX_DEFAULT, 9, DEV)
     ref_payload, _, _ = oracle_of(src, dst)
