@@ -23,7 +23,9 @@ Reported:
               timed with events recorded around it on its stream
   achievable: the read ceiling of the encoder's access pattern (a probe
               kernel that only reads), over old and new and over old alone,
-              and each main kernel's fraction of it
+              and each main kernel's fraction of it; and the in-place floor
+              (a probe that reads old and writes back, unchanged, the 16-byte
+              chunks the delta changes) with the apply kernel's fraction of it
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
   bound_overwrite : the same pair as version-2 overwrite payloads (absolute
@@ -339,11 +341,40 @@ def bound_overwrite(bd, pairs, steps):
             "decompress_gbps_weights": round(2 * n / td / 1e9, 2)}
 
 
-def read_ceiling(bd, n, dev, steps):
+def dirty_chunks(pairs, n, dev):
+    """One bit per 16-byte chunk of the first n elements of the workload's
+    tensors laid end to end (bit c & 31 of int32 word c >> 5 for chunk c): set
+    where old and new differ in any of the chunk's 8 elements."""
+    nchunks = n // 8192 * 1024
+    bits = torch.zeros(nchunks, dtype=torch.bool, device=dev)
+    at = 0
+    for src, dst in pairs:
+        m = src.numel()
+        if at >= nchunks * 8:
+            break
+        d = src.reshape(-1).view(torch.int16) != dst.reshape(-1).view(torch.int16)
+        lead, tail = at % 8, -(at + m) % 8
+        z = lambda k: torch.zeros(k, dtype=torch.bool, device=dev)
+        c = torch.cat([z(lead), d, z(tail)]).view(-1, 8).any(1)
+        c0 = at // 8
+        k = min(c.numel(), nchunks - c0)
+        bits[c0:c0 + k] |= c[:k]
+        at += m
+    w8 = torch.tensor([1, 2, 4, 8, 16, 32, 64, 128], dtype=torch.uint8, device=dev)
+    packed = (bits.view(-1, 8).to(torch.uint8) * w8).sum(1, dtype=torch.uint8)
+    chunk_pct = 100 * bits.float().mean().item()
+    line_pct = 100 * bits.view(-1, 8).any(1).float().mean().item()
+    return packed.view(torch.int32), chunk_pct, line_pct
+
+
+def read_ceiling(bd, n, dev, steps, pairs=None):
     """The read ceiling of the encoder's access pattern (bf16d_probe_read: one
     workgroup per 8192-element block, 16-byte loads, nothing else) over two
     flat n-element arrays, as the encoder reads old and new, and over one, as
-    the apply pass reads old.  Their contents do not matter."""
+    the apply pass reads old.  Their contents do not matter.  With the
+    workload's pairs, also the in-place floor (bf16d_probe_inplace): the same
+    reads of one array plus, written back unchanged, every 16-byte chunk that
+    the workload's delta changes."""
     a = torch.empty(n, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
     sink = torch.empty(1, dtype=torch.int64, device=dev)
@@ -361,6 +392,20 @@ def read_ceiling(bd, n, dev, steps):
         nbytes = (2 if arrays[1] is not None else 1) * 2 * full
         out[key] = {"bytes": nbytes, "ms": round(1e3 * t, 4), "gbps": round(nbytes / t / 1e9, 2),
                     "pct_of_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBPS, 2)}
+    if pairs is not None:
+        dirty, chunk_pct, line_pct = dirty_chunks(pairs, n, dev)
+        bd.probe_inplace(a, dirty, sink=sink)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            bd.probe_inplace(a, dirty, sink=sink)
+        ev[1].record()
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) / 1e3 / steps
+        out["inplace_floor"] = {"ms": round(1e3 * t, 4), "elements": full,
+                                "dirty_chunks_pct": round(chunk_pct, 3),
+                                "dirty_lines_pct": round(line_pct, 3)}
+        del dirty
     del a, b
     torch.cuda.empty_cache()
     return out
@@ -619,13 +664,21 @@ def main():
     # a large free slows the streamed receiver's copies for some seconds
     ceiling = None
     if not args.no_probe:
-        ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2))
+        ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2),
+                               pairs)
         ceiling["encode_kernel_frac_of_read2"] = round(comp_alg / t_enc / 1e9 /
                                                        ceiling["read2"]["gbps"], 4)
         ceiling["apply_kernel_frac_of_read1"] = round(dec_alg / t_app / 1e9 /
                                                       ceiling["read1"]["gbps"], 4)
         log(f"read ceiling: {ceiling['read2']['gbps']} GB/s over two arrays, "
             f"{ceiling['read1']['gbps']} GB/s over one")
+        # (the probe covers whole 8192-element blocks of the flat array: all
+        # but the last few thousand elements of the workload)
+        if "inplace_floor" in ceiling and ceiling["inplace_floor"]["elements"] >= 0.999 * n_total:
+            ceiling["apply_kernel_frac_of_inplace_floor"] = round(
+                ceiling["inplace_floor"]["ms"] / (1e3 * t_app), 4)
+            log(f"in-place floor: {ceiling['inplace_floor']['ms']} ms "
+                f"({ceiling['inplace_floor']['dirty_lines_pct']}% of 128-byte lines written)")
 
     gpu_payloads = [None] * len(pairs)
     cpu = None

@@ -34,7 +34,8 @@ __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_b
            "CompressBatch", "DecompressBatch", "StreamedDecompress", "RemappedBatch",
            "decompress_remapped", "race_compress", "race_decompress", "codec_available",
            "RaceFrame", "DEFAULT_RACE", "FormatError", "ChecksumError",
-           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT", "probe_read"]
+           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT", "probe_read",
+           "probe_inplace"]
 
 
 class FormatError(ValueError):
@@ -406,6 +407,24 @@ def probe_read(a: torch.Tensor, b: torch.Tensor | None = None,
         raise ValueError("sink must be an int64 tensor on a's device")
     _check_rc(_native.lib().bf16d_probe_read(pa, pb, a.numel(), sink.data_ptr(), _PROBE_KEY,
                                              _stream(a.device)), "bf16d_probe_read")
+
+
+def probe_inplace(w: torch.Tensor, dirty: torch.Tensor, sink: torch.Tensor | None = None) -> None:
+    """Measurement aid: read w with the apply pass's access pattern and write
+    back, unchanged, each 16-byte chunk that `dirty` marks (one bit per chunk,
+    int32 words, `bf16d_probe_inplace`), enqueued on the current stream."""
+    pw = _weights_ptr(w, "w")
+    if (dirty.device != w.device or dirty.dtype != torch.int32 or not dirty.is_contiguous()
+            or dirty.numel() < 32 * (w.numel() // BLOCK_ELEMS)):
+        raise ValueError("dirty must be a contiguous int32 tensor on w's device with 32 words "
+                         "per 8192-element block")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int64, device=w.device)
+    if sink.device != w.device or sink.dtype != torch.int64 or sink.numel() < 1:
+        raise ValueError("sink must be an int64 tensor on w's device")
+    _check_rc(_native.lib().bf16d_probe_inplace(pw, w.numel(), dirty.data_ptr(), sink.data_ptr(),
+                                                _PROBE_KEY, _stream(w.device)),
+              "bf16d_probe_inplace")
 
 
 def _first_capacity(n: int) -> int:

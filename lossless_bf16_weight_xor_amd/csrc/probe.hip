@@ -1,11 +1,20 @@
-// probe.hip -- a measurement aid, not a step of the method.
+// probe.hip -- measurement aids, not steps of the method.
 //
-// The encoder's whole-block access pattern with nothing else: one workgroup
-// of 256 threads per 8192-element block, four 16-byte loads per thread from
-// each array, all in flight together.  Its time is the read ceiling of that
-// pattern on the device, against which the encoder (both checkpoints) and
-// the apply pass (one) are compared; the published HBM peak stays the
-// roofline.
+// Both take the blocks in the main kernels' order: each XCD (workgroup index
+// mod 8) a contiguous range of blocks.
+//
+// probe_read_kernel: the encoder's whole-block access pattern with nothing
+// else: one workgroup of 256 threads per 8192-element block, four 16-byte
+// loads per thread from each array, all in flight together.  Its time is the
+// read ceiling of that pattern on the device, against which the encoder
+// (both checkpoints) and the apply pass (one) are compared.
+//
+// probe_inplace_kernel: the apply pass's traffic with nothing else: the same
+// whole-block reads of one array, and each 16-byte chunk that a bitmap marks
+// written back, unchanged, in place.  Given the chunks a delta changes, its
+// time is the floor of any in-place apply of that delta with this access
+// pattern: reads of every weight plus line-granular writes of the changed
+// chunks.  The published HBM peak stays the roofline of both.
 #include "internal.hpp"
 
 namespace bf16d {
@@ -20,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint16_t *__
                                                               uint64_t key) {
     auto *a = (BF16D_GMEM const uint16_t *)pa;
     auto *b = (BF16D_GMEM const uint16_t *)pb;
-    const uint64_t base = (uint64_t)blockIdx.x * kBlock;
+    const uint64_t base = xcd_tile(blockIdx.x, gridDim.x) * kBlock;
     uint4 x[kChunksPerThread], y[kChunksPerThread];
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
@@ -36,6 +45,50 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint16_t *__
                ((uint64_t)(x[i].z ^ y[i].z) << 32 | (x[i].w ^ y[i].w));
     // keeps the loads: the store happens only if the fold hits the caller's key
     if (acc == key) sink[0] = acc;
+}
+
+// dirty: bit (c & 31) of word c >> 5 marks chunk c (elements 8c .. 8c + 7).
+__global__ __launch_bounds__(kThreads) void probe_inplace_kernel(uint16_t *__restrict__ pw,
+                                                                 const uint32_t *__restrict__ pd,
+                                                                 uint64_t *__restrict__ sink,
+                                                                 uint64_t key) {
+    auto *w = (BF16D_GMEM uint16_t *)pw;
+    auto *dirty = (BF16D_GMEM const uint32_t *)pd;
+    const uint64_t base = xcd_tile(blockIdx.x, gridDim.x) * kBlock;
+    const uint64_t word0 = base / 8 / 32;   // the block's 1024 chunk bits: 32 words
+    uint4 x[kChunksPerThread];
+    uint32_t m[kChunksPerThread];
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t q = threadIdx.x + kThreads * i;
+        x[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(w + base + 8 * q);
+        m[i] = dirty[word0 + (q >> 5)];
+    }
+    uint64_t acc = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t q = threadIdx.x + kThreads * i;
+        acc += ((uint64_t)x[i].x << 32 | x[i].y) + ((uint64_t)x[i].z << 32 | x[i].w);
+        if ((m[i] >> (q & 31)) & 1u) {
+            uint4 v = x[i];
+            // the value is opaque here, so the store of what was just loaded
+            // from the same place is not removed as redundant
+            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+            *reinterpret_cast<BF16D_GMEM uint4 *>(w + base + 8 * q) = v;
+        }
+    }
+    if (acc == key) sink[0] = acc;
+}
+
+int probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink, uint64_t key,
+                  hipStream_t stream) {
+    const uint64_t blocks = n / kBlock;
+    if (!w || !dirty || !sink || ((uintptr_t)w & 15) || ((uintptr_t)dirty & 3) ||
+        ((uintptr_t)sink & 7) || blocks > 0x7FFFFFFFull)
+        return BF16D_EINVAL;
+    if (blocks == 0) return BF16D_OK;
+    probe_inplace_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(w, dirty, sink, key);
+    return hipGetLastError() == hipSuccess ? BF16D_OK : BF16D_EHIP;
 }
 
 int probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink, uint64_t key,
@@ -57,4 +110,9 @@ int probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink,
 extern "C" int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink,
                                 uint64_t key, hipStream_t stream) {
     return bf16d::probe_read(a, b, n, sink, key, stream);
+}
+
+extern "C" int bf16d_probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink,
+                                   uint64_t key, hipStream_t stream) {
+    return bf16d::probe_inplace(w, n, dirty, sink, key, stream);
 }

@@ -1,7 +1,8 @@
-"""The read-ceiling probe (a measurement aid): argument checks and that it
-runs over whole blocks.  It computes nothing the method uses, so there is no
-oracle value to compare; the checks are that it accepts what it documents
-and refuses the rest."""
+"""The read-ceiling and in-place floor probes (measurement aids): argument
+checks, that they run over whole blocks, and that the in-place probe leaves
+its array as it was.  They compute nothing the method uses, so there is no
+oracle value to compare; the checks are that they accept what they document
+and refuse the rest."""
 import pytest
 import torch
 
@@ -36,4 +37,48 @@ def test_probe_refuses_bad_arguments():
     assert L.bf16d_probe_read(a.data_ptr(), 0, 0, sink.data_ptr(), 1, s) == bd.OK
     with pytest.raises(ValueError):
         bd.probe_read(a, a[:8192], sink=sink)   # b shorter than a
+    torch.cuda.synchronize()
+
+
+def test_inplace_probe_leaves_the_array_as_it_was():
+    """The in-place floor probe writes marked chunks back unchanged: after two
+    runs (some blocks fully marked, one partly, one not at all) every element
+    is what it was, and the sink is untouched (its key is not hit)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    w = torch.randint(-32768, 32767, (3 * 8192 + 5,), dtype=torch.int16, device=dev,
+                      generator=g)
+    before = w.clone()
+    dirty = torch.zeros(3 * 32, dtype=torch.int32, device=dev)
+    dirty[:32] = torch.randint(-2**31, 2**31 - 1, (32,), dtype=torch.int32, device=dev,
+                               generator=g)
+    dirty[32:64] = -1   # every chunk of the second block
+    sink = torch.full((1,), 7, dtype=torch.int64, device=dev)
+    bd.probe_inplace(w, dirty, sink=sink)
+    bd.probe_inplace(w, dirty, sink=sink)
+    bd.probe_inplace(w[:100], dirty, sink=sink)   # no whole block: nothing launched
+    torch.cuda.synchronize()
+    assert torch.equal(w, before)
+    assert sink.item() == 7
+
+
+def test_inplace_probe_refuses_bad_arguments():
+    dev = torch.device("cuda:0")
+    w = torch.zeros(8192 * 2, dtype=torch.int16, device=dev)
+    dirty = torch.zeros(64, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
+    L = _native.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    pw, pd, ps = w.data_ptr(), dirty.data_ptr(), sink.data_ptr()
+    assert L.bf16d_probe_inplace(0, 8192, pd, ps, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw, 8192, 0, ps, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw, 8192, pd, 0, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw + 2, 8192, pd, ps, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw, 8192, pd + 2, ps, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw, 8192, pd, ps + 4, 1, s) == bd.EINVAL
+    assert L.bf16d_probe_inplace(pw, 0, pd, ps, 1, s) == bd.OK
+    with pytest.raises(ValueError):
+        bd.probe_inplace(w, dirty[:63], sink=sink)   # fewer than 32 words per block
+    with pytest.raises(ValueError):
+        bd.probe_inplace(w, dirty.view(torch.int16), sink=sink)
     torch.cuda.synchronize()
