@@ -25,7 +25,8 @@ Reported:
               kernel that only reads), over old and new and over old alone,
               and each main kernel's fraction of it; and the in-place floor
               (a probe that reads old and writes back, unchanged, the 16-byte
-              chunks the delta changes) with the apply kernel's fraction of it
+              chunks the delta changes: a reference point for that traffic,
+              not a strict bound) with the apply kernel's fraction of it
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
   bound_overwrite : the same pair as version-2 overwrite payloads (absolute

@@ -511,14 +511,14 @@ int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t 
  * apply with nothing else.  Reads the first 8192 * floor(n / 8192) elements
  * of w with the apply pass's whole-block pattern (in the same block order as
  * bf16d_probe_read) and writes back, unchanged, every 16-byte chunk c
- * (elements 8c .. 8c + 7) whose bit (c & 31) of
- * dirty[c >> 5] is set, so that, given the chunks a delta changes, its time
- * is the floor of applying that delta in place with this pattern.  w: device,
- * 16-byte aligned, n elements, left as it was; dirty: device, 4-byte
- * aligned, at least 32 * floor(n / 8192) words; sink as in bf16d_probe_read.
- * No other work may write w meanwhile.  Returns BF16D_EINVAL for a NULL or
- * misaligned pointer or more than 2^31 - 1 blocks; BF16D_EHIP if the launch
- * fails; else BF16D_OK. */
+ * (elements 8c .. 8c + 7) whose bit (c & 31) of dirty[c >> 5] is set, so
+ * that, given the chunks a delta changes, its time is the cost of applying
+ * that delta's traffic in place through the simplest kernel (a reference
+ * point, not a strict lower bound).  w: device, 16-byte aligned, n elements,
+ * left as it was; dirty: device, 4-byte aligned, at least 32 * floor(n /
+ * 8192) words; sink as in bf16d_probe_read.  No other work may write w
+ * meanwhile.  Returns BF16D_EINVAL for a NULL or misaligned pointer or more
+ * than 2^31 - 1 blocks; BF16D_EHIP if the launch fails; else BF16D_OK. */
 int bf16d_probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink,
                         uint64_t key, hipStream_t stream);
 

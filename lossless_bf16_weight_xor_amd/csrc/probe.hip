@@ -12,9 +12,11 @@
 // probe_inplace_kernel: the apply pass's traffic with nothing else: the same
 // whole-block reads of one array, and each 16-byte chunk that a bitmap marks
 // written back, unchanged, in place.  Given the chunks a delta changes, its
-// time is the floor of any in-place apply of that delta with this access
-// pattern: reads of every weight plus line-granular writes of the changed
-// chunks.  The published HBM peak stays the roofline of both.
+// time is the cost of an in-place apply's traffic (reads of every weight plus
+// writes of the changed chunks) through the simplest kernel: a reference
+// point for the apply pass, not a strict lower bound, since the order and
+// timing of the writes change their cost.  The published HBM peak stays the
+// roofline of both.
 #include "internal.hpp"
 
 namespace bf16d {
