@@ -41,3 +41,36 @@ def test_counter_traffic_is_reported_only_for_the_profiled_workload():
     assert (bench.measured_traffic(int(fields["elements_per_call"])) is not None) == current
     assert bench.measured_traffic(34_226_176_000) is None       # another workload
     assert bench.measured_traffic(1) is None
+
+
+def test_dirty_chunk_bitmap_of_the_in_place_probe():
+    """bench.dirty_chunks marks chunk c (elements 8c .. 8c + 7 of the tensors
+    laid end to end) in bit c & 31 of word c >> 5 exactly when old and new
+    differ in it, also for chunks that straddle two tensors, and covers whole
+    8192-element blocks only."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+    import bench
+    g = torch.Generator().manual_seed(11)
+    pairs = []
+    for m in (8192 * 3 + 5, 3, 100, 8192 * 2 - 3, 8192):
+        s = torch.randint(-1000, 1000, (m,), generator=g, dtype=torch.int16)
+        d = s.clone()
+        d[torch.randint(0, m, (m // 40 + 1,), generator=g)] += 1
+        pairs.append((s, d))
+    pairs.append((torch.zeros(8192, dtype=torch.int16), torch.zeros(8192, dtype=torch.int16)))
+    n = sum(s.numel() for s, _ in pairs)
+    words, chunk_pct, line_pct = bench.dirty_chunks(pairs, n, torch.device("cpu"))
+    full = n // 8192 * 8192
+    assert words.dtype == torch.int32 and words.numel() == full // 8192 * 32
+    old = torch.cat([s for s, _ in pairs]).numpy()[:full]
+    new = torch.cat([d for _, d in pairs]).numpy()[:full]
+    want = (old != new).reshape(-1, 8).any(1)
+    w = words.numpy().view(np.uint32)
+    got = (w[np.arange(want.size) >> 5] >> (np.arange(want.size) & 31)) & 1
+    assert np.array_equal(got.astype(bool), want)
+    assert abs(chunk_pct - 100 * want.mean()) < 1e-3
+    assert abs(line_pct - 100 * want.reshape(-1, 8).any(1).mean()) < 1e-3
+    start = n - 8192   # the all-zero last pair: its chunks are all clean
+    assert want[-(-start // 8):].sum() == 0
