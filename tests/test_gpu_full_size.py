@@ -7,12 +7,21 @@ in-place decompress (`DecompressBatch`).
   compared with the oracle's.
 - 7B-shaped checkpoint (291 tensors, 6.7e9 elements): every tensor is compared
   with the oracle, byte for byte.
-- 70B-shaped half model (360 tensors, 3.4e10 elements): the oracle checks the
-  tensors of the first and the last layer byte for byte.  Every tensor is
-  checked by properties that hold at any size: the exact class counts the
-  generator planted, the round trip, and a payload that depends only on the
-  XOR mask (compressing new -> old gives the same bytes).
+- 70B-shaped half model (360 tensors, 3.4e10 elements): every tensor is
+  compared with the oracle, byte for byte.  Every tensor is also checked by
+  properties that hold at any size: the exact class counts the generator
+  planted, the round trip, and a payload that depends only on the XOR mask
+  (compressing new -> old gives the same bytes).
+
+The oracle is single-threaded; the checkpoints' tensors are compared on a
+pool of host threads (the oracle's C calls run without the interpreter lock),
+each tensor copied to the host just before its turn so that only a bounded
+number of tensors is held in host memory at once.
 """
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -49,6 +58,40 @@ def _check_against_oracle(src, dst, payload, result, what):
     assert_same_bytes(payload.cpu().numpy(), ref_payload, what)
 
 
+def _check_all_against_oracle(pairs, comp, res, names, threads=None, in_flight=None):
+    """_check_against_oracle over every tensor, on a thread pool.  The host
+    copies are made on this thread, in order, at most `in_flight` tensors
+    ahead of the comparisons."""
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
+    in_flight = in_flight or 2 * threads
+    gate = threading.Semaphore(in_flight)
+    done = [0]
+    lock = threading.Lock()
+
+    def work(a, b, got, r, what):
+        try:
+            ref_payload, ref_cs, stats = oracle.compress(a, b)
+            assert r["checksum"] == ref_cs, f"{what}: checksum"
+            assert r["n_changed"] == stats["n_changed"] and r["n_rare"] == stats["n_rare"], what
+            assert_same_bytes(got, ref_payload, what)
+            with lock:
+                done[0] += 1
+                if done[0] % 60 == 0:
+                    log(f"  oracle agrees on {done[0]} tensors")
+        finally:
+            gate.release()
+
+    futures = []
+    with ThreadPoolExecutor(threads) as pool:
+        for j, ((s, d), r) in enumerate(zip(pairs, res)):
+            gate.acquire()
+            got = comp.payload(j, r["payload_bytes"]).cpu().numpy()
+            futures.append(pool.submit(work, to_u16(s), to_u16(d), got, r, names[j]))
+        for f in futures:
+            f.result()
+    return done[0]
+
+
 def _apply_in_place_and_compare(pairs, comp, res):
     """Batched decompress into src (in place), then src must equal dst."""
     items = [(s, comp.payload(j, r["payload_bytes"]), r["checksum"])
@@ -80,29 +123,23 @@ def test_config2_7b_checkpoint_every_tensor():
     comp, res = _compress_like_bench(pairs)
     specs = synth.seven_b_specs()
     for j, ((s, d), r) in enumerate(zip(pairs, res)):
-        _check_against_oracle(s, d, comp.payload(j, r["payload_bytes"]), r, specs[j].name)
         k = synth.exact_count("0.02", s.numel())
         _, n_exp, n_sign = synth.class_counts(k)
         assert r["n_changed"] == k and r["n_rare"] == n_exp + n_sign, specs[j].name
-        if j % 50 == 0:
-            log(f"  oracle agrees up to tensor {j}")
+    assert _check_all_against_oracle(pairs, comp, res, [sp.name for sp in specs]) == 291
+    log("  oracle agrees on all 291 tensors")
     _apply_in_place_and_compare(pairs, comp, res)
 
 
-def test_config5_70b_half_model_sampled_and_properties():
+def test_config5_70b_half_model_every_tensor():
     log("case 70B-shaped half model, 360 tensors")
     specs = synth.config5_specs()
     pairs = [(s.reshape(-1), d.reshape(-1)) for _, s, d in synth.config5(DEV)]
     assert len(pairs) == len(specs) == 360
     comp, res = _compress_like_bench(pairs)
     log("  compressed")
-    per_layer = len(specs) // 40
-    sampled = set(range(per_layer)) | set(range(len(specs) - per_layer, len(specs)))
-    for j in sorted(sampled):
-        s, d = pairs[j]
-        _check_against_oracle(s, d, comp.payload(j, res[j]["payload_bytes"]), res[j],
-                              specs[j].name)
-    log(f"  oracle agrees on {len(sampled)} sampled tensors")
+    assert _check_all_against_oracle(pairs, comp, res, [sp.name for sp in specs]) == 360
+    log("  oracle agrees on all 360 tensors")
     for j, ((s, _), r) in enumerate(zip(pairs, res)):
         k = synth.exact_count("0.01", s.numel())
         _, n_exp, n_sign = synth.class_counts(k)

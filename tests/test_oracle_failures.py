@@ -19,6 +19,7 @@ import pytest
 
 import oracle
 from lossless_bf16_weight_xor_amd import synth
+from tests import payload_build as pb
 from tests import payload_view as pv
 
 
@@ -65,6 +66,17 @@ def test_corrupt_header_is_rejected_untouched(case, offset, what):
     p[offset] ^= 0x01
     st, w = _apply(a, p, cs)
     assert st == oracle.EFORMAT and np.array_equal(w, a), what
+
+
+@pytest.mark.parametrize("version", [0, 2, 3, 0xFFFFFFFF])
+def test_unknown_format_version_is_rejected_untouched(case, version):
+    """Only version 1 (this header) and version 2 (with a binding block) are
+    read; anything else is refused before the weights are touched."""
+    a, b, payload, cs = case
+    p = payload.copy()
+    p[8:12] = np.frombuffer(struct.pack("<I", version), np.uint8)
+    st, w = _apply(a, p, cs)
+    assert st == oracle.EFORMAT and np.array_equal(w, a)
 
 
 def test_wrong_n_is_rejected(case):
@@ -117,18 +129,35 @@ def _segment_offsets(payload, n):
 
 @pytest.mark.parametrize("region", ["pos", "mant", "rare"])
 def test_corrupt_record_byte_ends_old(case, region):
-    """A flipped bit inside a record may decode to a malformed block
-    (EFORMAT) or to a well-formed but wrong mask (ECHECKSUM).  In both cases
-    the weights end exactly old."""
+    """A flipped bit inside a record decodes either to a malformed block
+    (EFORMAT) or to a well-formed but different mask (ECHECKSUM: canonical
+    records are a bijection with masks, so a different canonical record is a
+    different mask).  Which one is decided by the test-side record checker,
+    written from the format definition.  In both cases the weights end
+    exactly old.  Every bit of the first, middle and last 8 bytes of the
+    segment is flipped."""
     a, b, payload, cs = case
-    start, pb, mb, rb = _segment_offsets(payload, a.size)
-    where = {"pos": start + pb // 2, "mant": start + pb + mb // 2, "rare": start + pb + mb + 1}[region]
-    for bit in range(8):
-        p = payload.copy()
-        p[where] ^= np.uint8(1 << bit)
-        st, w = _apply(a, p, cs)
-        assert st in (oracle.EFORMAT, oracle.ECHECKSUM)
-        assert np.array_equal(w, a), (region, bit)
+    start, pos_b, mant_b, rare_b = _segment_offsets(payload, a.size)
+    seg0, seg_len = {"pos": (start, pos_b), "mant": (start + pos_b, mant_b),
+                     "rare": (start + pos_b + mant_b, rare_b)}[region]
+    desc = int(pv.descriptors(payload, a.size)[0])
+    L = pv.block_len(a.size, 0)
+    rec_len = pos_b + mant_b + rare_b
+    picks = sorted({*range(8), *range(seg_len // 2 - 4, seg_len // 2 + 4),
+                    *range(seg_len - 8, seg_len)} & set(range(seg_len)))
+    seen = set()
+    for k in picks:
+        for bit in range(8):
+            p = payload.copy()
+            p[seg0 + k] ^= np.uint8(1 << bit)
+            canonical = pb.check_record(bytes(p[start:start + rec_len]), desc, L) is not None
+            want = oracle.ECHECKSUM if canonical else oracle.EFORMAT
+            st, w = _apply(a, p, cs)
+            assert st == want, (region, k, bit, st)
+            assert np.array_equal(w, a), (region, k, bit)
+            seen.add(st)
+    # the checker is not trivially one-sided on this segment
+    assert oracle.EFORMAT in seen or region == "rare"
 
 
 def test_rare_word_without_exponent_or_sign_bits_is_malformed():

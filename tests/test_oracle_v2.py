@@ -229,3 +229,26 @@ def test_compress_v2_rejects_unknown_flags():
     old, new = _pair((100,), "0.1", 25)
     st, _, _ = oracle.compress_v2_raw(old, new, 0, 1, flags=2)
     assert st == oracle.EINVAL
+
+
+def test_overwrite_descriptor_with_a_word_short_is_rejected():
+    """r = c - 1 with the last word dropped and the header totals adjusted to
+    match: every count and length agrees except the rule that an overwrite
+    record holds exactly one word per change (r > c is refused by the
+    general r <= c rule).  It is a descriptor-table error, found before the
+    binding: EFORMAT even for a receiver holding another version, nothing
+    touched."""
+    old, new = _pair((8192,), "0.01", 26)
+    p, cs, _ = oracle.compress_v2(old, new, 1, 2, overwrite=True)
+    d = int(pv.descriptors(p, old.size)[0])
+    c, r, code = pv.split(d)
+    assert r == c
+    q = bytearray(bytes(p)[:-2])                     # one block: its record ends the payload
+    q[96:100] = np.uint32(c | ((c - 1) << 14) | (code << 28)).tobytes()
+    q[32:40] = np.uint64(pv.header(p)["n_rare"] - 1).tobytes()
+    q[56:64] = np.uint64(pv.header(p)["rare_bytes"] - 2).tobytes()
+    q = np.frombuffer(bytes(q), np.uint8)
+    for ver in (99, 1):
+        w = old.copy()
+        assert oracle.decompress_v2_inplace(w, q, cs, ver) == (oracle.EFORMAT, ver)
+        assert np.array_equal(w, old)
