@@ -58,7 +58,9 @@
  *
  * Conventions shared by every entry point:
  *   - The caller owns every buffer.  The library allocates no device memory
- *     and keeps no state between calls.
+ *     and keeps no state between calls; the one exception is the static
+ *     scratch of bf16d_decompress_noalloc, a fixed array in the library's
+ *     device code.
  *   - src, dst, weights, payload and workspace are device pointers and must
  *     be 16-byte aligned.
  *   - `results` must be memory the device can write: device memory, or
@@ -199,6 +201,35 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count,
                         void *workspace, size_t workspace_bytes,
                         bf16d_result *results, hipStream_t stream,
                         const bf16d_events *events);
+
+/* Allocation-free decompress, for callers that cannot allocate device
+ * memory (tight serving loops, harnesses that forbid allocation): the same
+ * call as bf16d_decompress, with the same kernels, statuses, rollback and
+ * argument checks, but its workspace is the library's own scratch instead of
+ * a caller buffer.  The caller still passes the jobs (weights and payloads)
+ * and `results`.
+ *
+ * The scratch is a static device array of BF16D_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU.  Every GPU the library runs on holds its own copy until
+ * the process ends; its address is taken on the first call made on each
+ * device.  A batch fits when its decompress workspace layout does, which
+ * needs at most
+ *   81 bytes per 8192-element block + 224 bytes per job + 8 KiB.
+ * All 291 tensors of a 7B-shaped checkpoint (822,593 blocks) fit in one
+ * call; larger batches must be split (by layer, for example).  A batch that
+ * does not fit returns BF16D_EINVAL with nothing enqueued.
+ *
+ * `stream` must belong to the current device (NULL: the current device's
+ * null stream); otherwise BF16D_EINVAL.  The job table is copied from host
+ * memory before the call returns, as in bf16d_decompress.  Calls share
+ * their GPU's scratch, so two calls that overlap in time on one GPU (for
+ * example on two streams) race and give undefined results; calls in one
+ * stream's order are safe.  Each call clears what it needs cleared, so the
+ * contents left by the previous call do not matter.  This call allocates no
+ * device memory. */
+#define BF16D_NOALLOC_SCRATCH_BYTES (64u << 20)
+int bf16d_decompress_noalloc(const bf16d_decompress_job *jobs, uint32_t count,
+                             bf16d_result *results, hipStream_t stream);
 
 /* Single-tensor forms of the two calls above, named after the pages'
  * delta_compress(src, dst) -> (payload, checksum) and

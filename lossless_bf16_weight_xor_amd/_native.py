@@ -26,7 +26,8 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress"
             "bf16d_status_string", "bf16d_format_version", "bf16d_codec_available",
             "bf16d_race_bound", "bf16d_race_compress", "bf16d_race_frame_info",
             "bf16d_race_decompress", "bf16d_compress_bound", "bf16d_decompress_bound",
-            "bf16d_probe_read", "bf16d_probe_inplace")
+            "bf16d_probe_read", "bf16d_probe_inplace", "bf16d_decompress_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 CODECS = {"stored": 0, "zstd": 1, "lz4": 2, "lz4hc": 3, "zlib": 4, "brotli": 5, "xz": 6}
 RACE_FRAME_HEADER = 32
@@ -154,6 +155,8 @@ def lib():
         L.bf16d_race_frame_info.restype = ctypes.c_int
         L.bf16d_race_decompress.argtypes = [ctypes.POINTER(RaceJob), u32, u32]
         L.bf16d_race_decompress.restype = ctypes.c_int
+        L.bf16d_decompress_noalloc.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, vp]
+        L.bf16d_decompress_noalloc.restype = ctypes.c_int
         L.bf16d_probe_read.argtypes = [vp, vp, u64, vp, u64, vp]
         L.bf16d_probe_read.restype = ctypes.c_int
         L.bf16d_probe_inplace.argtypes = [vp, u64, vp, vp, u64, vp]

@@ -5,6 +5,7 @@
 // Nothing here allocates device memory or keeps state between calls.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "internal.hpp"
@@ -333,6 +334,62 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count, void *
                         const bf16d_events *events) {
     return decompress_call(jobs, nullptr, nullptr, count, workspace, workspace_bytes, results,
                            stream, events);
+}
+
+}  // extern "C"
+
+// ---- allocation-free decompress ------------------------------------------------
+// The library's own scratch for bf16d_decompress_noalloc: one array per GPU
+// (each device that loads the library's code holds its own copy until the
+// process ends).  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[BF16D_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices];   // device address of `scratch` per device, once taken
+
+// The scratch of the current device (which must be `stream`'s device), taken
+// on the first call made on that device.
+int current_scratch(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BF16D_EHIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return BF16D_EHIP;
+        if (sdev != dev) return BF16D_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BF16D_EHIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return BF16D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bf16d_decompress_noalloc(const bf16d_decompress_job *jobs, uint32_t count,
+                             bf16d_result *results, hipStream_t stream) {
+    if (!jobs || count == 0 || !results) return BF16D_EINVAL;
+    // the size check first: a batch the scratch cannot hold touches nothing
+    DecompressPrep prep;
+    const int rc = decompress_prep(jobs, count, prep, nullptr);
+    if (rc != BF16D_OK) return rc;
+    if (make_layout(prep.tiles, prep.dtiles, count, false).total > BF16D_NOALLOC_SCRATCH_BYTES)
+        return BF16D_EINVAL;
+    void *ws = nullptr;
+    const int sc = current_scratch(stream, &ws);
+    if (sc != BF16D_OK) return sc;
+    return decompress_call(jobs, nullptr, nullptr, count, ws, BF16D_NOALLOC_SCRATCH_BYTES,
+                           results, stream, nullptr);
 }
 
 size_t bf16d_workspace_bytes_remapped(uint64_t total_n, uint32_t count, uint64_t total_segments) {
