@@ -376,17 +376,18 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
     workload's pairs, also the in-place floor (bf16d_probe_inplace): the same
     reads of one array plus, written back unchanged, every 16-byte chunk that
     the workload's delta changes."""
+    from lossless_bf16_weight_xor_amd import probe
     a = torch.empty(n, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
     sink = torch.empty(1, dtype=torch.int64, device=dev)
     full = n // 8192 * 8192
     out = {}
     for key, arrays in (("read2", (a, b)), ("read1", (a, None))):
-        bd.probe_read(*arrays, sink=sink)
+        probe.probe_read(*arrays, sink=sink)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         for _ in range(steps):
-            bd.probe_read(*arrays, sink=sink)
+            probe.probe_read(*arrays, sink=sink)
         ev[1].record()
         torch.cuda.synchronize()
         t = ev[0].elapsed_time(ev[1]) / 1e3 / steps
@@ -395,11 +396,11 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
                     "pct_of_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBPS, 2)}
     if pairs is not None:
         dirty, chunk_pct, line_pct = dirty_chunks(pairs, n, dev)
-        bd.probe_inplace(a, dirty, sink=sink)
+        probe.probe_inplace(a, dirty, sink=sink)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         for _ in range(steps):
-            bd.probe_inplace(a, dirty, sink=sink)
+            probe.probe_inplace(a, dirty, sink=sink)
         ev[1].record()
         torch.cuda.synchronize()
         t = ev[0].elapsed_time(ev[1]) / 1e3 / steps

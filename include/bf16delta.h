@@ -522,37 +522,6 @@ int bf16d_race_frame_info(const uint8_t *frame, uint64_t frame_bytes, uint64_t *
  * a NULL array or a NULL pointer with a non-zero size, else BF16D_OK. */
 int bf16d_race_decompress(bf16d_race_job *jobs, uint32_t count, uint32_t threads);
 
-/* ---- measurement aid (not a step of the method) --------------------------
- *
- * Reads the first 8192 * floor(n / 8192) elements of a, and of b unless b is
- * NULL, with the encoder's whole-block access pattern (one workgroup per
- * 8192-element block, 16-byte loads, the blocks split into one contiguous
- * range per XCD as the main kernels take them) and does nothing else, so that
- * its time is the read ceiling of that pattern: the "achievable" figure that
- * kernel times are compared against, beside the published HBM peak.  a and b
- * are device pointers to at least n elements each, 16-byte aligned; sink is 8
- * bytes of device memory, written only when a fold of the data equals key
- * (the store keeps the loads from being removed).  Enqueued on stream.
- * Returns BF16D_EINVAL for a NULL a or sink, a misaligned pointer or more
- * than 2^31 - 1 blocks; BF16D_EHIP if the launch fails; else BF16D_OK. */
-int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink,
-                     uint64_t key, hipStream_t stream);
-
-/* Measurement aid (not a step of the method): the traffic of an in-place
- * apply with nothing else.  Reads the first 8192 * floor(n / 8192) elements
- * of w with the apply pass's whole-block pattern (in the same block order as
- * bf16d_probe_read) and writes back, unchanged, every 16-byte chunk c
- * (elements 8c .. 8c + 7) whose bit (c & 31) of dirty[c >> 5] is set, so
- * that, given the chunks a delta changes, its time is the cost of applying
- * that delta's traffic in place through the simplest kernel (a reference
- * point, not a strict lower bound).  w: device, 16-byte aligned, n elements,
- * left as it was; dirty: device, 4-byte aligned, at least 32 * floor(n /
- * 8192) words; sink as in bf16d_probe_read.  No other work may write w
- * meanwhile.  Returns BF16D_EINVAL for a NULL or misaligned pointer or more
- * than 2^31 - 1 blocks; BF16D_EHIP if the launch fails; else BF16D_OK. */
-int bf16d_probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink,
-                        uint64_t key, hipStream_t stream);
-
 /* Human-readable name of a status code (static storage). */
 const char *bf16d_status_string(int status);
 

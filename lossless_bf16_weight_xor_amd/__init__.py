@@ -34,8 +34,7 @@ __all__ = ["delta_compress", "delta_decompress", "compress_batch", "decompress_b
            "CompressBatch", "DecompressBatch", "StreamedDecompress", "RemappedBatch",
            "decompress_remapped", "race_compress", "race_decompress", "codec_available",
            "RaceFrame", "DEFAULT_RACE", "FormatError", "ChecksumError",
-           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT", "probe_read",
-           "probe_inplace"]
+           "CapacityError", "max_payload_bytes", "workspace_bytes", "FORMAT"]
 
 
 class FormatError(ValueError):
@@ -388,50 +387,18 @@ def decompress_remapped(items) -> list[dict]:
     return batch.results()
 
 
-_PROBE_KEY = 0x9E3779B97F4A7C15   # the probe stores only if its fold equals this
-
-
-def probe_read(a: torch.Tensor, b: torch.Tensor | None = None,
-               sink: torch.Tensor | None = None) -> None:
-    """Measurement aid: read a (and b) with the encoder's access pattern and
-    nothing else, enqueued on the current stream (`bf16d_probe_read`)."""
-    pa = _weights_ptr(a, "a")
-    pb = 0
-    if b is not None:
-        pb = _weights_ptr(b, "b")
-        if b.device != a.device or b.numel() < a.numel():
-            raise ValueError("b must be on a's device and hold at least as many elements")
-    if sink is None:
-        sink = torch.empty(1, dtype=torch.int64, device=a.device)
-    if sink.device != a.device or sink.dtype != torch.int64 or sink.numel() < 1:
-        raise ValueError("sink must be an int64 tensor on a's device")
-    _check_rc(_native.lib().bf16d_probe_read(pa, pb, a.numel(), sink.data_ptr(), _PROBE_KEY,
-                                             _stream(a.device)), "bf16d_probe_read")
-
-
-def probe_inplace(w: torch.Tensor, dirty: torch.Tensor, sink: torch.Tensor | None = None) -> None:
-    """Measurement aid: read w with the apply pass's access pattern and write
-    back, unchanged, each 16-byte chunk that `dirty` marks (one bit per chunk,
-    int32 words, `bf16d_probe_inplace`), enqueued on the current stream."""
-    pw = _weights_ptr(w, "w")
-    if (dirty.device != w.device or dirty.dtype != torch.int32 or not dirty.is_contiguous()
-            or dirty.numel() < 32 * (w.numel() // BLOCK_ELEMS)):
-        raise ValueError("dirty must be a contiguous int32 tensor on w's device with 32 words "
-                         "per 8192-element block")
-    if sink is None:
-        sink = torch.empty(1, dtype=torch.int64, device=w.device)
-    if sink.device != w.device or sink.dtype != torch.int64 or sink.numel() < 1:
-        raise ValueError("sink must be an int64 tensor on w's device")
-    _check_rc(_native.lib().bf16d_probe_inplace(pw, w.numel(), dirty.data_ptr(), sink.data_ptr(),
-                                                _PROBE_KEY, _stream(w.device)),
-              "bf16d_probe_inplace")
+# Below this many bytes of worst-case payload a batch gets worst-case
+# capacities up front, so that it never runs twice; above it, a first guess
+# (1/16 of the weights plus the framing) keeps the arena small, and only the
+# jobs that report a larger size are compressed again.
+_UPFRONT_LIMIT = 256 << 20
 
 
 def _first_capacity(n: int) -> int:
-    """A first guess at the payload size: framing plus 1/8 of the weights.  A
-    denser delta reports its exact size and is encoded again."""
+    """A first guess at the payload size: framing plus 1/16 of the weights
+    (the payload of a delta changing up to about 6 % of the elements)."""
     nb = -(-n // BLOCK_ELEMS)
-    return min(max_payload_bytes(n), HEADER_BYTES + 4 * nb + (2 * n) // 8 + 4096)
+    return min(max_payload_bytes(n), HEADER_BYTES + 4 * nb + (2 * n) // 16 + 4096)
 
 
 def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]], bindings=None):
@@ -439,24 +406,38 @@ def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]], bindings=
     or per pair (base_version, target_version, overwrite) for version-2
     payloads.
 
+    Capacities: the worst case (bf16d_max_payload_bytes) when the whole batch's
+    worst case is below 256 MiB, so small batches always finish in one call;
+    otherwise a first guess of 1/16 of the weights, and the jobs that report
+    ECAPACITY (with their exact size) are compressed again in a second batch
+    of their own.
+
     Returns a list of (payload uint8 tensor, checksum int, stats dict).  The
-    payloads are views into one device arena."""
+    payloads are views into one or two device arenas."""
     extra = BOUND_EXTRA_BYTES if bindings is not None else 0
-    caps = [_first_capacity(s.numel()) + extra for s, _ in pairs]
+    worst = [max_payload_bytes(s.numel()) + extra for s, _ in pairs]
+    if sum(worst) <= _UPFRONT_LIMIT:
+        caps = worst
+    else:
+        caps = [_first_capacity(s.numel()) + extra for s, _ in pairs]
     batch = CompressBatch(pairs, caps, bindings)
     batch.run()
     res = batch.results()
+    where = [(batch, j) for j in range(len(pairs))]
     short = [j for j, r in enumerate(res) if r["status"] == ECAPACITY]
     if short:
-        caps = [res[j]["payload_bytes"] if j in short else caps[j] for j in range(len(pairs))]
-        batch = CompressBatch(pairs, caps, bindings)
-        batch.run()
-        res = batch.results()
+        again = CompressBatch([pairs[j] for j in short], [res[j]["payload_bytes"] for j in short],
+                              None if bindings is None else [bindings[j] for j in short])
+        again.run()
+        for k, (j, r) in enumerate(zip(short, again.results())):
+            res[j] = r
+            where[j] = (again, k)
     out = []
     for j, r in enumerate(res):
         if r["status"] != OK:
             raise RuntimeError(f"job {j}: {_native.status_string(r['status'])}")
-        out.append((batch.payload(j, r["payload_bytes"]), r["checksum"], r))
+        b, k = where[j]
+        out.append((b.payload(k, r["payload_bytes"]), r["checksum"], r))
     return out
 
 

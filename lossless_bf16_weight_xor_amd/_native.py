@@ -26,7 +26,10 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress"
             "bf16d_status_string", "bf16d_format_version", "bf16d_codec_available",
             "bf16d_race_bound", "bf16d_race_compress", "bf16d_race_frame_info",
             "bf16d_race_decompress", "bf16d_compress_bound", "bf16d_decompress_bound",
-            "bf16d_probe_read", "bf16d_probe_inplace", "bf16d_decompress_noalloc")
+            "bf16d_decompress_noalloc")
+# the benchmark's measurement aids, in their own library (bf16delta_probe.h)
+PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta_probe.so")
+PROBE_EXPORTED = ("bf16d_probe_read", "bf16d_probe_inplace")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 CODECS = {"stored": 0, "zstd": 1, "lz4": 2, "lz4hc": 3, "zlib": 4, "brotli": 5, "xz": 6}
@@ -157,12 +160,28 @@ def lib():
         L.bf16d_race_decompress.restype = ctypes.c_int
         L.bf16d_decompress_noalloc.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, vp]
         L.bf16d_decompress_noalloc.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+_probe_lib = None
+
+
+def probe_lib():
+    """The benchmark's measurement-aid library (bf16delta_probe.h)."""
+    global _probe_lib
+    if _probe_lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise LibraryMissing(
+                f"{PROBE_LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        u64, vp = ctypes.c_uint64, ctypes.c_void_p
         L.bf16d_probe_read.argtypes = [vp, vp, u64, vp, u64, vp]
         L.bf16d_probe_read.restype = ctypes.c_int
         L.bf16d_probe_inplace.argtypes = [vp, u64, vp, vp, u64, vp]
         L.bf16d_probe_inplace.restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _probe_lib = L
+    return _probe_lib
 
 
 def status_string(code: int) -> str:

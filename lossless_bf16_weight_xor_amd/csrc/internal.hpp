@@ -215,7 +215,11 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
     return z;
 }
 
-__device__ __forceinline__ uint64_t ld_acquire_agent(const uint64_t *p) {
+// Relaxed device-scope loads and stores.  They order nothing: a reader only
+// relies on the single word it reads.  The look-back status words carry
+// their flag and their value in one 64-bit word for exactly that reason (a
+// reader that sees the flag sees the value that came with it).
+__device__ __forceinline__ uint64_t ld_relaxed_agent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
@@ -240,9 +244,24 @@ __device__ __forceinline__ uint64_t xcd_tile(uint64_t b, uint64_t tiles) {
 // last workgroup reads with device-scope loads.  `dep` is the XOR of the
 // values the calling thread's atomics returned (0 in threads that made
 // none): the count waits for them to come back, so they are done before the
-// last workgroup can look.  No fence is used: on this chip a device-scope
-// fence writes back and invalidates the XCD's whole L2, for every workgroup.
-// Every thread must call it (it contains barriers).
+// last workgroup can look.  Every thread must call it (it contains barriers).
+//
+// Why this is safe without a fence.  The ordering comes from the hardware,
+// not from the HIP memory model: with relaxed atomics only, the model itself
+// would not order the sums before the count (that would take a release on
+// the count and an acquire in the last workgroup).  On gfx950 a
+// device-scope atomic is performed at the device's coherence point, and a
+// returning atomic has been performed there once its value is back in a
+// register.  The asm below makes the count's increment depend on those
+// values, so every sum this workgroup adds is at the coherence point before
+// its increment is issued.  The last workgroup's loads are device-scope
+// (they read the coherence point, not a stale L2 line) and are issued after
+// its own increment returned the final count, i.e. after every other
+// workgroup's increment, and so after every sum.  Only atomics cross
+// workgroups here; plain stores would need a real release.  The fence this
+// avoids is not free on this chip: a device-scope release writes back the
+// XCD's L2 and an acquire invalidates it, in every workgroup (0.14 ms per
+// call on the 7B-shaped decompress, measured).
 __device__ __forceinline__ bool last_workgroup(uint32_t *done, uint64_t dep) {
     __shared__ bool s_last;
     asm volatile("" ::"v"(dep) : "memory");
@@ -391,7 +410,7 @@ __device__ __forceinline__ uint64_t look_back(uint64_t *status, uint64_t tile, u
 #pragma unroll
         for (int k = 0; k < kLookDepth; ++k) {
             const int64_t idx = pred - lane - 64 * k;   // distance 1 + lane + 64k
-            v[k] = idx >= (int64_t)first ? ld_acquire_agent(&status[idx]) : kFlagPrefix;
+            v[k] = idx >= (int64_t)first ? ld_relaxed_agent(&status[idx]) : kFlagPrefix;
         }
         // wait only for the entries nearer than the nearest inclusive prefix
         // seen so far; re-pick that prefix after every reload
@@ -417,7 +436,7 @@ __device__ __forceinline__ uint64_t look_back(uint64_t *status, uint64_t tile, u
             for (int k = 0; k < kLookDepth; ++k) {
                 const int64_t idx = pred - lane - 64 * k;
                 if ((k < stop_k || (k == stop_k && lane < stop_lane)) && (v[k] >> 62) == 0)
-                    v[k] = ld_acquire_agent(&status[idx]);
+                    v[k] = ld_relaxed_agent(&status[idx]);
             }
         }
         uint64_t mine = 0;

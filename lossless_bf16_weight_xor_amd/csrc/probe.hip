@@ -18,6 +18,7 @@
 // timing of the writes change their cost.  The published HBM peak stays the
 // roofline of both.
 #include "internal.hpp"
+#include "bf16delta_probe.h"
 
 namespace bf16d {
 

@@ -14,6 +14,7 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bf16delta.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "bf16delta_probe.h")
 
 
 @pytest.fixture(scope="module")
@@ -25,8 +26,8 @@ def native():
     return _native
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bf16d_[a-z_]+)\s*\(", text)))
 
@@ -42,6 +43,20 @@ def test_every_declared_symbol_is_exported(native):
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(native.EXPORTED) == set(_declared_functions())
+
+
+def test_the_measurement_aids_live_in_their_own_library(native):
+    """The probes are declared in bf16delta_probe.h and exported by
+    libbf16delta_probe.so only, not by the product library."""
+    probe = ctypes.CDLL(native.PROBE_LIB_PATH)
+    names = _declared_functions(PROBE_HEADER)
+    assert set(names) == set(native.PROBE_EXPORTED) == {"bf16d_probe_read", "bf16d_probe_inplace"}
+    product = ctypes.CDLL(native.LIB_PATH)
+    for name in names:
+        assert hasattr(probe, name), name
+        assert not hasattr(product, name), name
+    assert all(os.path.exists(p) for p in (HEADER, PROBE_HEADER))
+    assert set(names).isdisjoint(_declared_functions())
 
 
 def test_no_kernel_takes_an_address_space_qualified_parameter():

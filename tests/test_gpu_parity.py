@@ -192,6 +192,24 @@ def test_thousands_of_tiny_jobs_in_one_call():
         assert torch.equal(w.view(torch.int16), dst.view(torch.int16)), j
 
 
+def test_compress_batch_compresses_again_only_the_dense_jobs():
+    """A batch whose worst case passes 256 MiB starts from a first guess of
+    1/16 of the weights; the dense job that does not fit is compressed again
+    on its own (its payload lands in a second arena), the sparse ones are
+    not, and every payload is the oracle's."""
+    log("case first-guess capacities with one dense job")
+    pairs = [pair((32 * 2 ** 20,), "0.01", synth.MIX_DEFAULT, 41, DEV),
+             pair((64 * 2 ** 20,), "0.3", synth.MIX_DEFAULT, 42, DEV),
+             pair((8192 * 3 + 5,), "0.02", synth.MIX_DEFAULT, 43, DEV)]
+    out = compress_batch(pairs)
+    arenas = [p.untyped_storage().data_ptr() for p, _, _ in out]
+    assert arenas[0] == arenas[2] != arenas[1]
+    for j, ((src, dst), (payload, cs, _)) in enumerate(zip(pairs, out)):
+        ref_payload, ref_cs, _ = oracle_of(src, dst)
+        assert cs == ref_cs, j
+        assert_same_bytes(payload_np(payload), ref_payload, f"job {j}")
+
+
 def test_capacity_too_small_reports_the_exact_size():
     src, dst = pair((5 * 8192,), "0.3", synth.MIX_DEFAULT, 9, DEV)
     ref_payload, _, _ = oracle_of(src, dst)

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import lossless_bf16_weight_xor_amd as bd
-from lossless_bf16_weight_xor_amd import _native
+from lossless_bf16_weight_xor_amd import _native, probe
 
 pytestmark = pytest.mark.gpu
 
@@ -17,9 +17,9 @@ def test_probe_runs_over_one_and_two_arrays():
     a = torch.randint(-32768, 32767, (3 * 8192 + 5,), dtype=torch.int16, device=dev)
     b = torch.randint(-32768, 32767, a.shape, dtype=torch.int16, device=dev)
     sink = torch.zeros(1, dtype=torch.int64, device=dev)
-    bd.probe_read(a, b, sink=sink)
-    bd.probe_read(a, None, sink=sink)
-    bd.probe_read(a[:100], None, sink=sink)   # no whole block: nothing launched
+    probe.probe_read(a, b, sink=sink)
+    probe.probe_read(a, None, sink=sink)
+    probe.probe_read(a[:100], None, sink=sink)   # no whole block: nothing launched
     torch.cuda.synchronize()
 
 
@@ -27,7 +27,7 @@ def test_probe_refuses_bad_arguments():
     dev = torch.device("cuda:0")
     a = torch.zeros(8192 * 2, dtype=torch.int16, device=dev)
     sink = torch.zeros(1, dtype=torch.int64, device=dev)
-    L = _native.lib()
+    L = _native.probe_lib()
     s = torch.cuda.current_stream().cuda_stream
     assert L.bf16d_probe_read(0, 0, 8192, sink.data_ptr(), 1, s) == bd.EINVAL
     assert L.bf16d_probe_read(a.data_ptr(), 0, 8192, 0, 1, s) == bd.EINVAL
@@ -36,7 +36,7 @@ def test_probe_refuses_bad_arguments():
                               s) == bd.EINVAL
     assert L.bf16d_probe_read(a.data_ptr(), 0, 0, sink.data_ptr(), 1, s) == bd.OK
     with pytest.raises(ValueError):
-        bd.probe_read(a, a[:8192], sink=sink)   # b shorter than a
+        probe.probe_read(a, a[:8192], sink=sink)   # b shorter than a
     torch.cuda.synchronize()
 
 
@@ -54,9 +54,9 @@ def test_inplace_probe_leaves_the_array_as_it_was():
                                generator=g)
     dirty[32:64] = -1   # every chunk of the second block
     sink = torch.full((1,), 7, dtype=torch.int64, device=dev)
-    bd.probe_inplace(w, dirty, sink=sink)
-    bd.probe_inplace(w, dirty, sink=sink)
-    bd.probe_inplace(w[:100], dirty, sink=sink)   # no whole block: nothing launched
+    probe.probe_inplace(w, dirty, sink=sink)
+    probe.probe_inplace(w, dirty, sink=sink)
+    probe.probe_inplace(w[:100], dirty, sink=sink)   # no whole block: nothing launched
     torch.cuda.synchronize()
     assert torch.equal(w, before)
     assert sink.item() == 7
@@ -67,7 +67,7 @@ def test_inplace_probe_refuses_bad_arguments():
     w = torch.zeros(8192 * 2, dtype=torch.int16, device=dev)
     dirty = torch.zeros(64, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int64, device=dev)
-    L = _native.lib()
+    L = _native.probe_lib()
     s = torch.cuda.current_stream().cuda_stream
     pw, pd, ps = w.data_ptr(), dirty.data_ptr(), sink.data_ptr()
     assert L.bf16d_probe_inplace(0, 8192, pd, ps, 1, s) == bd.EINVAL
@@ -78,7 +78,7 @@ def test_inplace_probe_refuses_bad_arguments():
     assert L.bf16d_probe_inplace(pw, 8192, pd, ps + 4, 1, s) == bd.EINVAL
     assert L.bf16d_probe_inplace(pw, 0, pd, ps, 1, s) == bd.OK
     with pytest.raises(ValueError):
-        bd.probe_inplace(w, dirty[:63], sink=sink)   # fewer than 32 words per block
+        probe.probe_inplace(w, dirty[:63], sink=sink)   # fewer than 32 words per block
     with pytest.raises(ValueError):
-        bd.probe_inplace(w, dirty.view(torch.int16), sink=sink)
+        probe.probe_inplace(w, dirty.view(torch.int16), sink=sink)
     torch.cuda.synchronize()
