@@ -21,6 +21,12 @@ Reported:
   decompress: GB/s of weights, and % of HBM peak on algorithmic bytes (2n + P + 2c)
   roofline  : the encode kernel (the dominant kernel of a step) against 8 TB/s,
               timed with events recorded around it on its stream
+  roofline_decompress : the apply kernel the same way, and on its effective
+              bytes: 2n + P + every 32-byte sector that holds a change (the
+              device writes sectors, not the changed elements alone)
+  change_rate_sweep : compress and decompress of one 1 GiB tensor at 0.085,
+              1, 3 and 5 % uniform changes, with their main kernels'
+              fractions of 8 TB/s
   achievable: the read ceiling of the encoder's access pattern (a probe
               kernel that only reads), over old and new and over old alone,
               and each main kernel's fraction of it; and the in-place floor
@@ -35,8 +41,10 @@ Reported:
               and the payload % of the weights after it
   streamed_receiver : the same decompress with the payloads in pinned host
               memory, copied in layer by layer while earlier layers are
-              applied, through a ring of three device slots with the copies
-              on two streams (and two slots on one stream, for comparison);
+              applied, through a ring of five device slots with the copies
+              on two streams and the applies on two compute lanes (and with
+              three slots and one lane, and two slots on one stream, for
+              comparison);
               PCIe-inclusive, context, not `value`
   cpu_baseline : the CPU oracle on a bounded sample of the same workload
 
@@ -149,7 +157,7 @@ def layer_groups(names, layers_per_group=1):
 
 
 def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_group, slots,
-             copies):
+             copies, lanes):
     """The streamed receiver: payloads in pinned host memory, applied layer by
     layer through a ring of `slots` device slots while the next layers'
     payloads are copied in.  Reported next to the device-resident numbers,
@@ -159,7 +167,7 @@ def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_g
     groups = layer_groups(names, layers_per_group)
     recv = [s.clone() for s, _ in pairs]
     sd = bd.StreamedDecompress(list(zip(recv, host, cs_new)), groups, slots=slots,
-                               copy_streams=copies)
+                               copy_streams=copies, lanes=lanes)
     # the host-to-device copy of every payload byte on its own
     P = sum(h.numel() for h in host)
     flat = torch.empty(P, dtype=torch.uint8).pin_memory()
@@ -196,7 +204,7 @@ def streamed(bd, names, pairs, payloads, cs_new, cs_old, steps, td, layers_per_g
     slot = sd.slot_bytes
     del recv, sd, dbuf
     return {"layers_per_group": layers_per_group, "groups": len(groups), "slots": slots,
-            "copy_streams": copies,
+            "copy_streams": copies, "lanes": lanes,
             "slot_bytes": slot,
             "ms": round(1e3 * ts, 4),
             "gbps_weights_pcie_inclusive": round(2 * n / ts / 1e9, 2),
@@ -413,6 +421,91 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
     return out
 
 
+def dirty_write_units(pairs):
+    """(32-byte sectors, 128-byte lines) that hold at least one changed
+    element, counted per tensor from its start (tensors start on 256-byte
+    boundaries, so these are the device's sectors and lines)."""
+    sectors = lines = 0
+    for src, dst in pairs:
+        d = src.reshape(-1).view(torch.int16) != dst.reshape(-1).view(torch.int16)
+        m = d.numel()
+        pad = (-m) % 64
+        if pad:
+            d = torch.cat([d, torch.zeros(pad, dtype=torch.bool, device=d.device)])
+        sectors += int(d.view(-1, 16).any(1).sum().item())
+        lines += int(d.view(-1, 64).any(1).sum().item())
+    return sectors, lines
+
+
+def change_rate_sweep(bd, dev, steps):
+    """Compress and verified in-place decompress of one 1 GiB tensor
+    (536,870,912 elements, uniform changes, 95/4.5/0.5) at each change rate
+    of the sweep, timed like the main step: whole calls and their main
+    kernels, with events on the call's stream.  Each rate's payload is the
+    same bytes twice over the timed calls (checked), and the receiver ends
+    bit-exact."""
+    from lossless_bf16_weight_xor_amd import synth
+    out = []
+    for rate in synth.C3_RATES:
+        src, dst = synth.config3(dev, rate)
+        n = src.numel()
+        comp = bd.CompressBatch([(src, dst)], [bd._first_capacity(n)])
+        comp.run()
+        r = comp.results()[0]
+        assert r["status"] == bd.OK, f"sweep {rate}: compress {r['status']}"
+        P, c = r["payload_bytes"], r["n_changed"]
+        payload = comp.payload(0, P)
+        ref = payload.clone()
+        rev = bd.CompressBatch([(dst, src)], [P])
+        rev.run()
+        cs_old, cs_new = rev.results()[0]["checksum"], r["checksum"]
+        del rev
+        recv = src.clone()
+        dec = bd.DecompressBatch([(recv, payload, cs_new)])
+        tc, te, td, ta = [], [], [], []
+        direction = 0
+        for i in range(steps + 2):
+            dec.jobs[0].checksum = cs_new if direction == 0 else cs_old
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            e[0].record()
+            comp.run(events=(e[1], e[2]))
+            e[3].record()
+            dec.run(events=(e[4], e[5]))
+            e[6].record()
+            torch.cuda.synchronize()
+            assert dec.results()[0]["status"] == bd.OK, f"sweep {rate}: decompress"
+            direction ^= 1
+            if i >= 2:
+                tc.append(e[0].elapsed_time(e[3]) / 1e3)
+                te.append(e[1].elapsed_time(e[2]) / 1e3)
+                td.append(e[3].elapsed_time(e[6]) / 1e3)
+                ta.append(e[4].elapsed_time(e[5]) / 1e3)
+        assert torch.equal(payload, ref), f"sweep {rate}: payload changed between calls"
+        want = dst if direction == 1 else src
+        assert torch.equal(recv.view(torch.int16), want.view(torch.int16)), f"sweep {rate}"
+        sectors, lines = dirty_write_units([(src, dst)])
+        ca, da = 4 * n + P, 2 * n + P + 2 * c
+        tc_, te_, td_, ta_ = (float(np.mean(x)) for x in (tc, te, td, ta))
+        out.append({
+            "rate": rate, "elements": n, "payload_pct_of_orig": round(100 * P / (2 * n), 4),
+            "compress_ms": round(1e3 * tc_, 4),
+            "compress_hbm_pct": round(100 * ca / tc_ / 1e9 / HBM_PEAK_GBPS, 2),
+            "encode_kernel_ms": round(1e3 * te_, 4),
+            "encode_kernel_frac": round(ca / te_ / 1e9 / HBM_PEAK_GBPS, 4),
+            "decompress_ms": round(1e3 * td_, 4),
+            "decompress_hbm_pct": round(100 * da / td_ / 1e9 / HBM_PEAK_GBPS, 2),
+            "apply_kernel_ms": round(1e3 * ta_, 4),
+            "apply_kernel_frac": round(da / ta_ / 1e9 / HBM_PEAK_GBPS, 4),
+            "dirty_sectors_pct": round(100 * sectors / (n / 16), 3),
+            "dirty_lines_pct": round(100 * lines / (n / 64), 3)})
+        log(f"sweep {rate}: compress {out[-1]['compress_ms']} ms "
+            f"({out[-1]['compress_hbm_pct']}%), decompress {out[-1]['decompress_ms']} ms "
+            f"({out[-1]['decompress_hbm_pct']}%)")
+        del comp, dec, recv, payload, ref, src, dst
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(pairs, gpu_payloads, budget_s: float):
     """The CPU oracle, single-threaded, timed on a bounded sample of the
     workload's tensors, walking from the last tensor back.  Each oracle
@@ -498,6 +591,8 @@ def main():
                     help="CPU threads of the codec race (capped at the host's cores)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the read-ceiling probe (bf16d_probe_read)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the change-rate sweep (one 1 GiB tensor at 0.085/1/3/5 %%)")
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -517,7 +612,7 @@ def main():
     n_total = sum(s.numel() for s, _ in pairs)
     log(f"generated {len(pairs)} tensors, {n_total} elements in {time.time() - t0:.1f}s")
 
-    # payload capacity: framing + 1/8 of the weights, exact size on overflow
+    # payload capacity: framing + 1/16 of the weights, exact size on overflow
     caps = [bd._first_capacity(s.numel()) for s, _ in pairs]
     comp = bd.CompressBatch(pairs, caps)
     comp.run()
@@ -602,6 +697,11 @@ def main():
     dec_alg = 2 * n_total + payload_total + 2 * n_changed
     value = w_bytes / (elapsed / args.steps) / 1e9
 
+    # the decompress's write traffic at the device's granularity: every
+    # 32-byte sector (and 128-byte line) holding a change is written
+    dirty_sectors, dirty_lines = dirty_write_units(pairs)
+    dec_eff = 2 * n_total + payload_total + 32 * dirty_sectors
+
     if args.with_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -649,10 +749,11 @@ def main():
         # 1.6-2.7x) is measured again after 15 s, at most twice; every attempt
         # is reported.
         stream_info = []
-        for lpg, slots, copies in ((1, 3, 2), (4, 3, 2), (1, 2, 1)):
+        for lpg, slots, copies, lanes in ((1, 5, 2, 2), (1, 3, 2, 1), (1, 2, 1, 1)):
             tries = []
             for attempt in range(3):
-                r = streamed(bd, names, pairs, payloads, cs_new, cs_old, 5, td, lpg, slots, copies)
+                r = streamed(bd, names, pairs, payloads, cs_new, cs_old, 5, td, lpg, slots, copies,
+                             lanes)
                 tries.append(r["ms"])
                 if r["ms"] <= 1.35 * r["h2d_payload_ms"] or attempt == 2:
                     break
@@ -662,8 +763,13 @@ def main():
             r["attempts_ms"] = tries
             stream_info.append(r)
 
-    # last of the GPU measurements: it frees two checkpoint-sized buffers, and
-    # a large free slows the streamed receiver's copies for some seconds
+    # after the streamed receiver: the sweep frees its buffers, and a large
+    # free slows the streamed receiver's copies for some seconds
+    sweep = None
+    if not args.no_sweep and args.workload == "7b":
+        sweep = change_rate_sweep(bd, dev, 5)
+
+    # last of the GPU measurements: it frees two checkpoint-sized buffers
     ceiling = None
     if not args.no_probe:
         ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2),
@@ -705,6 +811,12 @@ def main():
         "config": {"workload": desc, "tensors": len(pairs), "elements": n_total,
                    "weights_bytes": w_bytes, "parallelism": "single GPU"},
         "compress": {"gbps_weights": round(w_bytes / tc / 1e9, 2),
+                     # device memory beside the inputs: the call's workspace
+                     # and the payload arena (first-guess capacities)
+                     "workspace_bytes": comp.ws_bytes,
+                     "workspace_pct_of_weights": round(100 * comp.ws_bytes / w_bytes, 3),
+                     "arena_bytes": comp.arena.numel(),
+                     "arena_pct_of_weights": round(100 * comp.arena.numel() / w_bytes, 3),
                      "hbm_pct": round(100 * comp_alg / tc / 1e9 / HBM_PEAK_GBPS, 2),
                      "ms": round(1e3 * tc, 4),
                      "ms_median": round(1e3 * float(np.median(durations(0, 3))), 4),
@@ -712,6 +824,7 @@ def main():
                      "encode_kernel_ms": round(1e3 * t_enc, 4),
                      "algorithmic_bytes": comp_alg},
         "decompress": {"gbps_weights": round(w_bytes / td / 1e9, 2),
+                       "workspace_bytes": dec.ws_bytes,
                        "hbm_pct": round(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS, 2),
                        "ms": round(1e3 * td, 4),
                        "ms_median": round(1e3 * float(np.median(durations(3, 6))), 4),
@@ -730,7 +843,18 @@ def main():
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(dec_alg / t_app / 1e9 / HBM_PEAK_GBPS, 4),
                                 "traffic": measured_traffic(n_total, APPLY_TRAFFIC_PROFILE,
-                                                            APPLY_SOURCES)},
+                                                            APPLY_SOURCES),
+                                # 2n + P + every 32-byte sector holding a change:
+                                # the writes at the granularity the device moves
+                                "effective_bytes": dec_eff,
+                                "effective_achieved": round(dec_eff / t_app / 1e9, 2),
+                                "effective_frac": round(dec_eff / t_app / 1e9 / HBM_PEAK_GBPS, 4),
+                                "dirty_sectors_pct": round(100 * dirty_sectors * 16 / n_total, 3),
+                                "dirty_lines_pct": round(100 * dirty_lines * 64 / n_total, 3),
+                                "target_pct": 60.0,
+                                "target_met": bool(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS
+                                                   >= 60.0)},
+        "change_rate_sweep": sweep,
         "achievable": ceiling,
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,

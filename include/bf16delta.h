@@ -396,8 +396,9 @@ typedef struct bf16d_stream_job {
  *                  boundary; every group must fit.  The copy of group g
  *                  waits for the apply of group g - slots.
  *   workspace    : device, 16-byte aligned, at least
- *                  bf16d_workspace_bytes(sum of n, count) bytes; one
- *                  workspace serves every group, in stream order.
+ *                  bf16d_workspace_bytes(sum of n, count) bytes (enough
+ *                  with or without the extra lane); one workspace serves
+ *                  every group, each lane's groups in its stream order.
  *   results      : results[j] for job j, as in bf16d_decompress.
  *   compute      : stream of the applies; the call's work on the copy streams
  *                  starts only after the work enqueued on `compute` before
@@ -409,7 +410,17 @@ typedef struct bf16d_stream_job {
  *                  (about 10 us, more with the event that follows it), which
  *                  two streams hide behind each other's transfers.  A copy
  *                  stream may equal `compute` (that makes the pipeline
- *                  serial).  All streams must be of the same device.
+ *                  serial).
+ *   lanes        : n_lanes (0 or 1) more compute streams (host array; NULL
+ *                  when n_lanes is 0).  Group g's apply runs on `compute`
+ *                  when g % (1 + n_lanes) == 0, else on lanes[g % (1 +
+ *                  n_lanes) - 1], each lane with a workspace region of its
+ *                  own, so that one group's short set-up and check kernels
+ *                  overlap another group's apply.  The lanes start after the
+ *                  work enqueued on `compute` before the call, and `compute`
+ *                  waits for them at its end.  A lane should be a stream of
+ *                  its own (neither `compute` nor a copy stream).
+ *                  All streams must be of the same device.
  * Consecutive payloads of a group that lie in host memory exactly as they are
  * packed in the slot (each at the next 16-byte boundary after the previous
  * one) are copied with a single transfer, padding included.
@@ -421,7 +432,8 @@ int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t count,
                               void *staging, size_t slot_bytes, uint32_t slots,
                               void *workspace, size_t workspace_bytes,
                               bf16d_result *results, hipStream_t compute,
-                              const hipStream_t *copy, uint32_t copy_streams);
+                              const hipStream_t *copy, uint32_t copy_streams,
+                              const hipStream_t *lanes, uint32_t n_lanes);
 
 /* Codec race (host only): general-purpose compression of payloads.
  *

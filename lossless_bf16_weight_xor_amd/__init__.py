@@ -244,28 +244,57 @@ class DecompressBatch:
         return _results(self.result_buf, self.count)
 
 
+# The streamed receiver's copy and compute-lane streams, created once per
+# device and shared by every StreamedDecompress: HIP spreads streams over a
+# few hardware queues (4 by default), and streams that share a queue run one
+# after the other, so each receiver creating streams of its own would soon
+# put its copies and its applies on one queue.
+_side_streams: dict = {}
+
+
+def _streams(device: torch.device, kind: str, count: int) -> list:
+    key = (device.index, kind)
+    have = _side_streams.setdefault(key, [])
+    while len(have) < count:
+        have.append(torch.cuda.Stream(device=device))
+    return have[:count]
+
+
 class StreamedDecompress:
     """A prepared streamed receiver (bf16d_decompress_streamed): payloads in
     pinned host memory, applied in place group by group through a ring of
-    device slots, the copies on a stream of their own.
+    device slots, the copies on streams of their own.  The copy and lane
+    streams are shared by every receiver on a device, so calls of different
+    receivers must not overlap in time.
 
     items  : (weights device tensor, payload host uint8 tensor, checksum);
              pin the payloads (torch's pin_memory) for the copies to overlap.
     groups : number of jobs in each group, in order (for a model, a layer).
     slots  : device slots in the ring (2 to 64); with 3 the copies do not
-             wait on the apply just before them.
+             wait on the apply just before them, and with 5 (the default)
+             they almost never wait (7B-shaped checkpoint, one layer per
+             group: 1.04x the plain copy of the payloads, against 1.05x with
+             4 slots and 1.11x with 3).
     copy_streams : streams the groups' copies alternate over (1 to 8); with
              2 each transfer's fixed cost hides behind the other's transfer.
+             More than 2 beside two lanes exceeds HIP's 4 hardware queues by
+             default, and streams that share a queue serialise (3 measured
+             1.5x slower).
+    lanes  : compute streams the groups' applies alternate over (1 or 2):
+             the current stream, and with 2 one more, so that a group's
+             short kernels overlap the previous group's apply.
     The device slots are sized for the largest group."""
 
     def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
-                 groups: Sequence[int], slots: int = 3, copy_streams: int = 2):
+                 groups: Sequence[int], slots: int = 5, copy_streams: int = 2, lanes: int = 2):
         if not items or not groups or sum(groups) != len(items) or min(groups) <= 0:
             raise ValueError("groups must be positive and cover every item")
         if not 2 <= slots <= 64:
             raise ValueError("slots must be between 2 and 64")
         if not 1 <= copy_streams <= 8:
             raise ValueError("copy_streams must be between 1 and 8")
+        if lanes not in (1, 2):
+            raise ValueError("lanes must be 1 or 2")
         self.slots = slots
         self.device = items[0][0].device
         self.count = len(items)
@@ -292,8 +321,11 @@ class StreamedDecompress:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
                                       device=self.device)
-        self.copy_streams = [torch.cuda.Stream(device=self.device) for _ in range(copy_streams)]
+        self.copy_streams = _streams(self.device, "copy", copy_streams)
         self._copy = (ctypes.c_void_p * copy_streams)(*[c.cuda_stream for c in self.copy_streams])
+        self.lane_streams = _streams(self.device, "lane", lanes - 1)
+        self._lanes = (ctypes.c_void_p * max(1, lanes - 1))(
+            *[c.cuda_stream for c in self.lane_streams])
 
     @staticmethod
     def pin_packed(payloads: Sequence[torch.Tensor]) -> list[torch.Tensor]:
@@ -316,7 +348,8 @@ class StreamedDecompress:
         rc = _native.lib().bf16d_decompress_streamed(
             self.jobs, self.count, self.group_end, self.groups, self.staging.data_ptr(),
             self.slot_bytes, self.slots, self.workspace.data_ptr(), self.ws_bytes,
-            self.result_buf.data_ptr(), _stream(self.device), self._copy, len(self.copy_streams))
+            self.result_buf.data_ptr(), _stream(self.device), self._copy, len(self.copy_streams),
+            self._lanes if self.lane_streams else None, len(self.lane_streams))
         _check_rc(rc, "bf16d_decompress_streamed")
 
     def results(self) -> list[dict]:

@@ -124,7 +124,8 @@ def lib():
         L.bf16d_decompress_ex.restype = ctypes.c_int
         L.bf16d_decompress_streamed.argtypes = [ctypes.POINTER(StreamJob), u32,
                                                 ctypes.POINTER(ctypes.c_uint32), u32, vp, sz, u32,
-                                                vp, sz, vp, vp, ctypes.POINTER(vp), u32]
+                                                vp, sz, vp, vp, ctypes.POINTER(vp), u32,
+                                                ctypes.POINTER(vp), u32]
         L.bf16d_decompress_streamed.restype = ctypes.c_int
         L.bf16d_decompress_remapped.argtypes = [ctypes.POINTER(DecompressJob),
                                                 ctypes.POINTER(Remap), u32, vp, sz, vp, vp]

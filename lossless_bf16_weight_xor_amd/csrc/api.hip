@@ -215,9 +215,11 @@ size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
     const uint64_t tiles = blocks_of(total_n) + count;
     const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
     const size_t c = make_layout(tiles, dtiles, count, true).total;
-    // decompress; the streamed form also keeps every group's job table (at
-    // most 1024 bytes per job with alignment) after the decompress layout
-    const size_t d = make_layout(tiles, dtiles, count, false).total + 256 + 1024 * size_t(count);
+    // decompress; the streamed form keeps a decompress layout per compute
+    // lane (at most two), then every group's job table (at most 1024 bytes per
+    // job with alignment)
+    const size_t d = 2 * make_layout(tiles, dtiles, count, false).total + 512 +
+                     1024 * size_t(count);
     return c > d ? c : d;
 }
 

@@ -13,6 +13,14 @@
 // 18 us with the event after it); the groups' copies alternate over the
 // caller's copy streams, so one engine's set-up overlaps another's
 // transfer.  Everything is validated before any work is enqueued.
+//
+// Each group's apply is a whole batched decompress call (six launches: the
+// set-up, descriptor scan and plan before the apply kernel, the checksum sum
+// and fix-up after it).  On one compute stream those short kernels add up
+// to a third of the apply time and keep the copies waiting for slots.  With
+// several compute lanes (the caller's stream plus `lanes` more), group g runs
+// on lane g % (1 + lanes) with a workspace region of its own, so one group's
+// short kernels overlap another group's apply.
 #include <algorithm>
 #include <cstdint>
 #include <vector>
@@ -43,24 +51,32 @@ bool spans_disjoint(std::vector<Span> v) {
 
 constexpr uint32_t kMaxSlots = 64;
 constexpr uint32_t kMaxCopyStreams = 8;
+constexpr uint32_t kMaxLanes = 1;   // extra compute lanes beside the caller's stream
 
 struct Events {
-    hipEvent_t start = nullptr;
-    std::vector<hipEvent_t> copied, applied;
+    hipEvent_t start = nullptr, tables = nullptr;
+    std::vector<hipEvent_t> copied, applied, done;
     bool ok = true;
-    explicit Events(uint32_t slots) : copied(slots, nullptr), applied(slots, nullptr) {
-        ok = hipEventCreateWithFlags(&start, hipEventDisableTiming) == hipSuccess;
+    Events(uint32_t slots, uint32_t lanes)
+        : copied(slots, nullptr), applied(slots, nullptr), done(lanes, nullptr) {
+        ok = hipEventCreateWithFlags(&start, hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&tables, hipEventDisableTiming) == hipSuccess;
         for (uint32_t s = 0; s < slots && ok; ++s)
             ok = hipEventCreateWithFlags(&copied[s], hipEventDisableTiming) == hipSuccess &&
                  hipEventCreateWithFlags(&applied[s], hipEventDisableTiming) == hipSuccess;
+        for (uint32_t l = 0; l < lanes && ok; ++l)
+            ok = hipEventCreateWithFlags(&done[l], hipEventDisableTiming) == hipSuccess;
     }
     ~Events() {
         // an event still pending in a stream is released once it completes
         if (start) (void)hipEventDestroy(start);
+        if (tables) (void)hipEventDestroy(tables);
         for (size_t s = 0; s < copied.size(); ++s) {
             if (copied[s]) (void)hipEventDestroy(copied[s]);
             if (applied[s]) (void)hipEventDestroy(applied[s]);
         }
+        for (hipEvent_t e : done)
+            if (e) (void)hipEventDestroy(e);
     }
 };
 
@@ -71,13 +87,16 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
                                          void *staging, size_t slot_bytes, uint32_t slots,
                                          void *workspace, size_t workspace_bytes,
                                          bf16d_result *results, hipStream_t compute,
-                                         const hipStream_t *copy, uint32_t copy_streams) {
+                                         const hipStream_t *copy, uint32_t copy_streams,
+                                         const hipStream_t *lanes, uint32_t n_lanes) {
     if (!jobs || count == 0 || !group_end || groups == 0 || groups > count || !staging ||
         !aligned16(staging) || slot_bytes == 0 || slot_bytes % 16 != 0 || slots < 2 ||
         slots > kMaxSlots || slot_bytes > SIZE_MAX / slots || !workspace ||
         !aligned16(workspace) || !results || !copy || copy_streams == 0 ||
-        copy_streams > kMaxCopyStreams)
+        copy_streams > kMaxCopyStreams || n_lanes > kMaxLanes || (n_lanes > 0 && !lanes))
         return BF16D_EINVAL;
+    const uint32_t n_run = 1 + n_lanes;   // compute lanes: the caller's stream first
+    auto lane_stream = [&](uint32_t g) { return g % n_run == 0 ? compute : lanes[g % n_run - 1]; };
     // groups partition [0, count) in order; each group's payloads fit a slot.
     // Each group's decompress jobs point into its slot.
     std::vector<bf16d_decompress_job> dj(count);
@@ -119,8 +138,10 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
         tables += align_up(decompress_table_bytes(lay[g], cnt), 256);
         first = end;
     }
+    // lane l's call layout at l * base; the job tables after all of them
     base = align_up(base, 256);
-    const size_t need = base + tables;
+    const size_t lanes_bytes = base * n_run;
+    const size_t need = lanes_bytes + tables;
     if (workspace_bytes < need) return BF16D_EINVAL;
     spans.push_back({reinterpret_cast<uintptr_t>(staging),
                      reinterpret_cast<uintptr_t>(staging) + slots * slot_bytes});
@@ -134,27 +155,32 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
     for (uint32_t g = 0; g < groups; ++g) {
         const uint32_t end = group_end[g];
         decompress_table(dj.data() + first, end - first, prep[g], lay[g], host.data() + table_at[g]);
-        // the kernels of group g read their job table from its place after `base`
-        const size_t jobs_at = base + table_at[g];
+        // the kernels of group g read their job table from its place after the
+        // lanes' layouts; offsets are relative to the group's lane region
+        const size_t jobs_at = lanes_bytes + table_at[g] - (g % n_run) * base;
         lay[g].block_start = jobs_at + (lay[g].block_start - lay[g].jobs);
         lay[g].dtile_start = jobs_at + (lay[g].dtile_start - lay[g].jobs);
         lay[g].jobs = jobs_at;
         first = end;
     }
 
-    Events ev(slots);
+    Events ev(slots, n_run);
     if (!ev.ok) return BF16D_EHIP;
     auto fail = [](hipError_t e) { return e != hipSuccess; };
     auto *ws = static_cast<uint8_t *>(workspace);
-    // one upload of every job table (the source is pageable: the runtime
-    // stages it before returning), then copies start after it and after the
-    // caller's earlier work on the compute stream
-    if (fail(hipMemcpyAsync(ws + base, host.data(), host.size(), hipMemcpyHostToDevice,
-                            compute)) ||
-        fail(hipEventRecord(ev.start, compute)))
-        return BF16D_EHIP;
+    // the copies start after the caller's earlier work on the compute stream;
+    // the job tables go up meanwhile (one upload; the source is pageable, so
+    // the runtime stages it before returning), and the other lanes start
+    // after them
+    if (fail(hipEventRecord(ev.start, compute))) return BF16D_EHIP;
     for (uint32_t c = 0; c < copy_streams; ++c)
         if (fail(hipStreamWaitEvent(copy[c], ev.start, 0))) return BF16D_EHIP;
+    if (fail(hipMemcpyAsync(ws + lanes_bytes, host.data(), host.size(), hipMemcpyHostToDevice,
+                            compute)) ||
+        fail(hipEventRecord(ev.tables, compute)))
+        return BF16D_EHIP;
+    for (uint32_t l = 0; l < n_lanes; ++l)
+        if (fail(hipStreamWaitEvent(lanes[l], ev.tables, 0))) return BF16D_EHIP;
     first = 0;
     for (uint32_t g = 0; g < groups; ++g) {
         const uint32_t end = group_end[g], s = g % slots;
@@ -180,13 +206,19 @@ extern "C" int bf16d_decompress_streamed(const bf16d_stream_job *jobs, uint32_t 
                 return BF16D_EHIP;
             j = k;
         }
+        hipStream_t ls = lane_stream(g);
         if (fail(hipEventRecord(ev.copied[s], cs)) ||
-            fail(hipStreamWaitEvent(compute, ev.copied[s], 0)) ||
-            fail(launch_decompress(lay[g], ws, end - first, prep[g].tiles, prep[g].dtiles,
-                                   results + first, compute, nullptr)) ||
-            fail(hipEventRecord(ev.applied[s], compute)))
+            fail(hipStreamWaitEvent(ls, ev.copied[s], 0)) ||
+            fail(launch_decompress(lay[g], ws + (g % n_run) * base, end - first, prep[g].tiles,
+                                   prep[g].dtiles, results + first, ls, nullptr)) ||
+            fail(hipEventRecord(ev.applied[s], ls)))
             return BF16D_EHIP;
         first = end;
     }
+    // the caller's stream completes only after every lane
+    for (uint32_t l = 0; l < n_lanes; ++l)
+        if (fail(hipEventRecord(ev.done[l], lanes[l])) ||
+            fail(hipStreamWaitEvent(compute, ev.done[l], 0)))
+            return BF16D_EHIP;
     return BF16D_OK;
 }

@@ -164,12 +164,15 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
 
     copies = (ctypes.c_void_p * 2)(None, None)
 
+    lanes = (ctypes.c_void_p * 2)(None, None)
+
     def call(jobs=jobs, count=2, ends=(1, 2), staging=staging, slot=4096, slots=2, ws=ws,
-             ws_bytes=WS, results=ctypes.addressof(res), copy=copies, n_copy=1):
+             ws_bytes=WS, results=ctypes.addressof(res), copy=copies, n_copy=1, lanes=None,
+             n_lanes=0):
         ge = (ctypes.c_uint32 * max(1, len(ends)))(*ends) if ends is not None else None
         return lib.bf16d_decompress_streamed(jobs, count, ge, len(ends) if ends else 0, staging,
                                              slot, slots, ws, ws_bytes, results, None, copy,
-                                             n_copy)
+                                             n_copy, lanes, n_lanes)
 
     E = native.EINVAL
     assert call(count=0) == E
@@ -190,6 +193,8 @@ def test_streamed_arguments_are_rejected_before_any_gpu_work(native):
     assert call(copy=None) == E                 # no copy streams
     assert call(n_copy=0) == E
     assert call(n_copy=9) == E                  # at most 8
+    assert call(n_lanes=1) == E                 # a lane count without lanes
+    assert call(lanes=lanes, n_lanes=2) == E    # at most one extra lane
     # the third slot of a ring of three overlaps the second job's weights
     assert call(staging=w1 - 2 * 4096 - 16, slots=3) == E
     bad = (native.StreamJob * 2)(native.StreamJob(w0 + 2, 100, ctypes.addressof(payload), 64, 0),

@@ -31,25 +31,28 @@ def _make(seed0=500):
     return pairs, payloads, checksums
 
 
-def _run(pairs, payloads, checksums, groups, slots=3, copy_streams=2):
+def _run(pairs, payloads, checksums, groups, slots=3, copy_streams=2, lanes=2):
     recv = [s.clone() for s, _ in pairs]
     sd = bd.StreamedDecompress(list(zip(recv, payloads, checksums)), groups, slots=slots,
-                               copy_streams=copy_streams)
+                               copy_streams=copy_streams, lanes=lanes)
     sd.run()
     return recv, sd.results()
 
 
+@pytest.mark.parametrize("lanes", [1, 2])
 @pytest.mark.parametrize("slots,copies", [(2, 1), (3, 2), (5, 3)])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("groups", [[3, 1, 4, 4], [1] * 12, [12], [5, 7]])
-def test_streamed_apply_rebuilds_every_tensor(groups, packed, slots, copies):
+def test_streamed_apply_rebuilds_every_tensor(groups, packed, slots, copies, lanes):
     """packed: all payloads in one pinned buffer at 16-byte boundaries, so each
-    group goes over in one transfer; otherwise one pinned tensor each."""
-    log(f"case streamed groups={groups} packed={packed} slots={slots} copies={copies}")
+    group goes over in one transfer; otherwise one pinned tensor each.  With
+    two lanes, consecutive groups are applied on two compute streams."""
+    log(f"case streamed groups={groups} packed={packed} slots={slots} copies={copies} "
+        f"lanes={lanes}")
     pairs, payloads, checksums = _make()
     if packed:
         payloads = bd.StreamedDecompress.pin_packed(payloads)
-    recv, res = _run(pairs, payloads, checksums, groups, slots, copies)
+    recv, res = _run(pairs, payloads, checksums, groups, slots, copies, lanes)
     assert [r["status"] for r in res] == [bd.OK] * len(pairs)
     for j, (w, (_, d)) in enumerate(zip(recv, pairs)):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16)), f"tensor {j}"
@@ -74,17 +77,19 @@ def test_streamed_failures_match_the_oracle():
     assert all(res[j]["status"] == bd.OK for j in (0, 1, 3, 4, 6, 7, 8, 10, 11))
 
 
+@pytest.mark.parametrize("lanes", [1, 2])
 @pytest.mark.parametrize("slots,copies", [(2, 1), (2, 2), (3, 2), (3, 4)])
-def test_streamed_many_groups_reuse_the_slots_in_turn(slots, copies):
+def test_streamed_many_groups_reuse_the_slots_in_turn(slots, copies, lanes):
     """40 one-tensor groups: each slot is refilled 40 / slots times, so every
     copy waits for the apply `slots` groups back, on whichever copy stream
-    its group falls to."""
-    log(f"case streamed 40 groups slots={slots} copies={copies}")
+    its group falls to, and that apply ran on whichever lane its group fell
+    to."""
+    log(f"case streamed 40 groups slots={slots} copies={copies} lanes={lanes}")
     pairs = [synth.make_pair((8192 * (1 + i % 3) + i,), "0.05", synth.MIX_DEFAULT, 1300 + i, DEV)
              for i in range(40)]
     out = bd.compress_batch(pairs)
     payloads = [p.cpu().pin_memory() for p, _, _ in out]
-    recv, res = _run(pairs, payloads, [cs for _, cs, _ in out], [1] * 40, slots, copies)
+    recv, res = _run(pairs, payloads, [cs for _, cs, _ in out], [1] * 40, slots, copies, lanes)
     assert all(r["status"] == bd.OK for r in res)
     for w, (_, d) in zip(recv, pairs):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16))
