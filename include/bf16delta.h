@@ -160,8 +160,23 @@ typedef struct bf16d_decompress_job {
 uint64_t bf16d_max_payload_bytes(uint64_t n);
 
 /* Workspace bytes that suffice for any batch of `count` jobs totalling
- * total_n elements, in either direction. */
+ * total_n elements, in either direction.  For compress this includes a 2 KiB
+ * record slot per 8192-element block (12.5 % of the weights). */
 size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count);
+
+/* Compress workspace with record slots of slot_bytes per block (a multiple
+ * of 16 from 16 to 2048; 0 is returned for any other value).  Compress uses
+ * the largest slot (up to 2048 bytes, in steps of 16) that the workspace it
+ * is given holds, so a caller short of memory passes less: with 256-byte
+ * slots the workspace is about 1.9 % of the weights.  A block's record
+ * (its position, mantissa and rare segments) that does not fit its slot is
+ * staged at the tail of the job's payload buffer instead, in the room between
+ * the final payload and `capacity`; one that finds no room there is encoded
+ * a second time from the weights, which reads that block again.  The payload
+ * bytes are the same either way; only the time differs.  With small slots,
+ * bytes of the payload buffer from payload_bytes up to capacity are
+ * unspecified after the call. */
+size_t bf16d_compress_workspace_bytes(uint64_t total_n, uint32_t count, uint32_t slot_bytes);
 
 /* Compress `count` tensors in one batched pass: old = src, new = dst.
  * The job array is host memory.  It is copied into the workspace before

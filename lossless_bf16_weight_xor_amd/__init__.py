@@ -114,9 +114,15 @@ class CompressBatch:
     per job."""
 
     def __init__(self, pairs: Sequence[tuple[torch.Tensor, torch.Tensor]],
-                 capacities: Sequence[int] | None = None, bindings=None):
+                 capacities: Sequence[int] | None = None, bindings=None,
+                 slot_bytes: int | None = None):
         """bindings: None (version-1 payloads), or per job (base_version,
-        target_version, overwrite) for version-2 payloads (bf16d_compress_bound)."""
+        target_version, overwrite) for version-2 payloads (bf16d_compress_bound).
+        slot_bytes: None for the full workspace (a 2 KiB record slot per block,
+        12.5 % of the weights), or a smaller slot (a multiple of 16, 16 to
+        2048; 256 makes the workspace about 1.9 % of the weights), records
+        that do not fit being staged in the payload buffer's spare room
+        (bf16d_compress_workspace_bytes)."""
         if not pairs:
             raise ValueError("empty batch")
         self.device = pairs[0][0].device
@@ -140,7 +146,13 @@ class CompressBatch:
             self.offset.append(at)
             at += (cap + _ALIGN - 1) // _ALIGN * _ALIGN
         self.arena = torch.empty(max(at, _ALIGN), dtype=torch.uint8, device=self.device)
-        self.ws_bytes = workspace_bytes(sum(self.n), self.count)
+        if slot_bytes is None:
+            self.ws_bytes = workspace_bytes(sum(self.n), self.count)
+        else:
+            self.ws_bytes = int(_native.lib().bf16d_compress_workspace_bytes(
+                sum(self.n), self.count, int(slot_bytes)))
+            if self.ws_bytes == 0:
+                raise ValueError("slot_bytes must be a multiple of 16 from 16 to 2048")
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
                                       device=self.device)

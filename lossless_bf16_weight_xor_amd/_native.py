@@ -19,7 +19,8 @@ BLOCK_ELEMS = 8192
 HEADER_BYTES = 64
 FORMAT_VERSION = 1
 
-EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes", "bf16d_compress",
+EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes",
+            "bf16d_compress_workspace_bytes", "bf16d_compress",
             "bf16d_decompress", "bf16d_compress_ex", "bf16d_decompress_ex",
             "bf16d_delta_compress", "bf16d_delta_decompress", "bf16d_decompress_streamed",
             "bf16d_decompress_remapped", "bf16d_workspace_bytes_remapped",
@@ -112,6 +113,8 @@ def lib():
         L.bf16d_max_payload_bytes.restype = u64
         L.bf16d_workspace_bytes.argtypes = [u64, u32]
         L.bf16d_workspace_bytes.restype = sz
+        L.bf16d_compress_workspace_bytes.argtypes = [u64, u32, u32]
+        L.bf16d_compress_workspace_bytes.restype = sz
         L.bf16d_compress.argtypes = [ctypes.POINTER(CompressJob), u32, vp, sz, vp, vp]
         L.bf16d_compress.restype = ctypes.c_int
         L.bf16d_decompress.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp, vp]

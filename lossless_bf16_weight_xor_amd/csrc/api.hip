@@ -211,6 +211,13 @@ uint64_t bf16d_max_payload_bytes(uint64_t n) {
     return total;
 }
 
+size_t bf16d_compress_workspace_bytes(uint64_t total_n, uint32_t count, uint32_t slot_bytes) {
+    if (slot_bytes < kMinSlot || slot_bytes > kSlot || slot_bytes % 16 != 0) return 0;
+    const uint64_t tiles = blocks_of(total_n) + count;
+    const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
+    return make_layout(tiles, dtiles, count, true, slot_bytes).total;
+}
+
 size_t bf16d_workspace_bytes(uint64_t total_n, uint32_t count) {
     const uint64_t tiles = blocks_of(total_n) + count;
     const uint64_t dtiles = (tiles + kDescTile - 1) / kDescTile + count;
@@ -257,8 +264,20 @@ int compress_call(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
     }
     const uint64_t tiles = start[count], dtiles = dstart[count];
     if (tiles >= kMaxTiles) return BF16D_EINVAL;
-    const Layout l = make_layout(tiles, dtiles, count, true);
-    if (workspace_bytes < l.total) return BF16D_EINVAL;
+    // the largest record slot the workspace holds: kSlot, or less
+    uint32_t slot = kSlot;
+    Layout l = make_layout(tiles, dtiles, count, true, slot);
+    if (workspace_bytes < l.total) {
+        const Layout l0 = make_layout(tiles, dtiles, count, true, 0);
+        if (tiles == 0 || workspace_bytes < l0.total) return BF16D_EINVAL;
+        const uint64_t per = (workspace_bytes - l0.total) / tiles / 16 * 16;
+        slot = (uint32_t)(per < kSlot ? per : kSlot);
+        // the slot region's alignment may cost up to 255 bytes: step down
+        while (slot >= kMinSlot &&
+               workspace_bytes < (l = make_layout(tiles, dtiles, count, true, slot)).total)
+            slot -= 16;
+        if (slot < kMinSlot) return BF16D_EINVAL;
+    }
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
                       reinterpret_cast<uintptr_t>(workspace) + l.total, true});
     ranges.push_back({reinterpret_cast<uintptr_t>(results),

@@ -27,9 +27,13 @@
 // pass would stall it on a cross-workgroup look-back.  So the work is split:
 //   setup    : clears the call's sums and builds the tile -> job maps.
 //   encode   : one workgroup per tile, no inter-workgroup waits.  Reads old
-//              and new once.  Writes each record (if <= kSlot bytes) to a
-//              fixed per-tile slot in the workspace, plus its descriptor and
-//              checksum partials; larger records are listed for re-encoding.
+//              and new once.  Writes each record to a fixed per-tile slot in
+//              the workspace if it fits, plus its descriptor and checksum
+//              partials.  A record that does not fit its slot but is at most
+//              kSlot bytes is staged at the payload buffer's tail (16-byte
+//              aligned ranges taken top down with one atomic per record);
+//              larger ones, and those that find no room, are listed for
+//              re-encoding.
 //   offsets  : a decoupled look-back scan (Merrill and Garland, "Single-pass
 //              Parallel Prefix Scan with Decoupled Look-back", 2016) over the
 //              record sizes of each job: the stream offsets.  It writes
@@ -43,8 +47,13 @@
 // payload (its flag set) has no mantissa segment and carries the new value
 // of every change as a 16-bit word.  Overwrite tiles take their own compiled
 // instances of the same steps.
-// The slots cost 2 * (record bytes) of extra traffic, about 2% at a 2%
-// change rate.
+// The staging costs 2 * (record bytes) of extra traffic, about 2% at a 2%
+// change rate.  The slot size is the caller's choice through the workspace
+// it passes: kSlot bytes per tile (12.5 % of the weights) keeps every record
+// of a sparse delta in the workspace; 256 bytes (1.6 %) keeps the common
+// sparse records there and stages the rest in the payload buffer, which
+// must then have room for them beyond the final payload, or they are
+// encoded again.
 #include "internal.hpp"
 
 namespace bf16d {
@@ -98,6 +107,7 @@ struct EncodeShared {
     uint32_t last[kChunksPerThread * kWaves];   // [round][wave]: last changed position + 1
     uint32_t gmax[kWaves];
     uint8_t gap8[256];   // widest gap between set bits of an 8-bit mask (0 if < 2 bits)
+    uint64_t stage_at;   // payload offset of a record staged at the tail (0: no room)
 };
 
 // Fill sh.gap8 (once per workgroup; the caller synchronises).
@@ -288,7 +298,9 @@ __device__ __forceinline__ void or_fields(uint32_t *s_rec, const uint16_t *s_x,
 template <bool kFull, bool kOw>
 __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16_t *s_x,
                                            uint32_t *s_rec, EncodeShared &sh,
-                                           uint8_t *__restrict__ slots,
+                                           uint8_t *__restrict__ slots, uint32_t slot_bytes,
+                                           const CompressJob &job,
+                                           unsigned long long *__restrict__ stage,
                                            uint32_t *__restrict__ desc_out,
                                            uint64_t *__restrict__ partial,
                                            uint32_t *__restrict__ overflow,
@@ -305,15 +317,60 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
     TileCode k;
     scan<kOw>(tr, f, sh, k);   // its barriers also order the clearing above
 
-    const bool fits = k.len <= kSlot;
+    const bool fits = k.len <= kSlot;   // built in LDS; larger records are re-encoded
     if (fits) or_fields<true, kOw>(s_rec, s_x, k);
     const uint64_t acc = first_lane(wave_sum(k.acc));
     __syncthreads();
 
     if (fits) {
-        uint4 *slot = reinterpret_cast<uint4 *>(slots + t * kSlot);
-        const uint4 *rec = reinterpret_cast<const uint4 *>(s_rec);
-        for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) slot[u] = rec[u];
+        uint8_t *dst = slots + t * slot_bytes;
+        if (k.len > slot_bytes) {   // uniform: the record waits at the payload's tail
+            // a 16-byte aligned range between the descriptor table and the
+            // capacity, in block b's stack (b % ways): the stack's bytes
+            // [o, o + room) taken with one atomic, o counting from the top
+            // chunk by chunk; a range that crosses a chunk's end is
+            // abandoned and another taken, a few times at most, then the
+            // record is encoded again instead (nothing ever waits).  Where it
+            // lands decides only which record is copied from where, never
+            // the payload's bytes.
+            if (tid == 0) {
+                const uint64_t room = (k.len + 15) & ~15u;
+                const uint64_t top = job.capacity & ~15ull;
+                const uint64_t floor = (job.hdr + 4 * job.nb + 15) & ~15ull;
+                const uint64_t ways = job.nb < kStageWays ? job.nb : kStageWays;
+                const uint64_t span = top > floor ? (top - floor) / ways & ~15ull : 0;
+                const uint64_t C = span < kStageChunk ? span : kStageChunk;
+                const uint64_t w = tr.b % ways;
+                uint64_t at = 0;
+                for (uint32_t tries = 0; at == 0 && room <= C && tries < kStageTries; ++tries) {
+                    const uint64_t o = atomicAdd(&stage[w], room);
+                    if (o % C + room > C) continue;   // crosses a chunk's end
+                    const uint64_t below = ((o / C) * ways + w + 1) * C;
+                    if (below > top - floor) break;   // out of room
+                    at = top - below + o % C;
+                }
+                sh.stage_at = at;
+            }
+            __syncthreads();
+            const uint64_t at = sh.stage_at;
+            // the slot keeps where the record is: its address and offset, or
+            // a null address when there was no room (the tile is then
+            // listed for re-encoding here, and the place kernel skips it)
+            if (tid == 0)
+                *reinterpret_cast<ulonglong2 *>(dst) = make_ulonglong2(
+                    at ? (unsigned long long)(uintptr_t)(job.payload + at) : 0ull, at);
+            if (at == 0) {   // no room: encoded again once the offsets are known
+                if (tid == 0) overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
+                dst = nullptr;
+            } else {
+                dst = (uint8_t *)(job.payload + at);
+            }
+        }
+        if (dst) {
+            uint4 *out = reinterpret_cast<uint4 *>(dst);
+            const uint4 *rec = reinterpret_cast<const uint4 *>(s_rec);
+            for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) out[u] = rec[u];
+        }
     } else if (tid == 0) {
         overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
     }
@@ -327,26 +384,31 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
 // tile's loads in registers at half the occupancy.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
 void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ tile_job,
-                   uint8_t *__restrict__ slots, uint32_t *__restrict__ desc_out,
+                   uint8_t *__restrict__ slots, uint32_t slot_bytes,
+                   unsigned long long *__restrict__ stage, uint32_t *__restrict__ desc_out,
                    uint64_t *__restrict__ partial, uint32_t *__restrict__ overflow,
                    Control *__restrict__ ctrl) {
     __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];
     __shared__ __attribute__((aligned(16))) uint32_t s_rec[kSlot / 4 + 4];
     __shared__ EncodeShared sh;
     const uint64_t t = xcd_tile(blockIdx.x, gridDim.x);
-    const CompressJob &job = jobs[tile_job[t]];
+    const uint32_t j = tile_job[t];
+    const CompressJob &job = jobs[j];
+    unsigned long long *js = stage + (size_t)kStageWays * j;
     const TileRef tr = tile_ref(job, t);
     if (job.flags & kFlagOverwrite) {   // overwrite payloads: their own instances
         if (tr.L == kBlock)
-            encode_one<true, true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow,
-                                   ctrl);
+            encode_one<true, true>(tr, t, s_x, s_rec, sh, slots, slot_bytes, job, js, desc_out,
+                                   partial, overflow, ctrl);
         else
-            encode_one<false, true>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow,
-                                    ctrl);
+            encode_one<false, true>(tr, t, s_x, s_rec, sh, slots, slot_bytes, job, js, desc_out,
+                                    partial, overflow, ctrl);
     } else if (tr.L == kBlock) {
-        encode_one<true, false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+        encode_one<true, false>(tr, t, s_x, s_rec, sh, slots, slot_bytes, job, js, desc_out,
+                                partial, overflow, ctrl);
     } else {
-        encode_one<false, false>(tr, t, s_x, s_rec, sh, slots, desc_out, partial, overflow, ctrl);
+        encode_one<false, false>(tr, t, s_x, s_rec, sh, slots, slot_bytes, job, js, desc_out,
+                                 partial, overflow, ctrl);
     }
 }
 
@@ -354,17 +416,17 @@ void encode_kernel(const CompressJob *__restrict__ jobs, const uint32_t *__restr
 // Job j's header, checksum and result.  The sums are read with device-scope
 // loads: the offsets kernel's last workgroup runs this right after the other
 // workgroups' atomics.
-__device__ void finalize_job(const CompressJob *__restrict__ jobs,
-                             const JobSums *__restrict__ sums,
+__device__ void finalize_job(const CompressJob *__restrict__ jobs, JobSums *__restrict__ sums,
                              bf16d_result *__restrict__ results, uint32_t j) {
     const CompressJob job = jobs[j];
-    const JobSums *js = &sums[j];
+    JobSums *js = &sums[j];
     const unsigned long long S = ld_agent(&js->csum), c = ld_agent(&js->c), r = ld_agent(&js->r),
                              pos = ld_agent(&js->pos), mant = ld_agent(&js->mant),
                              nbm = ld_agent(&js->nbm);
     const uint64_t rare = 2 * r;
     const uint64_t P = job.hdr + 4 * job.nb + pos + mant + rare;
     const int status = P <= job.capacity ? BF16D_OK : BF16D_ECAPACITY;
+    js->P = P;   // for the place kernel: staged records below P are re-encoded
     if (status == BF16D_OK) {
         BF16D_GMEM uint32_t *h = reinterpret_cast<BF16D_GMEM uint32_t *>(job.payload);
         BF16D_GMEM uint64_t *h64 = reinterpret_cast<BF16D_GMEM uint64_t *>(job.payload);
@@ -400,7 +462,7 @@ __device__ void finalize_job(const CompressJob *__restrict__ jobs,
 // For calls without tiles (every tensor empty); otherwise the offsets
 // kernel's last workgroup finalizes the jobs.
 __global__ __launch_bounds__(kThreads) void compress_finalize_kernel(
-    const CompressJob *__restrict__ jobs, const JobSums *__restrict__ sums, uint32_t count,
+    const CompressJob *__restrict__ jobs, JobSums *__restrict__ sums, uint32_t count,
     bf16d_result *__restrict__ results) {
     const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j < count) finalize_job(jobs, sums, results, j);
@@ -413,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
     const CompressJob *__restrict__ jobs, const uint32_t *__restrict__ dtile_job,
     const uint64_t *__restrict__ dstart, const uint32_t *__restrict__ desc,
     uint64_t *__restrict__ dstatus, uint64_t *__restrict__ offsets,
-    PlaceEntry *__restrict__ place, const uint64_t *__restrict__ partial,
+    PlaceEntry *__restrict__ place, uint32_t slot_bytes, const uint64_t *__restrict__ partial,
     JobSums *__restrict__ sums, Control *__restrict__ ctrl, uint32_t count,
     bf16d_result *__restrict__ results) {
     __shared__ uint32_t s_tmp[kWaves];
@@ -484,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
             e.dst = job.payload + rel;
             e.len = (len > kSlot || rel >= cap) ? 0u
                                                  : (uint32_t)(cap - rel < len ? cap - rel : len);
-            e.pad = 0;
+            e.staged = len > slot_bytes ? kStaged : 0u;
             place[job.block0 + b] = e;
         }
         off += lens[k];
@@ -507,31 +569,62 @@ __global__ __launch_bounds__(kThreads) void record_offsets_kernel(
 }
 
 // ------------------------------------------------------------------- place ---
-// Slot -> payload.  Each wave copies kPlaceTiles records: all their slot
-// words are requested before the first store, so enough bytes are in flight
-// per wave.  Lane u of round m produces payload dword u + 64m of a record
-// from slot dwords i - 1 and i (the record's byte offset within a dword is
-// fixed per record); the dwords a record shares with its neighbours, and
-// anything past `capacity`, are written byte by byte or not at all.
+// Slot (or staged range) -> payload.  Each wave copies kPlaceTiles records:
+// all their source words are requested before the first store, so enough
+// bytes are in flight per wave.  Lane u of round m produces payload dword
+// u + 64m of a record from source dwords i - 1 and i (the record's byte
+// offset within a dword is fixed per record); the dwords a record shares
+// with its neighbours, and anything past `capacity`, are written byte by
+// byte or not at all.
+//
+// A staged record (one that did not fit its slot) waits at the payload
+// buffer's tail, at an offset its slot holds.  It is copied down only if it
+// lies wholly at or past the job's payload size P: then no record's final
+// place overlaps it.  Otherwise the final records reach into the tail, and
+// it is put on the re-encode list instead (encoded again, straight into its
+// final place, after this kernel).
 constexpr uint32_t kPlaceTiles = 4;
 constexpr uint32_t kPlaceRounds = kSlot / 256;   // 64 lanes x 4 bytes per round
 
 __global__ __launch_bounds__(kThreads) void place_kernel(const PlaceEntry *__restrict__ place,
                                                          const uint8_t *__restrict__ slots,
+                                                         uint32_t slot_bytes,
+                                                         const uint32_t *__restrict__ tile_job,
+                                                         const JobSums *__restrict__ sums,
+                                                         uint32_t *__restrict__ overflow,
+                                                         Control *__restrict__ ctrl,
                                                          uint64_t tiles) {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t t0 = ((uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kPlaceTiles;
     if (t0 >= tiles) return;   // whole wave; the kernel has no barriers
     uint4 e = make_uint4(0, 0, 0, 0);
-    if (lane < kPlaceTiles && t0 + lane < tiles)
-        e = *reinterpret_cast<const uint4 *>(place + t0 + lane);
+    uint64_t from = 0;   // lanes 0..3: where tile t0 + lane's record is read from
+    if (lane < kPlaceTiles && t0 + lane < tiles) {
+        const uint64_t t = t0 + lane;
+        e = *reinterpret_cast<const uint4 *>(place + t);
+        from = (uint64_t)(uintptr_t)(slots + t * slot_bytes);
+        if (e.z != 0 && e.w == kStaged) {
+            const ulonglong2 at = *reinterpret_cast<const ulonglong2 *>(slots + t * slot_bytes);
+            if (at.x == 0) {   // never staged: already on the re-encode list
+                e.z = 0;
+            } else if (at.y >= sums[tile_job[t]].P) {
+                from = at.x;
+            } else {   // the final records reach into it: encode it again
+                overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;
+                e.z = 0;
+            }
+        }
+    }
     // a record of up to kSlot bytes at a byte offset of 1..3 spans one payload
-    // dword more than its slot: the extra round reads nothing
+    // dword more than its source: the extra round reads nothing
     uint32_t rec[kPlaceTiles][kPlaceRounds + 1];
 #pragma unroll
     for (uint32_t k = 0; k < kPlaceTiles; ++k) {
         const uint32_t len = (uint32_t)__builtin_amdgcn_readlane((int)e.z, k);
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + (t0 + k) * kSlot);
+        const uint64_t fk = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)from, k) |
+                            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(from >> 32), k)
+                                << 32;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>((uintptr_t)fk);
 #pragma unroll
         for (uint32_t m = 0; m < kPlaceRounds; ++m) {
             rec[k][m] = 0;
@@ -665,7 +758,9 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     auto *dmap = reinterpret_cast<uint32_t *>(ws + l.dtile_job);
     auto *dstatus = reinterpret_cast<uint64_t *>(ws + l.dstatus);
     auto *slots = ws + l.slots;
+    const uint32_t slot_bytes = l.slot_bytes;
     auto *overflow = reinterpret_cast<uint32_t *>(ws + l.overflow);
+    auto *stage = reinterpret_cast<unsigned long long *>(ws + l.stage);
     auto *place = reinterpret_cast<PlaceEntry *>(ws + l.plan);
 
     SetupArgs sa{};
@@ -673,6 +768,8 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     sa.zero_words[0] = sizeof(Control) / 4;
     sa.zero[1] = reinterpret_cast<uint32_t *>(sums);
     sa.zero_words[1] = sizeof(JobSums) / 4 * (uint64_t)count;
+    sa.zero[2] = reinterpret_cast<uint32_t *>(stage);
+    sa.zero_words[2] = 2 * (uint64_t)kStageWays * count;
     sa.start[0] = bstart;
     sa.map[0] = map;
     sa.tiles[0] = tiles;
@@ -685,17 +782,18 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
     if (tiles) {
         if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
             return hipErrorInvalidValue;
-        encode_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, slots, desc, partial,
-                                                                overflow, ctrl);
+        encode_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(jobs, map, slots, slot_bytes,
+                                                                stage, desc, partial, overflow,
+                                                                ctrl);
         if (events && events->after && hipEventRecord(events->after, stream) != hipSuccess)
             return hipErrorInvalidValue;
         // its last workgroup also writes the headers and results
         record_offsets_kernel<<<(uint32_t)dtiles, kThreads, 0, stream>>>(
-            jobs, dmap, dstart, desc, dstatus, offsets, place, partial, sums, ctrl, count,
-            results);
+            jobs, dmap, dstart, desc, dstatus, offsets, place, slot_bytes, partial, sums, ctrl,
+            count, results);
         const uint64_t per_block = (uint64_t)kWaves * kPlaceTiles;
         place_kernel<<<(uint32_t)((tiles + per_block - 1) / per_block), kThreads, 0, stream>>>(
-            place, slots, tiles);
+            place, slots, slot_bytes, map, sums, overflow, ctrl, tiles);
         reencode_kernel<false><<<persistent_grid((const void *)reencode_kernel<false>, tiles),
                                  kThreads, 0, stream>>>(jobs, map, overflow, offsets, ctrl);
         if (any_overwrite)

@@ -37,9 +37,22 @@ constexpr uint32_t kChunks = kBlock / 8;                 // 16-byte chunks per b
 constexpr uint32_t kChunksPerThread = kChunks / kThreads;   // 4
 constexpr uint32_t kDescPerThread = 8;
 constexpr uint32_t kDescTile = kThreads * kDescPerThread;   // descriptors per scan tile
-// compress: workspace slot per tile for its record; larger records are
-// encoded a second time straight into the payload
+// compress: the largest record built in LDS and staged for the place
+// kernel (2 KiB); larger records are encoded a second time straight into the
+// payload.  Each tile has a workspace slot of `slot_bytes` (a multiple of
+// 16, from 16 to kSlot: the caller's workspace decides); a staged record
+// that does not fit its slot goes to the payload buffer's tail instead.
 constexpr uint32_t kSlot = 2048;
+constexpr uint32_t kMinSlot = 16;
+// Staging at the payload's tail: up to kStageWays stacks per job, each with
+// its own counter (block b uses stack b % ways), so that the blocks of one
+// large tensor do not all wait on one atomic.  The stacks take chunks of up
+// to kStageChunk bytes from the top of the buffer down, in turn (chunk i of
+// stack k is the (i * ways + k)-th from the top), so that the staged records
+// stay together at the top, above the final payload where possible.
+constexpr uint32_t kStageWays = 32;
+constexpr uint32_t kStageChunk = 8192;
+constexpr uint32_t kStageTries = 4;   // a range that crosses a chunk's end is abandoned
 
 // ---- decoupled look-back status words ---------------------------------------
 // bits 62..63: 0 = not yet published, 1 = tile aggregate, 2 = inclusive prefix
@@ -130,17 +143,21 @@ constexpr uint32_t kRoomCap = (1u << 17) - 1;
 // atomic per wave and tile, straight from the main kernels, contends on the
 // few addresses and measured much slower.)
 struct alignas(64) JobSums {
-    unsigned long long csum, c, r, pos, mant, nbm, pad0, pad1;
+    unsigned long long csum, c, r, pos, mant, nbm;
+    unsigned long long pad;
+    unsigned long long P;       // compress: payload bytes, written by finalize
 };
 
 // compress: where one tile's record goes, written by the offsets kernel for
 // the place kernel
 struct alignas(16) PlaceEntry {
     BF16D_GMEM uint8_t *dst;   // first byte of the record in the payload
-    uint32_t len;              // bytes to copy from the slot: 0 if none (empty, re-encoded
-                               // elsewhere, or past the capacity), else cut at the capacity
-    uint32_t pad;
+    uint32_t len;              // bytes to copy: 0 if none (empty, re-encoded elsewhere,
+                               // or past the capacity), else cut at the capacity
+    uint32_t staged;           // 1: the record waits at the payload's tail, and the
+                               // slot holds its address; 0: the record is in the slot
 };
+constexpr uint32_t kStaged = 1;
 static_assert(sizeof(PlaceEntry) == 16, "PlaceEntry is one 16-byte word");
 
 struct alignas(64) Control {
@@ -168,13 +185,16 @@ struct SetupArgs {
 // Workspace layout, computed identically by every entry point.
 struct Layout {
     size_t control, jobs, block_start, dtile_start, tile_job, status, partial, sums, desc,
-        dtile_job, dstatus, state, slots, overflow, plan, total;
+        dtile_job, dstatus, state, slots, overflow, stage, plan, total;
+    uint32_t slot_bytes;   // compress: the record slot of each tile
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool compress) {
+inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool compress,
+                          uint32_t slot_bytes = kSlot) {
     Layout l{};
+    l.slot_bytes = compress ? slot_bytes : 0;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -195,8 +215,10 @@ inline Layout make_layout(uint64_t tiles, uint64_t dtiles, uint32_t count, bool 
     l.dtile_job = take(4 * dtiles);
     l.dstatus = take(8 * dtiles);
     l.state = take(sizeof(DecompressState) * size_t(count));
-    l.slots = take(compress ? size_t(kSlot) * tiles : 0);     // compress: record slots
+    l.slots = take(compress ? size_t(slot_bytes) * tiles : 0);   // compress: record slots
     l.overflow = take(compress ? 4 * tiles : 0);              // compress: overflowing tiles
+    // compress: bytes taken in each part of each job's tail staging
+    l.stage = take(compress ? 8 * size_t(kStageWays) * count : 0);
     // per-tile plan: compress, where each record goes (PlaceEntry); decompress, ApplyPlan
     l.plan = take(compress ? sizeof(PlaceEntry) * tiles : sizeof(ApplyPlan) * tiles);
     l.total = off;
