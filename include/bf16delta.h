@@ -369,6 +369,47 @@ int bf16d_decompress_remapped(const bf16d_decompress_job *jobs, const bf16d_rema
                               uint32_t count, void *workspace, size_t workspace_bytes,
                               bf16d_result *results, hipStream_t stream);
 
+/* Remapped apply with the layout prepared once.
+ *
+ * A receiver that applies a delta at every step onto the same remapped layout
+ * can check and upload that layout once ("GPU-accelerated Weight
+ * Teleportation", section "Working with low-precision RL": the address
+ * metadata is prepared on the CPU for the layout, which does not change
+ * between steps).  bf16d_remap_prepare checks the segments as
+ * bf16d_decompress_remapped does (block-aligned, in order, covering each
+ * tensor, no two physical ranges overlapping) and writes:
+ *   plan      : host memory, bf16d_remap_plan_bytes(count, total_segments)
+ *               bytes, owned by the caller: the jobs' (weights, n) and the
+ *               sorted physical ranges;
+ *   block_map : device memory, 8-byte aligned, bf16d_remap_map_bytes(sum
+ *               of n, count) bytes, owned by the caller: the address of
+ *               every 8192-element block's first weight, uploaded on
+ *               `stream` (the host copy is staged before the call returns).
+ * Only the jobs' weights and n are read (payload fields are ignored).
+ * Returns BF16D_EINVAL for an invalid layout or short buffers, BF16D_EHIP
+ * if the upload fails.
+ *
+ * bf16d_decompress_remapped_prepared then applies payloads onto that layout:
+ * `jobs` must be the prepared jobs in the same order with the same weights
+ * (NULL for a remapped tensor) and n; their payloads and checksums may
+ * differ at every call.  Each call checks its payloads, workspace and
+ * results against each other and against the prepared ranges (a binary
+ * search each), and reads each block's place from block_map; nothing about
+ * the layout is uploaded or searched again.  The workspace needs
+ * bf16d_workspace_bytes(sum of n, count) bytes.  Statuses, rollback and the
+ * other errors are those of bf16d_decompress.  The plan and the map must
+ * stay unchanged while calls that use them run, and the physical buffers
+ * must be the ones prepared. */
+size_t bf16d_remap_plan_bytes(uint32_t count, uint64_t total_segments);
+size_t bf16d_remap_map_bytes(uint64_t total_n, uint32_t count);
+int bf16d_remap_prepare(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
+                        uint32_t count, void *plan, size_t plan_bytes, uint64_t *block_map,
+                        size_t map_bytes, hipStream_t stream);
+int bf16d_decompress_remapped_prepared(const bf16d_decompress_job *jobs, uint32_t count,
+                                       const void *plan, const uint64_t *block_map,
+                                       void *workspace, size_t workspace_bytes,
+                                       bf16d_result *results, hipStream_t stream);
+
 /* Streamed receiver: payloads in host memory, applied layer by layer.
  *
  * The double-buffered pipeline of "GPU-accelerated Weight Teleportation",

@@ -377,9 +377,13 @@ class RemappedBatch:
     tensor (no remap) or (n, segments) with segments a list of (first, view):
     logical elements [first, first + view.numel()) of the n-element tensor
     live in `view` (a contiguous 16-bit device view, `first` a multiple of
-    8192)."""
+    8192).
+    prepared: True (the default) checks and uploads the layout once
+    (bf16d_remap_prepare) and makes every run() a prepared call
+    (bf16d_decompress_remapped_prepared); False passes the segments at every
+    call (bf16d_decompress_remapped)."""
 
-    def __init__(self, items):
+    def __init__(self, items, prepared: bool = True):
         if not items:
             raise ValueError("empty batch")
         self.count = len(items)
@@ -413,8 +417,26 @@ class RemappedBatch:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
                                       device=device)
+        self.prepared = prepared
+        if prepared:
+            L = _native.lib()
+            self.plan = ctypes.create_string_buffer(
+                int(L.bf16d_remap_plan_bytes(self.count, total_segs)))
+            map_bytes = int(L.bf16d_remap_map_bytes(total_n, self.count))
+            self.block_map = torch.empty(map_bytes // 8, dtype=torch.int64, device=device)
+            rc = L.bf16d_remap_prepare(self.jobs, self.remaps, self.count, self.plan,
+                                       len(self.plan), self.block_map.data_ptr(), map_bytes,
+                                       _stream(device))
+            _check_rc(rc, "bf16d_remap_prepare")
 
     def run(self) -> None:
+        if self.prepared:
+            rc = _native.lib().bf16d_decompress_remapped_prepared(
+                self.jobs, self.count, self.plan, self.block_map.data_ptr(),
+                self.workspace.data_ptr(), self.ws_bytes, self.result_buf.data_ptr(),
+                _stream(self.device))
+            _check_rc(rc, "bf16d_decompress_remapped_prepared")
+            return
         rc = _native.lib().bf16d_decompress_remapped(
             self.jobs, self.remaps, self.count, self.workspace.data_ptr(), self.ws_bytes,
             self.result_buf.data_ptr(), _stream(self.device))
@@ -424,10 +446,10 @@ class RemappedBatch:
         return _results(self.result_buf, self.count)
 
 
-def decompress_remapped(items) -> list[dict]:
+def decompress_remapped(items, prepared: bool = True) -> list[dict]:
     """One remapped decompress call (see RemappedBatch); returns the per-job
     result dicts."""
-    batch = RemappedBatch(items)
+    batch = RemappedBatch(items, prepared)
     batch.run()
     return batch.results()
 

@@ -70,12 +70,14 @@ bool remap_valid(const bf16d_remap &m, uint64_t n) {
 }
 
 int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p,
-                    const bf16d_remap *remaps) {
+                    const bf16d_remap *remaps, bool mapped) {
     p.bstart.assign(size_t(count) + 1, 0);
     p.dstart.assign(size_t(count) + 1, 0);
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_decompress_job &J = jobs[j];
-        if (remaps && remaps[j].count > 0) {
+        if (mapped) {
+            // checked against the prepared plan by the caller
+        } else if (remaps && remaps[j].count > 0) {
             if (J.weights || !remap_valid(remaps[j], J.n)) return BF16D_EINVAL;
         } else if (J.n > 0 && (!J.weights || !aligned16(J.weights))) {
             return BF16D_EINVAL;
@@ -202,7 +204,177 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
 
 }  // namespace
 
+// ---- prepared remaps -------------------------------------------------------------
+// The host plan of bf16d_remap_prepare, in caller memory: a header, each job's
+// (weights, n) as prepared, and the sorted physical ranges the jobs write.
+namespace {
+
+constexpr uint64_t kPlanMagic = 0x504D5244363146ull;   // "F16DRMP"
+
+struct PlanHeader {
+    uint64_t magic;
+    uint32_t count, pad;
+    uint64_t nranges;   // sorted, pairwise disjoint written ranges
+    uint64_t tiles;     // blocks of the batch: entries of the block map
+};
+struct PlanJob {
+    uint64_t weights, n;
+};
+struct PlanRange {
+    uint64_t lo, hi;
+};
+
+size_t plan_bytes(uint32_t count, uint64_t ranges) {
+    return sizeof(PlanHeader) + sizeof(PlanJob) * size_t(count) + sizeof(PlanRange) * ranges;
+}
+
+// does [lo, hi) overlap one of the sorted, disjoint ranges r[0, m)?
+bool overlaps_sorted(const PlanRange *r, uint64_t m, uint64_t lo, uint64_t hi) {
+    if (hi <= lo) return false;
+    uint64_t a = 0, b = m;   // first range with r.hi > lo
+    while (a < b) {
+        const uint64_t mid = (a + b) / 2;
+        if (r[mid].hi <= lo) a = mid + 1; else b = mid;
+    }
+    return a < m && r[a].lo < hi;
+}
+
+}  // namespace
+
 extern "C" {
+
+size_t bf16d_remap_plan_bytes(uint32_t count, uint64_t total_segments) {
+    return plan_bytes(count, total_segments + count);
+}
+
+size_t bf16d_remap_map_bytes(uint64_t total_n, uint32_t count) {
+    return 8 * (size_t)(blocks_of(total_n) + count);
+}
+
+int bf16d_remap_prepare(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
+                        uint32_t count, void *plan, size_t plan_size, uint64_t *block_map,
+                        size_t map_bytes, hipStream_t stream) {
+    if (!jobs || count == 0 || !plan || !block_map ||
+        (reinterpret_cast<uintptr_t>(block_map) & 7u) != 0)
+        return BF16D_EINVAL;
+    // the layout: block-aligned segments in order, or plain weights
+    std::vector<Range> ranges;
+    uint64_t tiles = 0;
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_decompress_job &J = jobs[j];
+        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        if (remaps && remaps[j].count > 0) {
+            if (J.weights || !remap_valid(remaps[j], J.n)) return BF16D_EINVAL;
+            for (uint32_t k = 0; k < remaps[j].count; ++k) {
+                const bf16d_segment &g = remaps[j].segments[k];
+                ranges.push_back({reinterpret_cast<uintptr_t>(g.dst),
+                                  reinterpret_cast<uintptr_t>(g.dst) + 2 * g.count, true});
+            }
+        } else {
+            if (J.n > 0 && (!J.weights || !aligned16(J.weights))) return BF16D_EINVAL;
+            ranges.push_back({reinterpret_cast<uintptr_t>(J.weights),
+                              reinterpret_cast<uintptr_t>(J.weights) + 2 * J.n, true});
+        }
+        tiles += blocks_of(J.n);
+    }
+    if (tiles >= kMaxTiles || map_bytes < 8 * tiles) return BF16D_EINVAL;
+    ranges.push_back({reinterpret_cast<uintptr_t>(block_map),
+                      reinterpret_cast<uintptr_t>(block_map) + 8 * tiles, true});
+    if (!ranges_disjoint(ranges)) return BF16D_EINVAL;   // sorts them, drops empty ones
+    // the plan keeps the weights' ranges, not the map's
+    ranges.erase(std::remove_if(ranges.begin(), ranges.end(),
+                                [&](const Range &r) {
+                                    return r.lo == reinterpret_cast<uintptr_t>(block_map);
+                                }),
+                 ranges.end());
+    if (plan_size < plan_bytes(count, ranges.size())) return BF16D_EINVAL;
+
+    // the block map: each block's first weight
+    std::vector<uint64_t> map(tiles);
+    uint64_t t = 0;
+    for (uint32_t j = 0; j < count; ++j) {
+        const bf16d_decompress_job &J = jobs[j];
+        const uint64_t nb = blocks_of(J.n);
+        if (remaps && remaps[j].count > 0) {
+            uint32_t k = 0;
+            for (uint64_t b = 0; b < nb; ++b) {
+                const uint64_t e = b * kBlock;
+                while (remaps[j].segments[k].first + remaps[j].segments[k].count <= e) ++k;
+                const bf16d_segment &g = remaps[j].segments[k];
+                map[t++] = reinterpret_cast<uintptr_t>(g.dst + (e - g.first));
+            }
+        } else {
+            for (uint64_t b = 0; b < nb; ++b)
+                map[t++] = reinterpret_cast<uintptr_t>(J.weights + b * kBlock);
+        }
+    }
+    if (tiles && hipMemcpyAsync(block_map, map.data(), 8 * tiles, hipMemcpyHostToDevice,
+                                stream) != hipSuccess)
+        return BF16D_EHIP;
+
+    auto *h = static_cast<PlanHeader *>(plan);
+    h->magic = kPlanMagic;
+    h->count = count;
+    h->pad = 0;
+    h->nranges = ranges.size();
+    h->tiles = tiles;
+    auto *pj = reinterpret_cast<PlanJob *>(h + 1);
+    for (uint32_t j = 0; j < count; ++j)
+        pj[j] = {reinterpret_cast<uintptr_t>(jobs[j].weights), jobs[j].n};
+    auto *pr = reinterpret_cast<PlanRange *>(pj + count);
+    for (size_t i = 0; i < ranges.size(); ++i) pr[i] = {ranges[i].lo, ranges[i].hi};
+    return BF16D_OK;
+}
+
+int bf16d_decompress_remapped_prepared(const bf16d_decompress_job *jobs, uint32_t count,
+                                       const void *plan, const uint64_t *block_map,
+                                       void *workspace, size_t workspace_bytes,
+                                       bf16d_result *results, hipStream_t stream) {
+    if (!jobs || count == 0 || !plan || !block_map || !results || !workspace ||
+        !aligned16(workspace))
+        return BF16D_EINVAL;
+    const auto *h = static_cast<const PlanHeader *>(plan);
+    if (h->magic != kPlanMagic || h->count != count) return BF16D_EINVAL;
+    const auto *pj = reinterpret_cast<const PlanJob *>(h + 1);
+    const auto *pr = reinterpret_cast<const PlanRange *>(pj + count);
+    // the jobs the plan was made for: same tensors, in the same order
+    for (uint32_t j = 0; j < count; ++j)
+        if (pj[j].weights != reinterpret_cast<uintptr_t>(jobs[j].weights) ||
+            pj[j].n != jobs[j].n)
+            return BF16D_EINVAL;
+    DecompressPrep prep;
+    int rc = decompress_prep(jobs, count, prep, nullptr, true);
+    if (rc != BF16D_OK) return rc;
+    if (prep.tiles != h->tiles) return BF16D_EINVAL;
+    const Layout l = make_layout(prep.tiles, prep.dtiles, count, false);
+    if (workspace_bytes < l.total) return BF16D_EINVAL;
+    // this call's buffers against each other, and against the prepared
+    // physical ranges (sorted: a binary search each)
+    std::vector<Range> mine;
+    mine.reserve(size_t(count) + 3);
+    for (uint32_t j = 0; j < count; ++j)
+        mine.push_back({reinterpret_cast<uintptr_t>(jobs[j].payload),
+                        reinterpret_cast<uintptr_t>(jobs[j].payload) + jobs[j].payload_bytes,
+                        false});
+    mine.push_back({reinterpret_cast<uintptr_t>(workspace),
+                    reinterpret_cast<uintptr_t>(workspace) + l.total, true});
+    mine.push_back({reinterpret_cast<uintptr_t>(results),
+                    reinterpret_cast<uintptr_t>(results + count), true});
+    mine.push_back({reinterpret_cast<uintptr_t>(block_map),
+                    reinterpret_cast<uintptr_t>(block_map) + 8 * prep.tiles, false});
+    for (const Range &r : mine)
+        if (overlaps_sorted(pr, h->nranges, r.lo, r.hi)) return BF16D_EINVAL;
+    if (!ranges_disjoint(mine)) return BF16D_EINVAL;
+
+    std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
+    decompress_table(jobs, count, prep, l, host.data());
+    rc = upload(workspace, host, l.jobs, stream);
+    if (rc != BF16D_OK) return rc;
+    return launch_decompress(l, static_cast<uint8_t *>(workspace), count, prep.tiles,
+                             prep.dtiles, results, stream, nullptr, block_map) == hipSuccess
+               ? BF16D_OK
+               : BF16D_EHIP;
+}
 
 uint64_t bf16d_max_payload_bytes(uint64_t n) {
     const uint64_t full = n / kBlock, tail = n % kBlock;

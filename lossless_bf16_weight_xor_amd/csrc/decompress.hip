@@ -207,7 +207,7 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
                             const DecompressState *__restrict__ state,
                             const uint64_t *__restrict__ start, uint32_t count,
                             const uint64_t *__restrict__ offsets, ApplyPlan *__restrict__ plan,
-                            uint64_t tiles) {
+                            const uint64_t *__restrict__ block_map, uint64_t tiles) {
     for (uint64_t t = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; t < tiles;
          t += (uint64_t)gridDim.x * blockDim.x) {
         uint32_t lo = 0, hi = count;   // invariant: start[lo] <= t < start[hi]
@@ -228,7 +228,9 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
             const uint64_t b = t - job.block0;
             const uint64_t D = st.hdr + 4 * job.nb + offsets[t];
             const uint64_t room = job.payload_bytes - D;   // prepare checked D <= payload_bytes
-            if (job.nsegs == 0) {
+            if (block_map) {   // a prepared remap: the block's place, looked up once
+                p.w = (BF16D_GMEM uint16_t *)(uintptr_t)block_map[t];
+            } else if (job.nsegs == 0) {
                 p.w = job.weights + b * kBlock;
             } else {   // the segment holding block b (segments are block-aligned)
                 const uint64_t e = b * kBlock;
@@ -1009,7 +1011,7 @@ __global__ __launch_bounds__(kThreads) void sum_partials_kernel(
 
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                             const bf16d_events *events) {
+                             const bf16d_events *events, const uint64_t *block_map) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const DecompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
@@ -1044,7 +1046,7 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
     if (tiles) {
         const uint64_t g = (tiles + kThreads - 1) / kThreads;
         plan_kernel<<<(uint32_t)(g < 4096 ? g : 4096), kThreads, 0, stream>>>(
-            jobs, state, bstart, count, offsets, plan, tiles);
+            jobs, state, bstart, count, offsets, plan, block_map, tiles);
         if (events && events->before && hipEventRecord(events->before, stream) != hipSuccess)
             return hipErrorInvalidValue;
         apply_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(plan, state, partial);

@@ -558,8 +558,11 @@ struct DecompressPrep {
     std::vector<uint64_t> bstart, dstart;   // first tile / descriptor tile of each job
     uint64_t tiles = 0, dtiles = 0;
 };
+// `mapped`: the weights' places come from a prepared block map, so the jobs'
+// weights pointers are not checked here (the prepared call checks them
+// against its plan instead)
 int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, DecompressPrep &p,
-                    const bf16d_remap *remaps = nullptr);
+                    const bf16d_remap *remaps = nullptr, bool mapped = false);
 size_t decompress_table_bytes(const Layout &l, uint32_t count);
 void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
                       const Layout &l, uint8_t *out);
@@ -570,7 +573,9 @@ void launch_setup(const SetupArgs &a, hipStream_t stream);
 hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                            uint64_t dtiles, bf16d_result *results, hipStream_t stream,
                            const bf16d_events *events, bool any_overwrite);
+// block_map (may be null): the physical address of each tile's first weight,
+// prepared once for a remapped layout (bf16d_remap_prepare)
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                             const bf16d_events *events);
+                             const bf16d_events *events, const uint64_t *block_map = nullptr);
 }  // namespace bf16d

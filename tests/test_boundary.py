@@ -257,3 +257,49 @@ def test_bound_arguments_are_rejected_before_any_gpu_work(native):
     assert lib.bf16d_decompress_bound(dj, ws_ptr + 64, 1, ws_ptr, 1 << 15,
                                       ctypes.addressof(res), None) == native.EINVAL
     assert native.status_string(native.EVERSION).startswith("EVERSION")
+
+
+def test_remap_prepare_refuses_bad_layouts_before_any_gpu_work(native):
+    """bf16d_remap_prepare checks the layout before it uploads the block map,
+    so these calls need no GPU (the pointers are never touched)."""
+    lib = native.lib()
+    base = 1 << 40
+    n = 4 * 8192
+    plan = ctypes.create_string_buffer(int(lib.bf16d_remap_plan_bytes(2, 8)))
+    map_bytes = int(lib.bf16d_remap_map_bytes(2 * n, 2))
+    mp = base + (1 << 30)
+
+    def segs(*spec):
+        arr = (native.Segment * len(spec))(*[native.Segment(f, c, d) for f, c, d in spec])
+        return arr, native.Remap(arr, len(spec))
+
+    def call(spec0, spec1, plan_len=len(plan), m=mp, mb=map_bytes):
+        a0, r0 = segs(*spec0)
+        a1, r1 = segs(*spec1)
+        jobs = (native.DecompressJob * 2)(native.DecompressJob(None, n, None, 0, 0),
+                                          native.DecompressJob(None, n, None, 0, 0))
+        remaps = (native.Remap * 2)(r0, r1)
+        return lib.bf16d_remap_prepare(jobs, remaps, 2, plan, plan_len, m, mb, None)
+
+    half = 2 * 8192
+    good0 = [(0, half, base), (half, half, base + 4 * half)]
+    good1 = [(0, half, base + 2 * half), (half, half, base + 6 * half)]
+    E = native.EINVAL
+    # segments of the two tensors overlapping each other
+    assert call(good0, [(0, half, base + 2 * half), (half, half, base + 4 * half)]) == E
+    # not block-aligned, not in order, not covering n
+    assert call([(0, 8000, base), (8000, n - 8000, base + 2 * 8192 * 8)], good1) == E
+    assert call([(half, half, base), (0, half, base + 4 * half)], good1) == E
+    assert call([(0, half, base)], good1) == E
+    # a misaligned segment
+    assert call([(0, half, base + 2), (half, half, base + 4 * half)], good1) == E
+    # short plan, short or misaligned map, the map inside the weights
+    assert call(good0, good1, plan_len=16) == E
+    assert call(good0, good1, mb=8) == E
+    assert call(good0, good1, m=mp + 4) == E
+    assert call(good0, good1, m=base + 8) == E
+    # the prepared call refuses a plan that was never prepared
+    jobs = (native.DecompressJob * 2)()
+    ws = base + (1 << 31)
+    assert lib.bf16d_decompress_remapped_prepared(jobs, 2, plan, mp, ws, 1 << 20, ws + (1 << 21),
+                                                  None) == E

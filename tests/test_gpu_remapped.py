@@ -39,9 +39,10 @@ def _segments(fused, which, R, C):
             for g in range(R // G)]
 
 
+@pytest.mark.parametrize("prepared", [True, False])
 @pytest.mark.parametrize("R,C", [(512, 128), (256, 4096)])
-def test_gate_up_paired_in_groups_of_64(R, C):
-    log(f"case remapped gate/up R={R} C={C}")
+def test_gate_up_paired_in_groups_of_64(R, C, prepared):
+    log(f"case remapped gate/up R={R} C={C} prepared={prepared}")
     (g0, g1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 2000 + R, DEV)
     (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 3000 + R, DEV)
     # an identity job and a ragged two-segment job in the same call
@@ -58,15 +59,16 @@ def test_gate_up_paired_in_groups_of_64(R, C):
              ((R * C, _segments(fused, 1, R, C)), out[1][0], out[1][1]),
              (xw, out[2][0], out[2][1]),
              ((y0.numel(), [(0, ya), (2 * 8192, yb)]), out[3][0], out[3][1])]
-    res = bd.decompress_remapped(items)
+    res = bd.decompress_remapped(items, prepared)
     assert [r["status"] for r in res] == [bd.OK] * 4
     assert torch.equal(fused.view(torch.int16), want.view(torch.int16))
     assert torch.equal(xw.view(torch.int16), x1.view(torch.int16))
     assert torch.equal(torch.cat([ya, yb]).view(torch.int16), y1.view(torch.int16))
 
 
-def test_remapped_failure_leaves_the_physical_layout_old():
-    log("case remapped failure")
+@pytest.mark.parametrize("prepared", [True, False])
+def test_remapped_failure_leaves_the_physical_layout_old(prepared):
+    log(f"case remapped failure prepared={prepared}")
     R, C = 256, 128
     (g0, g1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 6000, DEV)
     (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_DEFAULT, 6001, DEV)
@@ -77,7 +79,7 @@ def test_remapped_failure_leaves_the_physical_layout_old():
     bad_payload[-1] ^= 0x20
     items = [((R * C, _segments(fused, 0, R, C)), out[0][0], out[0][1] ^ 1),   # wrong checksum
              ((R * C, _segments(fused, 1, R, C)), bad_payload, out[1][1])]     # bad record
-    res = bd.decompress_remapped(items)
+    res = bd.decompress_remapped(items, prepared)
     for j, (src, payload, cs) in enumerate([(g0, out[0][0], out[0][1] ^ 1),
                                              (u0, bad_payload, out[1][1])]):
         w = to_u16(src).copy()
@@ -110,3 +112,52 @@ def test_remapped_apply_of_version_2_payloads(overwrite):
     res = bd.decompress_remapped(items[:1])
     assert res[0]["status"] == bd.ECHECKSUM
     assert torch.equal(fused.view(torch.int16), before.view(torch.int16))
+
+
+def test_a_prepared_layout_serves_many_steps():
+    """One prepare, then steps that alternate the direction (old -> new -> old
+    ...) with the same payloads and the other checksum; every step checked.
+    A job table that differs from the prepared one is refused."""
+    log("case prepared remap over many steps")
+    R, C = 1024, 256
+    (g0, g1) = synth.make_pair((R, C), "0.02", synth.MIX_DEFAULT, 6200, DEV)
+    (u0, u1) = synth.make_pair((R, C), "0.02", synth.MIX_DEFAULT, 6201, DEV)
+    (x0, x1) = synth.make_pair((3 * 8192 + 5,), "0.02", synth.MIX_DEFAULT, 6202, DEV)
+    pairs = [(g0.reshape(-1), g1.reshape(-1)), (u0.reshape(-1), u1.reshape(-1)), (x0, x1)]
+    fwd = bd.compress_batch(pairs)
+    back = bd.compress_batch([(d, s) for s, d in pairs])
+    fused, xw = _paired(g0, u0), x0.clone()
+    items = [((R * C, _segments(fused, 0, R, C)), fwd[0][0], fwd[0][1]),
+             ((R * C, _segments(fused, 1, R, C)), fwd[1][0], fwd[1][1]),
+             (xw, fwd[2][0], fwd[2][1])]
+    batch = bd.RemappedBatch(items, prepared=True)
+    want = [(_paired(g0, u0), x0), (_paired(g1, u1), x1)]
+    for step in range(6):
+        direction = (step + 1) % 2           # after this step: 1 = new, 0 = old
+        for j in range(3):
+            batch.jobs[j].checksum = (fwd if direction else back)[j][1]
+        batch.run()
+        assert [r["status"] for r in batch.results()] == [bd.OK] * 3, step
+        wf, wx = want[direction]
+        assert torch.equal(fused.view(torch.int16), wf.view(torch.int16)), step
+        assert torch.equal(xw.view(torch.int16), wx.view(torch.int16)), step
+    # another tensor in place of the prepared one: refused, nothing enqueued
+    other = x0.clone()
+    saved = batch.jobs[2].weights
+    batch.jobs[2].weights = other.data_ptr()
+    with pytest.raises(RuntimeError):
+        batch.run()
+    batch.jobs[2].weights = saved
+    # a payload that lies inside the prepared weights: refused
+    saved_p = batch.jobs[0].payload
+    batch.jobs[0].payload = fused.data_ptr() + 4096
+    with pytest.raises(RuntimeError):
+        batch.run()
+    batch.jobs[0].payload = saved_p
+    # the refused calls enqueued nothing: the weights are still old
+    for j in range(3):
+        batch.jobs[j].checksum = fwd[j][1]
+    batch.run()
+    assert [r["status"] for r in batch.results()] == [bd.OK] * 3
+    assert torch.equal(fused.view(torch.int16), want[1][0].view(torch.int16))
+    assert torch.equal(xw.view(torch.int16), want[1][1].view(torch.int16))
