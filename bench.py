@@ -24,6 +24,9 @@ Reported:
   roofline_decompress : the apply kernel the same way, and on its effective
               bytes: 2n + P + every 32-byte sector that holds a change (the
               device writes sectors, not the changed elements alone)
+  decompress_verify_first : the two-pass decompress that checks every job
+              before writing it (weights untouched on failure), against the
+              single in-place pass
   compress_small_workspace : the same compress with 256-byte record slots
               (workspace about 1.9 % of the weights instead of 12.9 %)
   change_rate_sweep : compress and decompress of one 1 GiB tensor at 0.085,
@@ -275,6 +278,47 @@ def small_workspace(bd, pairs, comp, res, steps, slot_bytes=256):
            "time_ratio": round(tsm / tf, 4), "payloads_identical": same}
     del small
     return out
+
+
+def verify_first(bd, pairs, payloads, cs_new, cs_old, steps):
+    """The verify-first decompress (bf16d_decompress_verified: a checking pass
+    with no stores, then a pass that writes the verified jobs' changed
+    chunks) timed in turns with the single in-place pass on a receiver of its
+    own; both receivers end bit-exact."""
+    recv_a = [s.clone() for s, _ in pairs]
+    recv_b = [s.clone() for s, _ in pairs]
+    fused = bd.DecompressBatch([(w, p, c) for w, p, c in zip(recv_a, payloads, cs_new)])
+    vf = bd.DecompressBatch([(w, p, c) for w, p, c in zip(recv_b, payloads, cs_new)],
+                            verify_first=True)
+    tf, tv, tk, direction = [], [], [], 0
+    for i in range(steps + 1):
+        cs = cs_new if direction == 0 else cs_old
+        for j in range(len(cs)):
+            fused.jobs[j].checksum = cs[j]
+            vf.jobs[j].checksum = cs[j]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e[0].record()
+        fused.run()
+        e[1].record()
+        e[2].record()
+        vf.run(events=(e[3], e[4]))
+        e[5].record()
+        torch.cuda.synchronize()
+        assert all(r["status"] == bd.OK for r in fused.results()), "in-place decompress failed"
+        assert all(r["status"] == bd.OK for r in vf.results()), "verified decompress failed"
+        direction ^= 1
+        if i:
+            tf.append(e[0].elapsed_time(e[1]) / 1e3)
+            tv.append(e[2].elapsed_time(e[5]) / 1e3)
+            tk.append(e[3].elapsed_time(e[4]) / 1e3)
+    for wa, wb, (s, d) in zip(recv_a, recv_b, pairs):
+        want = d if direction == 1 else s
+        assert torch.equal(wa.view(torch.int16), want.view(torch.int16)), "in-place not exact"
+        assert torch.equal(wb.view(torch.int16), want.view(torch.int16)), "verified not exact"
+    t_f, t_v, t_k = (float(np.median(x)) for x in (tf, tv, tk))
+    del recv_a, recv_b, fused, vf
+    return {"ms": round(1e3 * t_v, 4), "check_pass_ms": round(1e3 * t_k, 4),
+            "in_place_ms_same_rounds": round(1e3 * t_f, 4), "ratio_to_in_place": round(t_v / t_f, 4)}
 
 
 def remapped(bd, names, shapes, pairs, payloads, cs_new, cs_old, steps):
@@ -764,6 +808,13 @@ def main():
     log(f"compress with 256-byte slots: workspace {small_ws['workspace_pct_of_weights']}% of "
         f"the weights, {small_ws['ms']} ms ({small_ws['time_ratio']}x the full workspace)")
 
+    vf_info = None
+    if args.workload != "70b-half":   # two more receivers would not fit beside the 70B share
+        vf_info = verify_first(bd, pairs, payloads, cs_new, cs_old, 4)
+        vf_info["hbm_pct"] = round(100 * dec_alg / (vf_info["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 2)
+        log(f"verify-first decompress: {vf_info['ms']} ms ({vf_info['ratio_to_in_place']}x the "
+            f"in-place pass)")
+
     remap_info = None
     if not args.no_remapped and args.workload in ("7b", "70b-half"):
         from lossless_bf16_weight_xor_amd import synth
@@ -910,6 +961,7 @@ def main():
                                                    >= 60.0)},
         "change_rate_sweep": sweep,
         "compress_small_workspace": small_ws,
+        "decompress_verify_first": vf_info,
         "achievable": ceiling,
         "streamed_receiver": stream_info,
         "remapped_decompress": remap_info,

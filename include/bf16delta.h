@@ -246,6 +246,23 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count,
 int bf16d_decompress_noalloc(const bf16d_decompress_job *jobs, uint32_t count,
                              bf16d_result *results, hipStream_t stream);
 
+/* Verify-first decompress: the apply of bf16d_decompress split in two
+ * passes, so that the weights are never touched by a payload that fails.
+ * The first pass decodes every record and checks it, and sums the checksum
+ * of the would-be result (old weights XOR the mask) without storing
+ * anything; only jobs that pass (BF16D_OK) are then written, by a second
+ * pass that decodes the record again and reads, XORs and stores only the
+ * 16-byte chunks that change.  On BF16D_EFORMAT and BF16D_ECHECKSUM the
+ * weights are untouched (bf16d_decompress rolls them back instead, which
+ * ends with the same bits but writes them twice meanwhile).  It moves more
+ * bytes than the single in-place pass: the changed chunks are read twice
+ * and the payload decoded twice.  Arguments, statuses and results are those
+ * of bf16d_decompress_ex (events bracket the first pass's kernel).  NeMo-DCR
+ * summary: an update left placed wrongly or half-applied is unusable. */
+int bf16d_decompress_verified(const bf16d_decompress_job *jobs, uint32_t count,
+                              void *workspace, size_t workspace_bytes, bf16d_result *results,
+                              hipStream_t stream, const bf16d_events *events);
+
 /* Single-tensor forms of the two calls above, named after the pages'
  * delta_compress(src, dst) -> (payload, checksum) and
  * delta_decompress(src, payload, checksum) -> dst ("Every byte counts:

@@ -197,10 +197,16 @@ class DecompressBatch:
     checksum) triples.  `run()` enqueues it on the current stream."""
 
     def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
-                 versions: torch.Tensor | None = None):
+                 versions: torch.Tensor | None = None, verify_first: bool = False):
         """versions: None, or the receiver's version words, an int64 tensor of
         len(items) on the weights' device, checked against version-2 payloads
-        and advanced in place (bf16d_decompress_bound)."""
+        and advanced in place (bf16d_decompress_bound).
+        verify_first: check every job before writing it, so that a failing
+        payload never touches its weights (bf16d_decompress_verified; not
+        with version words)."""
+        if verify_first and versions is not None:
+            raise ValueError("verify_first is not offered with version words")
+        self.verify_first = verify_first
         if not items:
             raise ValueError("empty batch")
         self.device = items[0][0].device
@@ -247,9 +253,10 @@ class DecompressBatch:
             _check_rc(rc, "bf16d_decompress_bound")
             return
         ev = _events(events)
-        rc = _native.lib().bf16d_decompress_ex(self.jobs, self.count, self.workspace.data_ptr(),
-                                               self.ws_bytes, self.result_buf.data_ptr(),
-                                               _stream(self.device), ev)
+        fn = _native.lib().bf16d_decompress_verified if self.verify_first else \
+            _native.lib().bf16d_decompress_ex
+        rc = fn(self.jobs, self.count, self.workspace.data_ptr(), self.ws_bytes,
+                self.result_buf.data_ptr(), _stream(self.device), ev)
         _check_rc(rc, "bf16d_decompress")
 
     def results(self) -> list[dict]:
@@ -509,11 +516,12 @@ def compress_batch(pairs: Sequence[tuple[torch.Tensor, torch.Tensor]], bindings=
 
 
 def decompress_batch(items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
-                     versions: torch.Tensor | None = None) -> list[dict]:
+                     versions: torch.Tensor | None = None,
+                     verify_first: bool = False) -> list[dict]:
     """Apply several payloads in place in one batched call, optionally with the
-    receiver's version words (see DecompressBatch).  Returns the per-job
-    result dicts, without raising on per-job failures."""
-    batch = DecompressBatch(items, versions)
+    receiver's version words or verified first (see DecompressBatch).
+    Returns the per-job result dicts, without raising on per-job failures."""
+    batch = DecompressBatch(items, versions, verify_first)
     batch.run()
     return batch.results()
 

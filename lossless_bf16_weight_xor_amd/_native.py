@@ -27,7 +27,7 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes",
             "bf16d_status_string", "bf16d_format_version", "bf16d_codec_available",
             "bf16d_race_bound", "bf16d_race_compress", "bf16d_race_frame_info",
             "bf16d_race_decompress", "bf16d_compress_bound", "bf16d_decompress_bound",
-            "bf16d_decompress_noalloc", "bf16d_remap_plan_bytes", "bf16d_remap_map_bytes",
+            "bf16d_decompress_noalloc", "bf16d_decompress_verified", "bf16d_remap_plan_bytes", "bf16d_remap_map_bytes",
             "bf16d_remap_prepare", "bf16d_decompress_remapped_prepared")
 # the benchmark's measurement aids, in their own library (bf16delta_probe.h)
 PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta_probe.so")
@@ -163,6 +163,9 @@ def lib():
         L.bf16d_race_frame_info.restype = ctypes.c_int
         L.bf16d_race_decompress.argtypes = [ctypes.POINTER(RaceJob), u32, u32]
         L.bf16d_race_decompress.restype = ctypes.c_int
+        L.bf16d_decompress_verified.argtypes = [ctypes.POINTER(DecompressJob), u32, vp, sz, vp,
+                                                vp, ctypes.POINTER(Events)]
+        L.bf16d_decompress_verified.restype = ctypes.c_int
         L.bf16d_remap_plan_bytes.argtypes = [u32, u64]
         L.bf16d_remap_plan_bytes.restype = sz
         L.bf16d_remap_map_bytes.argtypes = [u64, u32]

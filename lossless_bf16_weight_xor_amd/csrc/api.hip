@@ -99,7 +99,7 @@ size_t decompress_table_bytes(const Layout &l, uint32_t count) {
 }
 
 void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
-                      const Layout &l, uint8_t *out) {
+                      const Layout &l, uint8_t *out, bool verify_first) {
     auto *dj = reinterpret_cast<DecompressJob *>(out);
     for (uint32_t j = 0; j < count; ++j) {
         dj[j].weights = (BF16D_GMEM uint16_t *)jobs[j].weights;
@@ -113,6 +113,7 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
         dj[j].segs = nullptr;
         dj[j].nsegs = 0;
         dj[j].version = nullptr;
+        dj[j].verify_first = verify_first ? 1u : 0u;
     }
     std::memcpy(out + (l.block_start - l.jobs), p.bstart.data(), 8 * p.bstart.size());
     std::memcpy(out + (l.dtile_start - l.jobs), p.dstart.data(), 8 * p.dstart.size());
@@ -127,7 +128,8 @@ namespace {
 // launch.
 int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
                     uint64_t *versions, uint32_t count, void *workspace, size_t workspace_bytes,
-                    bf16d_result *results, hipStream_t stream, const bf16d_events *events) {
+                    bf16d_result *results, hipStream_t stream, const bf16d_events *events,
+                    bool verify_first = false) {
     if (!jobs || count == 0 || !results || !workspace || !aligned16(workspace))
         return BF16D_EINVAL;
     if (versions && (reinterpret_cast<uintptr_t>(versions) & 7u) != 0) return BF16D_EINVAL;
@@ -168,7 +170,7 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     if (!ranges_disjoint(ranges)) return BF16D_EINVAL;
 
     std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
-    decompress_table(jobs, count, prep, l, host.data());
+    decompress_table(jobs, count, prep, l, host.data(), verify_first);
     if (versions) {
         auto *dj = reinterpret_cast<DecompressJob *>(host.data());
         for (uint32_t j = 0; j < count; ++j) dj[j].version = (BF16D_GMEM uint64_t *)(versions + j);
@@ -197,7 +199,7 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     rc = upload(workspace, host, l.jobs, stream);
     if (rc != BF16D_OK) return rc;
     return launch_decompress(l, static_cast<uint8_t *>(workspace), count, prep.tiles, prep.dtiles,
-                             results, stream, events) == hipSuccess
+                             results, stream, events, nullptr, verify_first) == hipSuccess
                ? BF16D_OK
                : BF16D_EHIP;
 }
@@ -515,6 +517,13 @@ int bf16d_decompress_bound(const bf16d_decompress_job *jobs, uint64_t *versions,
                            hipStream_t stream) {
     return decompress_call(jobs, nullptr, versions, count, workspace, workspace_bytes, results,
                            stream, nullptr);
+}
+
+int bf16d_decompress_verified(const bf16d_decompress_job *jobs, uint32_t count,
+                              void *workspace, size_t workspace_bytes, bf16d_result *results,
+                              hipStream_t stream, const bf16d_events *events) {
+    return decompress_call(jobs, nullptr, nullptr, count, workspace, workspace_bytes, results,
+                           stream, events, true);
 }
 
 int bf16d_decompress(const bf16d_decompress_job *jobs, uint32_t count, void *workspace,

@@ -245,7 +245,7 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
             p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + st.hdr + 4 * b);
             p.len_room = block_length(job.n, b) |
                          (uint32_t)(room < kRoomCap ? room : kRoomCap) << 14 |
-                         (st.ow ? kPlanOverwrite : 0u);
+                         (st.ow ? kPlanOverwrite : (job.verify_first ? kPlanVerifyFirst : 0u));
             p.block = (uint32_t)b;
         }
         plan[t] = p;
@@ -517,8 +517,14 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
 //   been read.
 //   kPass: kPassApply (XOR, store, checksum), kPassRollback (XOR again, store,
 //   no checksum), kPassVerify (overwrite record: checksum of the result, no
-//   store), kPassCommit (overwrite record: store, no checksum).
-enum : int { kPassApply = 0, kPassRollback = 1, kPassVerify = 2, kPassCommit = 3 };
+//   store), kPassCommit (overwrite record: store, no checksum),
+//   kPassVerifyXor (XOR record, verified first: checksum of old ^ mask, no
+//   store), kPassCommitXor (a verified XOR record: each changed chunk's old
+//   value loaded only now, XOR, store; no checksum).
+enum : int {
+    kPassApply = 0, kPassRollback = 1, kPassVerify = 2, kPassCommit = 3, kPassVerifyXor = 4,
+    kPassCommitXor = 5
+};
 
 template <int kPass>
 __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o)[kChunksPerThread],
@@ -527,8 +533,10 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                                             uint64_t *__restrict__ partial, uint16_t *s_x,
                                             uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
     constexpr bool kOw = kPass == kPassVerify || kPass == kPassCommit;
-    constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify;
-    constexpr bool kStore = kPass != kPassVerify;
+    constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify || kPass == kPassVerifyXor;
+    constexpr bool kStore = kPass != kPassVerify && kPass != kPassVerifyXor;
+    // a verified XOR record's commit reads only the changed chunks' old values
+    constexpr bool kLateOld = kPass == kPassCommitXor;
     // the commit writes each verified value at its position: absolute values
     // need neither the old weights nor the tile
     constexpr bool kDirect = kPass == kPassCommit;
@@ -747,9 +755,12 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
             const uint32_t z = tid >> 16;
             reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(z, z, z, z);
             if (!bad) {
-                nw = make_uint4(nw.x ^ t.x, nw.y ^ t.y, nw.z ^ t.z, nw.w ^ t.w);
                 BF16D_GMEM uint16_t *dstp = pe.w + e0;
-                if (valid == 8) {
+                if (kLateOld) nw = load_chunk(dstp, valid);
+                nw = make_uint4(nw.x ^ t.x, nw.y ^ t.y, nw.z ^ t.z, nw.w ^ t.w);
+                if (!kStore) {
+                    // verified first: the result is only summed
+                } else if (valid == 8) {
                     *reinterpret_cast<BF16D_GMEM uint4 *>(dstp) = nw;
                 } else {
                     for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
@@ -814,6 +825,7 @@ __device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
     auto fetch = [&](uint64_t u) -> ApplyPlan {
         if (u >= tiles) return none;
         ApplyPlan p = plan[u];
+        if (p.len_room & kPlanVerifyFirst) return none;   // committed by commit_kernel
         if (p.len_room & 0x3FFFu) {
             const DecompressState &st = state[p.job];
             if ((st.rollback | st.commit) == 0) p = none;
@@ -858,15 +870,24 @@ __device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
 // and the short last block of a tensor are compiled separately (see
 // load_old), so that the wave waits only for the record word before the
 // decode while the weight loads stay in flight.
-template <bool kFull, bool kOw>
+//   kPass: kPassApply, kPassVerify (overwrite record), kPassVerifyXor or
+//   kPassCommitXor (which reads no whole block: only the changed chunks,
+//   once the record is decoded).
+template <bool kFull, int kPass>
 __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
                                           DecompressState *__restrict__ state,
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
                                           uint32_t *s_raw, ApplyShared &sa) {
+    constexpr bool kOw = kPass == kPassVerify;
     const uint32_t tid = threadIdx.x;
     uint4 rv = load_record_word(pe, tid);
     uint4 o[kChunksPerThread];
-    load_old<kFull>(pe, o, tid);
+    if (kPass == kPassCommitXor) {
+#pragma unroll
+        for (uint32_t i = 0; i < kChunksPerThread; ++i) o[i] = make_uint4(0, 0, 0, 0);
+    } else {
+        load_old<kFull>(pe, o, tid);
+    }
     rv = fix_record_word(pe, rv, tid);
     if (pe.desc & 0x3FFFu) {   // changed elements: the decode needs a clear tile
         if (!kOw)   // (an overwrite tile is filled with the weights instead)
@@ -878,8 +899,8 @@ __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
     none.w = nullptr;
     none.rec = nullptr;
     none.desc = none.len_room = none.job = none.block = 0;
-    finish_tile<kOw ? kPassVerify : kPassApply>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state,
-                                                partial, s_x, s_raw, sa, tid);
+    finish_tile<kPass>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x, s_raw,
+                       sa, tid);
 }
 
 // The apply pass: one workgroup per tile, 8 workgroups per CU (20 KiB of
@@ -899,14 +920,38 @@ void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restric
     const uint32_t L = pe.len_room & 0x3FFFu;
     if (pe.len_room & kPlanOverwrite) {   // overwrite records: verified here, written later
         if (L == kBlock)
-            apply_one<true, true>(pe, tile, state, partial, s_x, s_raw, sa);
+            apply_one<true, kPassVerify>(pe, tile, state, partial, s_x, s_raw, sa);
         else if (L != 0)
-            apply_one<false, true>(pe, tile, state, partial, s_x, s_raw, sa);
+            apply_one<false, kPassVerify>(pe, tile, state, partial, s_x, s_raw, sa);
+    } else if (pe.len_room & kPlanVerifyFirst) {   // XOR records verified first
+        if (L == kBlock)
+            apply_one<true, kPassVerifyXor>(pe, tile, state, partial, s_x, s_raw, sa);
+        else if (L != 0)
+            apply_one<false, kPassVerifyXor>(pe, tile, state, partial, s_x, s_raw, sa);
     } else if (L == kBlock) {
-        apply_one<true, false>(pe, tile, state, partial, s_x, s_raw, sa);
+        apply_one<true, kPassApply>(pe, tile, state, partial, s_x, s_raw, sa);
     } else if (L != 0) {   // 0: the job was rejected
-        apply_one<false, false>(pe, tile, state, partial, s_x, s_raw, sa);
+        apply_one<false, kPassApply>(pe, tile, state, partial, s_x, s_raw, sa);
     }
+}
+
+// The second pass of a verify-first call: the XOR records of the jobs that
+// passed, one workgroup per tile as in the apply pass (so that 8 workgroups
+// per CU keep their changed chunks' loads in flight); each changed chunk's
+// old value is read only now, XOR-ed and stored.  Exits at once when no job
+// of the call passed.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void commit_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
+                   const Control *__restrict__ ctrl) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kBlock];        // dense XOR tile
+    __shared__ __attribute__((aligned(16))) uint32_t s_raw[kStageWords];  // staged record
+    __shared__ ApplyShared sa;
+    if (ctrl->any_commit_xor == 0) return;
+    const uint64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const ApplyPlan pe = plan[tile];
+    if ((pe.len_room & kPlanVerifyFirst) == 0 || (pe.len_room & 0x3FFFu) == 0) return;
+    if (state[pe.job].commit == 0) return;   // uniform: the job failed, nothing is written
+    apply_one<false, kPassCommitXor>(pe, tile, state, nullptr, s_x, s_raw, sa);
 }
 
 // After the finalize step: the rollback of failed XOR jobs (applying the same
@@ -948,11 +993,13 @@ __device__ void finalize_job(const DecompressJob *__restrict__ jobs,
         res.n_changed = st->sum_c;
         res.n_rare = st->sum_r;
         res.n_bitmap_blocks = st->n_bitmap;
-        if (st->ow) {
-            // overwrite: nothing was written yet; the fix-up pass writes it
+        if (st->ow || job.verify_first) {
+            // overwrite, or an XOR job verified first: nothing was written
+            // yet; the fix-up pass (overwrite) or the commit pass (XOR)
+            // writes it
             if (res.status == BF16D_OK) {
                 st->commit = 1;
-                atomicOr(&ctrl->any_commit, 1u);
+                atomicOr(st->ow ? &ctrl->any_commit : &ctrl->any_commit_xor, 1u);
             }
         } else if (res.status != BF16D_OK) {
             st->rollback = 1;
@@ -1011,7 +1058,8 @@ __global__ __launch_bounds__(kThreads) void sum_partials_kernel(
 
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                             const bf16d_events *events, const uint64_t *block_map) {
+                             const bf16d_events *events, const uint64_t *block_map,
+                             bool verify_first) {
     auto *ctrl = reinterpret_cast<Control *>(ws + l.control);
     auto *jobs = reinterpret_cast<const DecompressJob *>(ws + l.jobs);
     auto *bstart = reinterpret_cast<const uint64_t *>(ws + l.block_start);
@@ -1057,6 +1105,8 @@ hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint6
             jobs, dmap, state, partial, sums, ctrl, count, results);
         fixup_kernel<<<persistent_grid((const void *)fixup_kernel, tiles), kThreads, 0, stream>>>(
             plan, state, ctrl, tiles);
+        if (verify_first)
+            commit_kernel<<<(uint32_t)tiles, kThreads, 0, stream>>>(plan, state, ctrl);
     } else {
         decompress_finalize_kernel<<<(count + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
             jobs, state, sums, ctrl, count, results);

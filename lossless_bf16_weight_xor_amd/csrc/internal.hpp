@@ -106,6 +106,7 @@ struct alignas(64) DecompressJob {
     BF16D_GMEM const RemapSegment *segs;   // remapped: the job's segments; else nullptr
     uint32_t nsegs;             // 0: no remap, the weights pointer is used
     BF16D_GMEM uint64_t *version;   // the receiver's version word, or nullptr
+    uint32_t verify_first;      // XOR records: verified before anything is written
 };
 
 // per-job device state of a decompress call (zeroed by the setup kernel)
@@ -128,14 +129,16 @@ struct alignas(32) ApplyPlan {
     BF16D_GMEM const uint8_t *rec;   // first byte of the block's record
     uint32_t desc;        // the block's descriptor
     uint32_t len_room;    // block length (bits 0..13; 0 = skip the tile) | payload bytes
-                          // left from `rec`, capped at 2^17 - 1 (bits 14..30) |
-                          // kPlanOverwrite (bit 31): an overwrite record
+                          // left from `rec`, capped at 2^16 - 1 (bits 14..29) |
+                          // kPlanVerifyFirst (bit 30): an XOR record verified before
+                          // it is written | kPlanOverwrite (bit 31): an overwrite record
     uint32_t job;
     uint32_t block;       // block index within the job
 };
 static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
 constexpr uint32_t kPlanOverwrite = 1u << 31;
-constexpr uint32_t kRoomCap = (1u << 17) - 1;
+constexpr uint32_t kPlanVerifyFirst = 1u << 30;
+constexpr uint32_t kRoomCap = (1u << 16) - 1;   // above any record window (24 KiB + 15)
 
 // per-job sums (zeroed at the start of a call), accumulated with one atomic
 // per job and scan tile of 2048 blocks: the checksum sum S (both directions,
@@ -168,7 +171,8 @@ struct alignas(64) Control {
     uint32_t any_commit;      // decompress: some overwrite payload is to be written
     uint32_t scan_done;       // workgroups of the descriptor/offset scan that have finished
     uint32_t sum_done;        // decompress: workgroups of the checksum sum that have finished
-    uint32_t pad[9];
+    uint32_t any_commit_xor;  // decompress: some job verified first is to be written
+    uint32_t pad[8];
 };
 
 // Set-up of a batched call in one launch: zero fills and tile -> job maps.
@@ -565,7 +569,7 @@ int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, Decompress
                     const bf16d_remap *remaps = nullptr, bool mapped = false);
 size_t decompress_table_bytes(const Layout &l, uint32_t count);
 void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const DecompressPrep &p,
-                      const Layout &l, uint8_t *out);
+                      const Layout &l, uint8_t *out, bool verify_first = false);
 
 // workgroups of a persistent kernel: as many as fit on the device at once
 uint32_t persistent_grid(const void *kernel, uint64_t tiles, size_t dynamic_lds = 0);
@@ -577,5 +581,6 @@ hipError_t launch_compress(const Layout &l, uint8_t *ws, uint32_t count, uint64_
 // prepared once for a remapped layout (bf16d_remap_prepare)
 hipError_t launch_decompress(const Layout &l, uint8_t *ws, uint32_t count, uint64_t tiles,
                              uint64_t dtiles, bf16d_result *results, hipStream_t stream,
-                             const bf16d_events *events, const uint64_t *block_map = nullptr);
+                             const bf16d_events *events, const uint64_t *block_map = nullptr,
+                             bool verify_first = false);
 }  // namespace bf16d

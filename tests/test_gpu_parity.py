@@ -235,11 +235,11 @@ def injected():
     return src, dst, payload_np(payload), cs
 
 
-def _gpu_apply(src, payload_bytes: np.ndarray, cs):
+def _gpu_apply(src, payload_bytes: np.ndarray, cs, verify_first=False):
     w = src.clone()
     p = torch.from_numpy(payload_bytes.copy()).to(DEV) if payload_bytes.size else \
         torch.zeros(16, dtype=torch.uint8, device=DEV)[:0]
-    r = decompress_batch([(w, p, cs)])[0]
+    r = decompress_batch([(w, p, cs)], verify_first=verify_first)[0]
     return r["status"], w
 
 
@@ -248,8 +248,8 @@ def _oracle_apply(src, payload_bytes, cs):
     return oracle.decompress_inplace(w, payload_bytes, cs), w
 
 
-def _same_outcome(src, p, cs, what):
-    st_g, w_g = _gpu_apply(src, p, cs)
+def _same_outcome(src, p, cs, what, verify_first=False):
+    st_g, w_g = _gpu_apply(src, p, cs, verify_first)
     st_o, w_o = _oracle_apply(src, p, cs)
     assert st_g == st_o, f"{what}: status gpu {st_g} oracle {st_o}"
     assert np.array_equal(to_u16(w_g), w_o), f"{what}: weights differ from the oracle's"
@@ -355,3 +355,49 @@ def test_payload_applies_in_both_directions():
     w = dst.clone()
     delta_decompress(w, payload, cs_old)
     assert torch.equal(w.view(torch.int16), src.view(torch.int16))
+
+
+# ------------------------------------------------- verify-first decompress ---
+
+def test_verified_decompress_failures_match_the_oracle(injected):
+    """bf16d_decompress_verified: the same statuses and final weights as the
+    oracle for a wrong checksum, a wrong baseline, header and table
+    corruption, truncation and flipped record bits."""
+    src, dst, p, cs = injected
+    log("case verify-first failures")
+    assert _same_outcome(src, p, cs, "good", True) == OK
+    assert _same_outcome(src, p, cs ^ 1, "wrong checksum", True) == ECHECKSUM
+    bad = src.clone()
+    bad.view(torch.int16)[5] ^= 1
+    assert _same_outcome(bad, p, cs, "wrong baseline", True) == ECHECKSUM
+    for offset in (0, 8, 24, 64, 66):
+        q = p.copy()
+        q[offset] ^= 0x01
+        assert _same_outcome(src, q, cs, f"header byte {offset}", True) == EFORMAT
+    assert _same_outcome(src, p[:-7], cs, "truncated", True) == EFORMAT
+    start = pv.data_offset(src.numel())
+    for byte in range(start, min(start + 48, p.size)):
+        for bit in (0, 3, 6):
+            q = p.copy()
+            q[byte] ^= np.uint8(1 << bit)
+            assert _same_outcome(src, q, cs, f"byte {byte} bit {bit}", True) in (EFORMAT,
+                                                                                 ECHECKSUM)
+
+
+@pytest.mark.parametrize("rate", ["0.02", "0.3", "1"])
+def test_verified_decompress_batch_rebuilds_and_refuses(rate):
+    """A batch of ragged tensors (gap lists, bitmaps, short last blocks), the
+    second job with a wrong checksum: the others are rebuilt bit for bit and
+    the failing one is left exactly as it was."""
+    log(f"case verify-first batch rate={rate}")
+    pairs = [pair((n,), rate, synth.MIX_ADVERSARIAL, 8100 + k, DEV)
+             for k, n in enumerate((3 * 8192 + 77, 8192, 70001, 1, 5 * 8192))]
+    out = compress_batch(pairs)
+    ws = [s.clone() for s, _ in pairs]
+    items = [(w, p, cs) for w, (p, cs, _) in zip(ws, out)]
+    items[1] = (ws[1], out[1][0], out[1][1] ^ 0x77)
+    res = decompress_batch(items, verify_first=True)
+    assert [r["status"] for r in res] == [OK, ECHECKSUM, OK, OK, OK]
+    for j, (w, (s, d)) in enumerate(zip(ws, pairs)):
+        want = s if j == 1 else d
+        assert torch.equal(w.view(torch.int16), want.view(torch.int16)), j
