@@ -509,6 +509,18 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
         out["inplace_floor"] = {"ms": round(1e3 * t, 4), "elements": full,
                                 "dirty_chunks_pct": round(chunk_pct, 3),
                                 "dirty_lines_pct": round(line_pct, 3)}
+        # the same chunk writes alone, into the second array (no reads)
+        probe.probe_write(b, dirty)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            probe.probe_write(b, dirty)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out["write_changed_chunks_only"] = {
+            "ms": round(ev[0].elapsed_time(ev[1]) / steps, 4),
+            "note": "the in-place pass's writes alone (no reads): with read1 it splits the "
+                    "in-place floor into its two parts"}
         del dirty
     del a, b
     torch.cuda.empty_cache()

@@ -45,6 +45,18 @@ int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t 
 int bf16d_probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink,
                         uint64_t key, hipStream_t stream);
 
+/* Measurement aid: the in-place apply's writes with nothing else.  Writes
+ * (a pattern, not data) every 16-byte chunk c of the first 8192 *
+ * floor(n / 8192) elements of w whose bit (c & 31) of dirty[c >> 5] is set,
+ * in the blocks' XCD-aware order, and reads nothing from w: beside
+ * bf16d_probe_read of the same elements, its time shows how much of the
+ * in-place traffic is the scattered writes of the changed chunks.  w:
+ * device, 16-byte aligned, n elements, overwritten at the marked chunks (a
+ * scratch array); dirty as in bf16d_probe_inplace.  Returns BF16D_EINVAL for
+ * a NULL or misaligned pointer or more than 2^31 - 1 blocks; BF16D_EHIP if
+ * the launch fails; else BF16D_OK. */
+int bf16d_probe_write(uint16_t *w, uint64_t n, const uint32_t *dirty, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

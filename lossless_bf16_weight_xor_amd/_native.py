@@ -31,7 +31,7 @@ EXPORTED = ("bf16d_max_payload_bytes", "bf16d_workspace_bytes",
             "bf16d_remap_prepare", "bf16d_decompress_remapped_prepared")
 # the benchmark's measurement aids, in their own library (bf16delta_probe.h)
 PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbf16delta_probe.so")
-PROBE_EXPORTED = ("bf16d_probe_read", "bf16d_probe_inplace")
+PROBE_EXPORTED = ("bf16d_probe_read", "bf16d_probe_inplace", "bf16d_probe_write")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 CODECS = {"stored": 0, "zstd": 1, "lz4": 2, "lz4hc": 3, "zlib": 4, "brotli": 5, "xz": 6}
@@ -198,6 +198,8 @@ def probe_lib():
         L.bf16d_probe_read.restype = ctypes.c_int
         L.bf16d_probe_inplace.argtypes = [vp, u64, vp, vp, u64, vp]
         L.bf16d_probe_inplace.restype = ctypes.c_int
+        L.bf16d_probe_write.argtypes = [vp, u64, vp, vp]
+        L.bf16d_probe_write.restype = ctypes.c_int
         _probe_lib = L
     return _probe_lib
 

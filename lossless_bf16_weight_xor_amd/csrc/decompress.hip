@@ -257,7 +257,7 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
 // the 16-byte boundary at or before the record) are staged in LDS, one load
 // per thread; fields beyond are read from HBM (only dense blocks have such
 // long records).
-constexpr uint32_t kStageChunks = 252;
+constexpr uint32_t kStageChunks = 244;   // LDS: 16 KiB tile + 3904 + 192 = 20 KiB, 8 workgroups per CU
 constexpr uint32_t kStageWords = 4 * kStageChunks;
 
 // Bit reader over a record: window dwords [0, kStageWords - 1) come from LDS,
@@ -305,6 +305,7 @@ __device__ __forceinline__ uint32_t window_bits(uint32_t w0, uint32_t w1, uint32
 
 struct ApplyShared {
     uint32_t a[kWaves], b[kWaves], c[kWaves], f[kWaves];
+    uint32_t dirty[kChunks / 32];   // sparse tiles: one bit per 16-byte chunk with a change
 };
 
 // OR of `v` over the workgroup; also a barrier.  (The library's
@@ -405,12 +406,18 @@ constexpr uint32_t kFastFields = 4;
 
 //   kDirect: each value is stored straight to its weight (the commit of a
 //   verified overwrite record) instead of into s_x.
+//   sparse: the tile was not cleared beforehand (a tile of at most 256
+//   changes, decoded by wave 0 alone): the wave first zeroes the chunks its
+//   positions fall in and marks them in sa.dirty, then stores the values.
+//   Within the wave the zeroing stores all come before the value stores, so
+//   two positions in one chunk are safe.
 template <bool kOw, bool kDirect>
 __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint32_t c,
                                                       uint32_t r, uint32_t w, uint32_t L,
                                                       uint32_t mant0, uint32_t rare0,
                                                       uint16_t *s_x, ApplyShared &sa,
-                                                      uint32_t tid, BF16D_GMEM uint16_t *wts) {
+                                                      uint32_t tid, BF16D_GMEM uint16_t *wts,
+                                                      bool sparse = false) {
     const uint32_t lane = tid & 63, wave = tid >> 6;
     // A sparse block (at most 256 fields) is decoded by wave 0 alone: its
     // scans stay within the wave, with no exchange of totals between waves
@@ -481,6 +488,20 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
         }
     }
     uint32_t bad = (total_g1 - 1 >= L) | (esc_total != r) | (any_top == 0);
+    if (sparse) {   // uniform; only with `one`, so all of this is wave 0's
+        uint32_t r2 = run;
+#pragma unroll
+        for (uint32_t k = 0; k < kFastFields; ++k) {
+            if (k < nf) {
+                r2 += gk[k] + 1;
+                const uint32_t p = r2 - 1;
+                if (p < L) {
+                    reinterpret_cast<uint4 *>(s_x)[p >> 3] = make_uint4(0, 0, 0, 0);
+                    atomicOr(&sa.dirty[p >> 8], 1u << ((p >> 3) & 31));
+                }
+            }
+        }
+    }
 #pragma unroll
     for (uint32_t k = 0; k < kFastFields; ++k) {
         if (k < nf) {
@@ -526,7 +547,18 @@ enum : int {
     kPassCommitXor = 5
 };
 
-template <int kPass>
+// A tile of at most 256 changes in a gap list that lies wholly in the staged
+// window: wave 0 decodes it alone.  In the one-tile-per-workgroup passes it
+// is also `sparse`: its LDS tile is not cleared and read back whole, only
+// the chunks with changes (marked in a bitmap) are.
+__device__ __forceinline__ bool sparse_tile(const TileGeom &g) {
+    return g.code != kCodeBitmap && g.c != 0 && g.c <= 64 * kFastFields &&
+           g.lead + g.len + 12 <= 4 * kStageWords;
+}
+
+//   kSparseOk: the tile is not reused after this call (one tile per
+//   workgroup), so a sparse tile may leave s_x dirty.
+template <int kPass, bool kSparseOk = false>
 __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o)[kChunksPerThread],
                                             uint64_t tile, const ApplyPlan &next, uint4 rv_next,
                                             DecompressState *__restrict__ state,
@@ -543,6 +575,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const TileGeom g = tile_geom(pe, tid);
     const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
+    const bool sparse = kSparseOk && !kOw && sparse_tile(g);   // uniform
 
     RecordBits rb;
     rb.lds = s_raw;
@@ -568,7 +601,7 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
         if (code != kCodeBitmap && c <= kFastFields * kThreads &&
             g.lead + g.len + 12 <= 4 * kStageWords) {
             bad = decode_delta_fast<kOw, kDirect>(rb, c, r, code, L, mant0, rare0, s_x, sa, tid,
-                                                  pe.w);
+                                                  pe.w, sparse);
             if (tid == 0 && 8 * pb > c * code)               // position padding
                 bad |= rb.get(c * code, 8 * pb - c * code) != 0;
         } else if (code == kCodeBitmap) {
@@ -747,13 +780,16 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     for (uint32_t s = 0; s < valid; ++s) dstp[s] = (uint16_t)chunk_elem(nw, s);
                 }
             }
-        } else if (const uint4 t = changed ? reinterpret_cast<const uint4 *>(s_x)[q]
-                                           : make_uint4(0, 0, 0, 0);
+        } else if (const uint4 t = (changed && (!sparse || ((sa.dirty[q >> 5] >> (q & 31)) & 1u)))
+                                       ? reinterpret_cast<const uint4 *>(s_x)[q]
+                                       : make_uint4(0, 0, 0, 0);
                    (t.x | t.y | t.z | t.w) != 0) {   // dirty
-            // tid >> 16 is 0; written so the zero is not one more register
-            // held across the persistent loop
-            const uint32_t z = tid >> 16;
-            reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(z, z, z, z);
+            if (!kSparseOk) {
+                // tid >> 16 is 0; written so the zero is not one more
+                // register held across the persistent loop
+                const uint32_t z = tid >> 16;
+                reinterpret_cast<uint4 *>(s_x)[q] = make_uint4(z, z, z, z);
+            }
             if (!bad) {
                 BF16D_GMEM uint16_t *dstp = pe.w + e0;
                 if (kLateOld) nw = load_chunk(dstp, valid);
@@ -890,17 +926,22 @@ __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
     }
     rv = fix_record_word(pe, rv, tid);
     if (pe.desc & 0x3FFFu) {   // changed elements: the decode needs a clear tile
-        if (!kOw)   // (an overwrite tile is filled with the weights instead)
-            for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
-                reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+        if (!kOw) {   // (an overwrite tile is filled with the weights instead)
+            if (sparse_tile(tile_geom(pe, tid))) {   // uniform: only its chunks, marked
+                if (tid < kChunks / 32) sa.dirty[tid] = 0;
+            } else {
+                for (uint32_t u = tid; u < kBlock / 8; u += kThreads)
+                    reinterpret_cast<uint4 *>(s_x)[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
         stage_record_word(pe, rv, s_raw, tid);
     }
     ApplyPlan none;
     none.w = nullptr;
     none.rec = nullptr;
     none.desc = none.len_room = none.job = none.block = 0;
-    finish_tile<kPass>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x, s_raw,
-                       sa, tid);
+    finish_tile<kPass, true>(pe, o, tile, none, make_uint4(0, 0, 0, 0), state, partial, s_x,
+                             s_raw, sa, tid);
 }
 
 // The apply pass: one workgroup per tile, 8 workgroups per CU (20 KiB of

@@ -9,6 +9,11 @@
 // read ceiling of that pattern on the device, against which the encoder
 // (both checkpoints) and the apply pass (one) are compared.
 //
+// probe_write_kernel: the apply pass's writes alone: each 16-byte chunk a
+// bitmap marks is written, in the same block order, and nothing is read.
+// Beside the read probe it shows how the in-place traffic splits into reads
+// of every weight and writes of the changed chunks.
+//
 // probe_inplace_kernel: the apply pass's traffic with nothing else: the same
 // whole-block reads of one array, and each 16-byte chunk that a bitmap marks
 // written back, unchanged, in place.  Given the chunks a delta changes, its
@@ -94,6 +99,32 @@ int probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink
     return hipGetLastError() == hipSuccess ? BF16D_OK : BF16D_EHIP;
 }
 
+// dirty as in probe_inplace_kernel; each marked chunk of w is overwritten
+// (with a pattern derived from the bitmap), nothing is read from w.
+__global__ __launch_bounds__(kThreads) void probe_write_kernel(uint16_t *__restrict__ pw,
+                                                               const uint32_t *__restrict__ pd) {
+    auto *w = (BF16D_GMEM uint16_t *)pw;
+    auto *dirty = (BF16D_GMEM const uint32_t *)pd;
+    const uint64_t base = xcd_tile(blockIdx.x, gridDim.x) * kBlock;
+    const uint64_t word0 = base / 8 / 32;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunksPerThread; ++i) {
+        const uint32_t q = threadIdx.x + kThreads * i;
+        const uint32_t m = dirty[word0 + (q >> 5)];
+        if ((m >> (q & 31)) & 1u)
+            *reinterpret_cast<BF16D_GMEM uint4 *>(w + base + 8 * q) = make_uint4(m, q, m ^ q, ~m);
+    }
+}
+
+int probe_write(uint16_t *w, uint64_t n, const uint32_t *dirty, hipStream_t stream) {
+    const uint64_t blocks = n / kBlock;
+    if (!w || !dirty || ((uintptr_t)w & 15) || ((uintptr_t)dirty & 3) || blocks > 0x7FFFFFFFull)
+        return BF16D_EINVAL;
+    if (blocks == 0) return BF16D_OK;
+    probe_write_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(w, dirty);
+    return hipGetLastError() == hipSuccess ? BF16D_OK : BF16D_EHIP;
+}
+
 int probe_read(const uint16_t *a, const uint16_t *b, uint64_t n, uint64_t *sink, uint64_t key,
                hipStream_t stream) {
     const uint64_t blocks = n / kBlock;
@@ -118,4 +149,9 @@ extern "C" int bf16d_probe_read(const uint16_t *a, const uint16_t *b, uint64_t n
 extern "C" int bf16d_probe_inplace(uint16_t *w, uint64_t n, const uint32_t *dirty, uint64_t *sink,
                                    uint64_t key, hipStream_t stream) {
     return bf16d::probe_inplace(w, n, dirty, sink, key, stream);
+}
+
+extern "C" int bf16d_probe_write(uint16_t *w, uint64_t n, const uint32_t *dirty,
+                                 hipStream_t stream) {
+    return bf16d::probe_write(w, n, dirty, stream);
 }

@@ -48,3 +48,15 @@ def probe_inplace(w: torch.Tensor, dirty: torch.Tensor, sink: torch.Tensor | Non
     _check_rc(_native.probe_lib().bf16d_probe_inplace(pw, w.numel(), dirty.data_ptr(), sink.data_ptr(),
                                                 _PROBE_KEY, _stream(w.device)),
               "bf16d_probe_inplace")
+
+
+def probe_write(w: torch.Tensor, dirty: torch.Tensor) -> None:
+    """Measurement aid: write (a pattern) each 16-byte chunk of w that `dirty`
+    marks, read nothing (`bf16d_probe_write`); w is a scratch array."""
+    pw = _weights_ptr(w, "w")
+    if (dirty.device != w.device or dirty.dtype != torch.int32 or not dirty.is_contiguous()
+            or dirty.numel() < 32 * (w.numel() // BLOCK_ELEMS)):
+        raise ValueError("dirty must be a contiguous int32 tensor on w's device with 32 words "
+                         "per 8192-element block")
+    _check_rc(_native.probe_lib().bf16d_probe_write(pw, w.numel(), dirty.data_ptr(),
+                                                    _stream(w.device)), "bf16d_probe_write")

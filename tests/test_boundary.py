@@ -50,7 +50,8 @@ def test_the_measurement_aids_live_in_their_own_library(native):
     libbf16delta_probe.so only, not by the product library."""
     probe = ctypes.CDLL(native.PROBE_LIB_PATH)
     names = _declared_functions(PROBE_HEADER)
-    assert set(names) == set(native.PROBE_EXPORTED) == {"bf16d_probe_read", "bf16d_probe_inplace"}
+    assert set(names) == set(native.PROBE_EXPORTED) == {"bf16d_probe_read", "bf16d_probe_inplace",
+                                                        "bf16d_probe_write"}
     product = ctypes.CDLL(native.LIB_PATH)
     for name in names:
         assert hasattr(probe, name), name

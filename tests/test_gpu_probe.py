@@ -1,6 +1,7 @@
-"""The read-ceiling and in-place floor probes (measurement aids): argument
-checks, that they run over whole blocks, and that the in-place probe leaves
-its array as it was.  They compute nothing the method uses, so there is no
+"""The read-ceiling, in-place floor and write-only probes (measurement aids):
+argument checks, that they run over whole blocks, that the in-place probe
+leaves its array as it was, and that the write probe writes exactly the
+marked chunks.  They compute nothing the method uses, so there is no
 oracle value to compare; the checks are that they accept what they document
 and refuse the rest."""
 import pytest
@@ -10,6 +11,7 @@ import lossless_bf16_weight_xor_amd as bd
 from lossless_bf16_weight_xor_amd import _native, probe
 
 pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
 
 
 def test_probe_runs_over_one_and_two_arrays():
@@ -82,3 +84,23 @@ def test_inplace_probe_refuses_bad_arguments():
     with pytest.raises(ValueError):
         probe.probe_inplace(w, dirty.view(torch.int16), sink=sink)
     torch.cuda.synchronize()
+
+
+def test_write_probe_writes_exactly_the_marked_chunks():
+    """The write-only probe touches the marked 16-byte chunks of whole blocks
+    and nothing else."""
+    n = 3 * 8192 + 100
+    w = torch.zeros(n, dtype=torch.int16, device=DEV)
+    dirty = torch.zeros(32 * 3, dtype=torch.int32, device=DEV)
+    marked = [0, 5, 31, 32, 1023, 1024 + 7, 2 * 1024 + 1000]
+    for c in marked:
+        dirty[c >> 5] |= 1 << (c & 31)
+    probe.probe_write(w, dirty)
+    torch.cuda.synchronize()
+    got = (w.view(-1)[:3 * 8192].view(-1, 8) != 0).any(1).nonzero().flatten().tolist()
+    assert got == marked
+    assert int((w[3 * 8192:] != 0).sum()) == 0     # the partial last block is not a whole block
+    L = _native.probe_lib()
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.bf16d_probe_write(w.data_ptr() + 2, n, dirty.data_ptr(), s) == bd.EINVAL
+    assert L.bf16d_probe_write(w.data_ptr(), n, 0, s) == bd.EINVAL
