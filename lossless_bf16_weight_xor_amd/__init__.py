@@ -197,13 +197,17 @@ class DecompressBatch:
     checksum) triples.  `run()` enqueues it on the current stream."""
 
     def __init__(self, items: Sequence[tuple[torch.Tensor, torch.Tensor, int]],
-                 versions: torch.Tensor | None = None, verify_first: bool = False):
+                 versions: torch.Tensor | None = None, verify_first: bool = False,
+                 workspace_bytes_override: int | None = None):
         """versions: None, or the receiver's version words, an int64 tensor of
         len(items) on the weights' device, checked against version-2 payloads
         and advanced in place (bf16d_decompress_bound).
         verify_first: check every job before writing it, so that a failing
         payload never touches its weights (bf16d_decompress_verified; not
-        with version words)."""
+        with version words).
+        workspace_bytes_override: a workspace of this size instead of
+        bf16d_workspace_bytes (which leaves room for the undo area of
+        overwrite payloads; a smaller one verifies them first instead)."""
         if verify_first and versions is not None:
             raise ValueError("verify_first is not offered with version words")
         self.verify_first = verify_first
@@ -220,8 +224,10 @@ class DecompressBatch:
                 raise TypeError("versions must be a contiguous 64-bit tensor with one word "
                                 "per job on the weights' device")
         n_total = sum(w.numel() for w, _, _ in items)
-        self.ws_bytes = workspace_bytes(n_total, self.count)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.ws_bytes = workspace_bytes(n_total, self.count) if workspace_bytes_override is None \
+            else int(workspace_bytes_override)
+        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8,
+                                     device=self.device)
         self.result_buf = torch.empty(self.count * RESULT_BYTES, dtype=torch.uint8,
                                       device=self.device)
         self.jobs = (DecompressJob * self.count)()

@@ -114,6 +114,7 @@ void decompress_table(const bf16d_decompress_job *jobs, uint32_t count, const De
         dj[j].nsegs = 0;
         dj[j].version = nullptr;
         dj[j].verify_first = verify_first ? 1u : 0u;
+        dj[j].undo = nullptr;
     }
     std::memcpy(out + (l.block_start - l.jobs), p.bstart.data(), 8 * p.bstart.size());
     std::memcpy(out + (l.dtile_start - l.jobs), p.dstart.data(), 8 * p.dstart.size());
@@ -143,6 +144,15 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
     const size_t seg_at = align_up(l.total, 256);
     const size_t need = nsegs ? seg_at + sizeof(RemapSegment) * nsegs : l.total;
     if (workspace_bytes < need) return BF16D_EINVAL;
+    // room for an undo area (one byte per payload byte) lets overwrite
+    // payloads be written in place in one pass; without it they are verified
+    // first and written after
+    const size_t undo_at = align_up(need, 256);
+    size_t undo_bytes = 0;
+    for (uint32_t j = 0; j < count; ++j) undo_bytes += align_up(jobs[j].payload_bytes, 16);
+    const bool with_undo = !verify_first && workspace_bytes >= undo_at &&
+                           workspace_bytes - undo_at >= undo_bytes;
+    const size_t used = with_undo ? undo_at + undo_bytes : need;
     std::vector<Range> ranges;
     ranges.reserve(2 * size_t(count) + nsegs + 3);
     for (uint32_t j = 0; j < count; ++j) {
@@ -161,7 +171,7 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
                           reinterpret_cast<uintptr_t>(J.payload) + J.payload_bytes, false});
     }
     ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
-                      reinterpret_cast<uintptr_t>(workspace) + need, true});
+                      reinterpret_cast<uintptr_t>(workspace) + used, true});
     ranges.push_back({reinterpret_cast<uintptr_t>(results),
                       reinterpret_cast<uintptr_t>(results + count), true});
     if (versions)
@@ -171,6 +181,14 @@ int decompress_call(const bf16d_decompress_job *jobs, const bf16d_remap *remaps,
 
     std::vector<uint8_t> host(decompress_table_bytes(l, count), 0);
     decompress_table(jobs, count, prep, l, host.data(), verify_first);
+    if (with_undo) {
+        auto *dj = reinterpret_cast<DecompressJob *>(host.data());
+        size_t at = undo_at;
+        for (uint32_t j = 0; j < count; ++j) {
+            dj[j].undo = (BF16D_GMEM uint8_t *)(static_cast<uint8_t *>(workspace) + at);
+            at += align_up(jobs[j].payload_bytes, 16);
+        }
+    }
     if (versions) {
         auto *dj = reinterpret_cast<DecompressJob *>(host.data());
         for (uint32_t j = 0; j < count; ++j) dj[j].version = (BF16D_GMEM uint64_t *)(versions + j);

@@ -86,6 +86,10 @@ __device__ void prepare_job(const DecompressJob *__restrict__ jobs,
     st->hdr = hdr;
     st->ow = ow;
     st->bound = bound;
+    st->undo = ow && job.undo != nullptr;
+    st->undo_delta = st->undo ? (long long)((uintptr_t)job.undo -
+                                            (uintptr_t)(job.payload + hdr + 4 * job.nb))
+                              : 0;
     st->state = !ok ? kStateRejected : (wrong_version ? kStateVersion : kStateReady);
 }
 
@@ -245,7 +249,8 @@ __global__ void plan_kernel(const DecompressJob *__restrict__ jobs,
             p.desc = *reinterpret_cast<BF16D_GMEM const uint32_t *>(job.payload + st.hdr + 4 * b);
             p.len_room = block_length(job.n, b) |
                          (uint32_t)(room < kRoomCap ? room : kRoomCap) << 14 |
-                         (st.ow ? kPlanOverwrite : (job.verify_first ? kPlanVerifyFirst : 0u));
+                         (st.ow ? kPlanOverwrite | (st.undo ? kPlanUndo : 0u)
+                                : (job.verify_first ? kPlanVerifyFirst : 0u));
             p.block = (uint32_t)b;
         }
         plan[t] = p;
@@ -411,13 +416,17 @@ constexpr uint32_t kFastFields = 4;
 //   positions fall in and marks them in sa.dirty, then stores the values.
 //   Within the wave the zeroing stores all come before the value stores, so
 //   two positions in one chunk are safe.
-template <bool kOw, bool kDirect>
+//   kUndo (overwrite records): 1 = keep each replaced value (the tile holds
+//   the old weights) in undo[j] before the new one goes in; 2 = write undo[j]
+//   back (with kDirect: the restore of a failed in-place overwrite).
+template <bool kOw, bool kDirect, int kUndo = 0>
 __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint32_t c,
                                                       uint32_t r, uint32_t w, uint32_t L,
                                                       uint32_t mant0, uint32_t rare0,
                                                       uint16_t *s_x, ApplyShared &sa,
                                                       uint32_t tid, BF16D_GMEM uint16_t *wts,
-                                                      bool sparse = false) {
+                                                      bool sparse = false,
+                                                      BF16D_GMEM uint16_t *undo = nullptr) {
     const uint32_t lane = tid & 63, wave = tid >> 6;
     // A sparse block (at most 256 fields) is decoded by wave 0 alone: its
     // scans stay within the wave, with no exchange of totals between waves
@@ -517,12 +526,14 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
                 }
                 ++e;
             }
-            if (p >= L)
+            if (p >= L) {
                 bad = 1;
-            else if (kDirect)
-                wts[p] = (uint16_t)x;
-            else
+            } else if (kDirect) {
+                wts[p] = kUndo == 2 ? undo[jb + k] : (uint16_t)x;
+            } else {
+                if (kUndo == 1) undo[jb + k] = s_x[p];
                 s_x[p] = (uint16_t)x;
+            }
         }
     }
     return bad;
@@ -542,9 +553,12 @@ __device__ __forceinline__ uint32_t decode_delta_fast(const RecordBits &rb, uint
 //   kPassVerifyXor (XOR record, verified first: checksum of old ^ mask, no
 //   store), kPassCommitXor (a verified XOR record: each changed chunk's old
 //   value loaded only now, XOR, store; no checksum).
+//   kPassOwUndo (overwrite record, in place: each replaced value kept in the
+//   undo area, result stored and summed), kPassOwRestore (a failed in-place
+//   overwrite: the kept values written back; no checksum).
 enum : int {
     kPassApply = 0, kPassRollback = 1, kPassVerify = 2, kPassCommit = 3, kPassVerifyXor = 4,
-    kPassCommitXor = 5
+    kPassCommitXor = 5, kPassOwUndo = 6, kPassOwRestore = 7
 };
 
 // A tile of at most 256 changes in a gap list that lies wholly in the staged
@@ -564,18 +578,29 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                                             DecompressState *__restrict__ state,
                                             uint64_t *__restrict__ partial, uint16_t *s_x,
                                             uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
-    constexpr bool kOw = kPass == kPassVerify || kPass == kPassCommit;
-    constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify || kPass == kPassVerifyXor;
+    constexpr bool kOw = kPass == kPassVerify || kPass == kPassCommit || kPass == kPassOwUndo ||
+                         kPass == kPassOwRestore;
+    constexpr bool kSum = kPass == kPassApply || kPass == kPassVerify || kPass == kPassVerifyXor ||
+                          kPass == kPassOwUndo;
     constexpr bool kStore = kPass != kPassVerify && kPass != kPassVerifyXor;
     // a verified XOR record's commit reads only the changed chunks' old values
     constexpr bool kLateOld = kPass == kPassCommitXor;
-    // the commit writes each verified value at its position: absolute values
-    // need neither the old weights nor the tile
-    constexpr bool kDirect = kPass == kPassCommit;
+    // the commit writes each verified value at its position, and the restore
+    // each kept value: absolute values need neither the old weights nor the
+    // tile
+    constexpr bool kDirect = kPass == kPassCommit || kPass == kPassOwRestore;
+    constexpr int kUndo = kPass == kPassOwUndo ? 1 : (kPass == kPassOwRestore ? 2 : 0);
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const TileGeom g = tile_geom(pe, tid);
     const uint32_t L = g.L, c = g.c, r = g.r, code = g.code, pb = g.pb, mb = g.mb;
     const bool sparse = kSparseOk && !kOw && sparse_tile(g);   // uniform
+    // the tile's undo range: its record's offset within the job's records,
+    // in the job's undo area (made even: ranges of neighbouring tiles still
+    // do not overlap, as a record of c changes is at least 2c bytes)
+    BF16D_GMEM uint16_t *undo = nullptr;
+    if (kUndo)
+        undo = (BF16D_GMEM uint16_t *)(((uintptr_t)pe.rec + state[pe.job].undo_delta) &
+                                       ~(uintptr_t)1);
 
     RecordBits rb;
     rb.lds = s_raw;
@@ -600,8 +625,8 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
         __syncthreads();   // record staged; s_x clear (overwrite: s_x = the weights)
         if (code != kCodeBitmap && c <= kFastFields * kThreads &&
             g.lead + g.len + 12 <= 4 * kStageWords) {
-            bad = decode_delta_fast<kOw, kDirect>(rb, c, r, code, L, mant0, rare0, s_x, sa, tid,
-                                                  pe.w, sparse);
+            bad = decode_delta_fast<kOw, kDirect, kUndo>(rb, c, r, code, L, mant0, rare0, s_x,
+                                                         sa, tid, pe.w, sparse, undo);
             if (tid == 0 && 8 * pb > c * code)               // position padding
                 bad |= rb.get(c * code, 8 * pb - c * code) != 0;
         } else if (code == kCodeBitmap) {
@@ -678,10 +703,18 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     }
                     ++e;
                 }
-                if (kDirect)
-                    pe.w[p] = (uint16_t)x;
-                else
+                // a malformed bitmap may set more than c bits: the undo range
+                // of the tile holds c entries, so ranks from c on are not kept
+                // (nothing of a malformed block is stored) nor restored
+                if (kDirect) {
+                    if (kUndo != 2)
+                        pe.w[p] = (uint16_t)x;
+                    else if (jj < c)
+                        pe.w[p] = undo[jj];
+                } else {
+                    if (kUndo == 1 && jj < c) undo[jj] = s_x[p];
                     s_x[p] = (uint16_t)x;
+                }
                 ++jj;
             }
         } else {
@@ -735,12 +768,14 @@ __device__ __forceinline__ void finish_tile(const ApplyPlan &pe, const uint4 (&o
                     }
                     ++e;
                 }
-                if (p >= L)
+                if (p >= L) {
                     bad = 1;
-                else if (kDirect)
-                    pe.w[p] = (uint16_t)x;
-                else
+                } else if (kDirect) {
+                    pe.w[p] = kUndo == 2 ? undo[jj] : (uint16_t)x;
+                } else {
+                    if (kUndo == 1) undo[jj] = s_x[p];
                     s_x[p] = (uint16_t)x;
+                }
             }
             if (tid == 0 && 8 * pb > c * w)                  // position padding
                 bad |= rb.get(c * w, 8 * pb - c * w) != 0;
@@ -826,7 +861,8 @@ __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
                                           uint32_t *s_raw, ApplyShared &sa, uint32_t tid) {
     uint4 o[kChunksPerThread];
-    if (kPass == kPassCommit) {   // writes values only: the old weights are not read
+    if (kPass == kPassCommit || kPass == kPassOwRestore) {   // writes values only: the
+                                                             // old weights are not read
 #pragma unroll
         for (uint32_t i = 0; i < kChunksPerThread; ++i) o[i] = make_uint4(0, 0, 0, 0);
     } else {
@@ -861,7 +897,9 @@ __device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
     auto fetch = [&](uint64_t u) -> ApplyPlan {
         if (u >= tiles) return none;
         ApplyPlan p = plan[u];
-        if (p.len_room & kPlanVerifyFirst) return none;   // committed by commit_kernel
+        // XOR records verified first are committed by commit_kernel (the
+        // same bit on an overwrite record means an in-place one: restored here)
+        if ((p.len_room & (kPlanOverwrite | kPlanVerifyFirst)) == kPlanVerifyFirst) return none;
         if (p.len_room & 0x3FFFu) {
             const DecompressState &st = state[p.job];
             if ((st.rollback | st.commit) == 0) p = none;
@@ -885,7 +923,9 @@ __device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
         const ApplyPlan pnn = fetch(t + 2 * G);
         const uint32_t L = pc.len_room & 0x3FFFu;
         const bool ow = (pc.len_room & kPlanOverwrite) != 0;
-        if (L == kBlock && ow)
+        if (L != 0 && ow && (pc.len_room & kPlanUndo))   // a failed in-place overwrite
+            pass_step<kPassOwRestore, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
+        else if (L == kBlock && ow)
             pass_step<kPassCommit, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
         else if (L == kBlock)
             pass_step<kPassRollback, true>(pc, pn, t, state, partial, s_x, s_raw, sa, tid);
@@ -914,7 +954,7 @@ __device__ __forceinline__ void apply_one(const ApplyPlan &pe, uint64_t tile,
                                           DecompressState *__restrict__ state,
                                           uint64_t *__restrict__ partial, uint16_t *s_x,
                                           uint32_t *s_raw, ApplyShared &sa) {
-    constexpr bool kOw = kPass == kPassVerify;
+    constexpr bool kOw = kPass == kPassVerify || kPass == kPassOwUndo;
     const uint32_t tid = threadIdx.x;
     uint4 rv = load_record_word(pe, tid);
     uint4 o[kChunksPerThread];
@@ -959,7 +999,13 @@ void apply_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restric
     const uint64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const ApplyPlan pe = plan[tile];
     const uint32_t L = pe.len_room & 0x3FFFu;
-    if (pe.len_room & kPlanOverwrite) {   // overwrite records: verified here, written later
+    if ((pe.len_room & (kPlanOverwrite | kPlanUndo)) == (kPlanOverwrite | kPlanUndo)) {
+        // overwrite records written in place, the replaced values kept
+        if (L == kBlock)
+            apply_one<true, kPassOwUndo>(pe, tile, state, partial, s_x, s_raw, sa);
+        else if (L != 0)
+            apply_one<false, kPassOwUndo>(pe, tile, state, partial, s_x, s_raw, sa);
+    } else if (pe.len_room & kPlanOverwrite) {   // overwrite records: verified, written later
         if (L == kBlock)
             apply_one<true, kPassVerify>(pe, tile, state, partial, s_x, s_raw, sa);
         else if (L != 0)
@@ -990,7 +1036,9 @@ void commit_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restri
     if (ctrl->any_commit_xor == 0) return;
     const uint64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const ApplyPlan pe = plan[tile];
-    if ((pe.len_room & kPlanVerifyFirst) == 0 || (pe.len_room & 0x3FFFu) == 0) return;
+    if ((pe.len_room & (kPlanOverwrite | kPlanVerifyFirst)) != kPlanVerifyFirst ||
+        (pe.len_room & 0x3FFFu) == 0)
+        return;
     if (state[pe.job].commit == 0) return;   // uniform: the job failed, nothing is written
     apply_one<false, kPassCommitXor>(pe, tile, state, nullptr, s_x, s_raw, sa);
 }
@@ -1034,7 +1082,13 @@ __device__ void finalize_job(const DecompressJob *__restrict__ jobs,
         res.n_changed = st->sum_c;
         res.n_rare = st->sum_r;
         res.n_bitmap_blocks = st->n_bitmap;
-        if (st->ow || job.verify_first) {
+        if (st->ow && st->undo) {
+            // written in place: a failure restores the kept values
+            if (res.status != BF16D_OK) {
+                st->rollback = 1;
+                atomicOr(&ctrl->any_rollback, 1u);
+            }
+        } else if (st->ow || job.verify_first) {
             // overwrite, or an XOR job verified first: nothing was written
             // yet; the fix-up pass (overwrite) or the commit pass (XOR)
             // writes it

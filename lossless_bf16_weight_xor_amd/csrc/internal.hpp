@@ -107,6 +107,10 @@ struct alignas(64) DecompressJob {
     uint32_t nsegs;             // 0: no remap, the weights pointer is used
     BF16D_GMEM uint64_t *version;   // the receiver's version word, or nullptr
     uint32_t verify_first;      // XOR records: verified before anything is written
+    // overwrite records: an undo area laid out like the job's records (the
+    // old value of a record's j-th change at record offset + 2j), or nullptr
+    // (then an overwrite job is verified first and written after)
+    BF16D_GMEM uint8_t *undo;
 };
 
 // per-job device state of a decompress call (zeroed by the setup kernel)
@@ -120,6 +124,8 @@ struct alignas(64) DecompressState {
     uint32_t hdr;          // header bytes of the payload (set by the prepare kernel)
     uint32_t ow;           // an overwrite payload
     uint32_t bound;        // a version-2 payload
+    uint32_t undo;         // overwrite, written in place with an undo log (set by prepare)
+    long long undo_delta;  // undo area minus the start of the job's records (bytes)
 };
 
 // decompress: everything the apply pass needs about one tile, gathered once
@@ -138,6 +144,9 @@ struct alignas(32) ApplyPlan {
 static_assert(sizeof(ApplyPlan) == 32, "ApplyPlan is two 16-byte words");
 constexpr uint32_t kPlanOverwrite = 1u << 31;
 constexpr uint32_t kPlanVerifyFirst = 1u << 30;
+// with kPlanOverwrite, the same bit: an overwrite record written in place
+// with an undo log (instead of verified first)
+constexpr uint32_t kPlanUndo = kPlanVerifyFirst;
 constexpr uint32_t kRoomCap = (1u << 16) - 1;   // above any record window (24 KiB + 15)
 
 // per-job sums (zeroed at the start of a call), accumulated with one atomic

@@ -181,3 +181,57 @@ def test_plain_decompress_reads_bound_payloads_without_the_binding():
     assert [r["status"] for r in res] == [bd.OK, bd.OK]
     for w, (_, d) in zip(recv, pairs):
         assert torch.equal(w.view(torch.int16), d.view(torch.int16))
+
+
+def _smallest_workspace(items, versions):
+    """The smallest workspace the call accepts (no room for an undo area):
+    found by bisection on the host-side size check, which refuses a short
+    workspace before enqueueing anything."""
+    lo, hi = 0, bd.workspace_bytes(sum(w.numel() for w, _, _ in items), len(items))
+    while hi - lo > 256:
+        mid = (lo + hi) // 2 // 256 * 256
+        batch = bd.DecompressBatch(items, versions, workspace_bytes_override=mid)
+        try:
+            batch.run()
+            hi = mid
+        except RuntimeError:
+            lo = mid
+        torch.cuda.synchronize()
+    return hi
+
+
+@pytest.mark.parametrize("room", ["undo", "none"])
+def test_overwrite_in_place_and_verified_first_end_alike(room):
+    """Overwrite payloads are written in place with an undo log when the
+    workspace has room for it, and verified first otherwise.  Either way:
+    the oracle's statuses, the new weights on OK, and the weights exactly as
+    they were (partly written or not) on a failure."""
+    log(f"case overwrite room={room}")
+    shapes = [((3 * 8192 + 5,), "0.05"), ((8192,), "0.3"), ((2 * 8192 + 1,), "0.6"),
+              ((70001,), "0.02"), ((4096,), "1.0")]
+    pairs = [tuple(t.reshape(-1) for t in _pair(sh, r, 70 + i)) for i, (sh, r) in
+             enumerate(shapes)]
+    out = bd.compress_batch(pairs, [(7, 8, True)] * len(pairs))
+    payloads = [p.clone() for p, _, _ in out]
+    checksums = [cs for _, cs, _ in out]
+    checksums[1] ^= 1                       # wrong checksum
+    payloads[3][-1] ^= 0x10                 # a corrupt value: the checksum fails
+    recv = [s.clone() for s, _ in pairs]
+    s4, d4 = pairs[4]
+    recv[4] = torch.where(torch.arange(s4.numel(), device=DEV) % 3 == 0, d4, s4)  # partly written
+    start = [to_u16(w).copy() for w in recv]
+    ver = _versions([7] * len(pairs))
+    items = [(w, p, cs) for w, p, cs in zip(recv, payloads, checksums)]
+    override = None if room == "undo" else _smallest_workspace(items, ver)
+    ver = _versions([7] * len(pairs))
+    res = bd.DecompressBatch(items, ver, workspace_bytes_override=override)
+    res.run()
+    res = res.results()
+    got_ver = ver.cpu().tolist()
+    for j in range(len(pairs)):
+        w = start[j].copy()
+        want, want_ver = oracle.decompress_v2_inplace(w, payload_np(payloads[j]), checksums[j], 7)
+        assert res[j]["status"] == want, f"job {j}: {res[j]['status']} vs oracle {want}"
+        assert got_ver[j] == want_ver, f"job {j}: version"
+        assert np.array_equal(to_u16(recv[j]), w), f"job {j}: weights"
+    assert [r["status"] for r in res] == [bd.OK, bd.ECHECKSUM, bd.OK, bd.ECHECKSUM, bd.OK]
