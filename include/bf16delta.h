@@ -328,11 +328,17 @@ int bf16d_compress_bound(const bf16d_compress_job *jobs, const bf16d_binding *bi
  *   - BF16D_OK for a version-2 payload: versions[i] = target_version,
  *     written together with the weights; on any other status it is kept;
  *   - a version-1 payload leaves versions[i] alone.
- * An overwrite payload is verified before anything is written (its checksum
- * is that of the would-be result) and then written: the weights end new on
- * BF16D_OK and untouched on any other status.  bf16d_decompress and the
+ * An overwrite payload ends with the weights new on BF16D_OK and exactly as
+ * they were before the call (partly written or not) on any other status.
+ * When the workspace has room beyond the call's own layout for an undo area
+ * of one byte per payload byte (bf16d_workspace_bytes leaves it for any
+ * sparse delta), it is applied in place in one pass and each replaced value
+ * is kept in the undo area; a job that fails is then restored from it.
+ * Without that room it is verified first (its checksum is that of the
+ * would-be result) and written after, which reads and decodes the payload
+ * twice.  This holds in bf16d_decompress too.  bf16d_decompress and the
  * streamed and remapped calls read version-2 payloads too, without checking
- * the binding. */
+ * the binding (the streamed and remapped calls always verify first). */
 int bf16d_decompress_bound(const bf16d_decompress_job *jobs, uint64_t *versions, uint32_t count,
                            void *workspace, size_t workspace_bytes, bf16d_result *results,
                            hipStream_t stream);
