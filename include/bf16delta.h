@@ -338,7 +338,8 @@ int bf16d_compress_bound(const bf16d_compress_job *jobs, const bf16d_binding *bi
  * would-be result) and written after, which reads and decodes the payload
  * twice.  This holds in bf16d_decompress too.  bf16d_decompress and the
  * streamed and remapped calls read version-2 payloads too, without checking
- * the binding (the streamed and remapped calls always verify first). */
+ * the binding (the streamed call and the prepared remapped call always
+ * verify overwrite payloads first). */
 int bf16d_decompress_bound(const bf16d_decompress_job *jobs, uint64_t *versions, uint32_t count,
                            void *workspace, size_t workspace_bytes, bf16d_result *results,
                            hipStream_t stream);
