@@ -470,14 +470,13 @@ def dirty_chunks(pairs, n, dev):
     return packed.view(torch.int32), chunk_pct, line_pct
 
 
-def read_ceiling(bd, n, dev, steps, pairs=None):
+def read_ceiling(bd, n, dev, steps, dirty=None):
     """The read ceiling of the encoder's access pattern (bf16d_probe_read: one
     workgroup per 8192-element block, 16-byte loads, nothing else) over two
     flat n-element arrays, as the encoder reads old and new, and over one, as
     the apply pass reads old.  Their contents do not matter.  With the
-    workload's pairs, also the in-place floor (bf16d_probe_inplace): the same
-    reads of one array plus, written back unchanged, every 16-byte chunk that
-    the workload's delta changes."""
+    workload's changed-chunk bitmap, also the apply pass's writes alone
+    (bf16d_probe_write: the changed 16-byte chunks, no reads)."""
     from lossless_bf16_weight_xor_amd import probe
     a = torch.empty(n, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
@@ -496,20 +495,7 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
         nbytes = (2 if arrays[1] is not None else 1) * 2 * full
         out[key] = {"bytes": nbytes, "ms": round(1e3 * t, 4), "gbps": round(nbytes / t / 1e9, 2),
                     "pct_of_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBPS, 2)}
-    if pairs is not None:
-        dirty, chunk_pct, line_pct = dirty_chunks(pairs, n, dev)
-        probe.probe_inplace(a, dirty, sink=sink)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(steps):
-            probe.probe_inplace(a, dirty, sink=sink)
-        ev[1].record()
-        torch.cuda.synchronize()
-        t = ev[0].elapsed_time(ev[1]) / 1e3 / steps
-        out["inplace_floor"] = {"ms": round(1e3 * t, 4), "elements": full,
-                                "dirty_chunks_pct": round(chunk_pct, 3),
-                                "dirty_lines_pct": round(line_pct, 3)}
-        # the same chunk writes alone, into the second array (no reads)
+    if dirty is not None:
         probe.probe_write(b, dirty)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
@@ -519,12 +505,54 @@ def read_ceiling(bd, n, dev, steps, pairs=None):
         torch.cuda.synchronize()
         out["write_changed_chunks_only"] = {
             "ms": round(ev[0].elapsed_time(ev[1]) / steps, 4),
-            "note": "the in-place pass's writes alone (no reads): with read1 it splits the "
+            "note": "the apply pass's writes alone (no reads); with read1 it splits the "
                     "in-place floor into its two parts"}
-        del dirty
     del a, b
     torch.cuda.empty_cache()
     return out
+
+
+def flat_receiver(tensors, dev):
+    """Copies of `tensors` laid end to end in one buffer, as views (None and
+    plain clones if some tensor's size is not a multiple of 8 elements, which
+    would leave a view off a 16-byte boundary)."""
+    if any(t.numel() % 8 for t in tensors):
+        return None, [t.clone() for t in tensors]
+    buf = torch.empty(sum(t.numel() for t in tensors), dtype=torch.int16, device=dev)
+    views, at = [], 0
+    for t in tensors:
+        v = buf[at:at + t.numel()]
+        v.copy_(t.reshape(-1).view(torch.int16))
+        views.append(v.view(t.dtype))
+        at += t.numel()
+    return buf, views
+
+
+def apply_against_floor(decompress_once, check, rbuf, dirty, rounds):
+    """apply_kernel and the in-place floor probe, timed in the same rounds
+    over the same memory.  Each round is one verified decompress of the
+    workload (its apply kernel between HIP events), then bf16d_probe_inplace
+    over the receiver's buffer: every whole block read, and every 16-byte
+    chunk that the delta changes written back unchanged, with nothing
+    decoded."""
+    from lossless_bf16_weight_xor_amd import probe
+    n = dirty.numel() // 32 * 8192
+    sink = torch.empty(1, dtype=torch.int64, device=rbuf.device)
+    ta, tp = [], []
+    for i in range(rounds + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        decompress_once((e[0], e[1]))
+        torch.cuda.synchronize()
+        check()
+        e[2].record()
+        probe.probe_inplace(rbuf[:n], dirty, sink=sink)
+        e[3].record()
+        torch.cuda.synchronize()
+        if i >= 1:
+            ta.append(e[0].elapsed_time(e[1]))
+            tp.append(e[2].elapsed_time(e[3]))
+    return {"ms": round(float(np.median(tp)), 4), "elements": n, "rounds": rounds,
+            "apply_kernel_same_rounds_ms": round(float(np.median(ta)), 4)}
 
 
 def dirty_write_units(pairs):
@@ -543,14 +571,18 @@ def dirty_write_units(pairs):
     return sectors, lines
 
 
-def change_rate_sweep(bd, dev, steps):
+def change_rate_sweep(bd, dev, steps, with_floor=True):
     """Compress and verified in-place decompress of one 1 GiB tensor
     (536,870,912 elements, uniform changes, 95/4.5/0.5) at each change rate
     of the sweep, timed like the main step: whole calls and their main
     kernels, with events on the call's stream.  Each rate's payload is the
     same bytes twice over the timed calls (checked), and the receiver ends
-    bit-exact."""
+    bit-exact.  With `with_floor`, every round also times the in-place floor
+    probe over the receiver (its reads plus the changed chunks written back
+    unchanged)."""
     from lossless_bf16_weight_xor_amd import synth
+    if with_floor:
+        from lossless_bf16_weight_xor_amd import probe
     out = []
     for rate in synth.C3_RATES:
         src, dst = synth.config3(dev, rate)
@@ -568,11 +600,13 @@ def change_rate_sweep(bd, dev, steps):
         del rev
         recv = src.clone()
         dec = bd.DecompressBatch([(recv, payload, cs_new)])
-        tc, te, td, ta = [], [], [], []
+        dirty = dirty_chunks([(src, dst)], n, dev)[0] if with_floor else None
+        sink = torch.empty(1, dtype=torch.int64, device=dev)
+        tc, te, td, ta, tp = [], [], [], [], []
         direction = 0
         for i in range(steps + 2):
             dec.jobs[0].checksum = cs_new if direction == 0 else cs_old
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
             e[0].record()
             comp.run(events=(e[1], e[2]))
             e[3].record()
@@ -581,11 +615,19 @@ def change_rate_sweep(bd, dev, steps):
             torch.cuda.synchronize()
             assert dec.results()[0]["status"] == bd.OK, f"sweep {rate}: decompress"
             direction ^= 1
+            if dirty is not None:
+                # the in-place floor over the receiver itself, in the same round
+                e[7].record()
+                probe.probe_inplace(recv, dirty, sink=sink)
+                e[8].record()
+                torch.cuda.synchronize()
             if i >= 2:
                 tc.append(e[0].elapsed_time(e[3]) / 1e3)
                 te.append(e[1].elapsed_time(e[2]) / 1e3)
                 td.append(e[3].elapsed_time(e[6]) / 1e3)
                 ta.append(e[4].elapsed_time(e[5]) / 1e3)
+                if dirty is not None:
+                    tp.append(e[7].elapsed_time(e[8]) / 1e3)
         assert torch.equal(payload, ref), f"sweep {rate}: payload changed between calls"
         want = dst if direction == 1 else src
         assert torch.equal(recv.view(torch.int16), want.view(torch.int16)), f"sweep {rate}"
@@ -604,10 +646,14 @@ def change_rate_sweep(bd, dev, steps):
             "apply_kernel_frac": round(da / ta_ / 1e9 / HBM_PEAK_GBPS, 4),
             "dirty_sectors_pct": round(100 * sectors / (n / 16), 3),
             "dirty_lines_pct": round(100 * lines / (n / 64), 3)})
+        if tp:
+            out[-1]["inplace_floor_ms"] = round(1e3 * float(np.median(tp)), 4)
+            out[-1]["apply_kernel_frac_of_inplace_floor"] = round(
+                float(np.median(tp)) / float(np.median(ta)), 4)
         log(f"sweep {rate}: compress {out[-1]['compress_ms']} ms "
             f"({out[-1]['compress_hbm_pct']}%), decompress {out[-1]['decompress_ms']} ms "
             f"({out[-1]['decompress_hbm_pct']}%)")
-        del comp, dec, recv, payload, ref, src, dst
+        del comp, dec, recv, payload, ref, src, dst, dirty
         torch.cuda.empty_cache()
     return out
 
@@ -746,7 +792,9 @@ def main():
     assert same, "reverse payload differs"
     del rev
 
-    receiver = [s.clone() for s, _ in pairs]
+    # the receiver: the old tensors laid end to end in one buffer, so the
+    # in-place floor probe can later run over the memory the apply pass writes
+    rbuf, receiver = flat_receiver([s for s, _ in pairs], dev)
     dec = bd.DecompressBatch([(w, p, c) for w, p, c in zip(receiver, payloads, cs_new)])
     torch.cuda.synchronize()
     log(f"payload {payload_total} B ({100 * payload_total / (2 * n_total):.3f}% of orig), "
@@ -754,10 +802,13 @@ def main():
 
     direction = [0]   # 0: receiver holds old, 1: it holds new
 
-    def step(ev=None):
+    def set_checksums():
         cs = cs_new if direction[0] == 0 else cs_old
         for j in range(len(cs)):
             dec.jobs[j].checksum = cs[j]
+
+    def step(ev=None):
+        set_checksums()
         if ev: ev[0].record()
         comp.run(events=(ev[1], ev[2]) if ev else None)
         if ev: ev[3].record()
@@ -784,10 +835,13 @@ def main():
     dres = dec.results()
     assert all(r["status"] == bd.OK for r in dres), "decompress failed in the timed region"
     assert all(r["status"] == bd.OK for r in comp.results()), "compress failed in the timed region"
-    expect_new = direction[0] == 1
-    for w, (s, d) in zip(receiver, pairs):
-        ref = d if expect_new else s
-        assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "receiver not bit-exact"
+    def check_receiver():
+        expect_new = direction[0] == 1
+        for w, (s, d) in zip(receiver, pairs):
+            ref = d if expect_new else s
+            assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), "receiver not bit-exact"
+
+    check_receiver()
 
     def durations(a, b):
         return [evs[i][a].elapsed_time(evs[i][b]) / 1e3 for i in range(args.steps)]
@@ -807,6 +861,28 @@ def main():
     # 32-byte sector (and 128-byte line) holding a change is written
     dirty_sectors, dirty_lines = dirty_write_units(pairs)
     dec_eff = 2 * n_total + payload_total + 32 * dirty_sectors
+
+    # the changed 16-byte chunks (for the probes), then the apply kernel and
+    # the in-place floor in the same rounds over the receiver's memory
+    dirty = floor = None
+    if not args.no_probe:
+        dirty, chunk_pct, line_pct = dirty_chunks(pairs, n_total // 8192 * 8192, dev)
+        if rbuf is not None:
+            def decompress_once(events):
+                set_checksums()
+                dec.run(events=events)
+                direction[0] ^= 1
+
+            def check_statuses():
+                assert all(r["status"] == bd.OK for r in dec.results()), "decompress failed"
+
+            floor = apply_against_floor(decompress_once, check_statuses, rbuf, dirty, 6)
+            floor["dirty_chunks_pct"] = round(chunk_pct, 3)
+            floor["dirty_lines_pct"] = round(line_pct, 3)
+            check_receiver()
+            log(f"in-place floor over the receiver: {floor['ms']} ms, apply kernel in the same "
+                f"rounds {floor['apply_kernel_same_rounds_ms']} ms "
+                f"({floor['dirty_lines_pct']}% of 128-byte lines written)")
 
     if args.with_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -884,26 +960,26 @@ def main():
     # free slows the streamed receiver's copies for some seconds
     sweep = None
     if not args.no_sweep and args.workload == "7b":
-        sweep = change_rate_sweep(bd, dev, 5)
+        sweep = change_rate_sweep(bd, dev, 5, with_floor=not args.no_probe)
 
     # last of the GPU measurements: it frees two checkpoint-sized buffers
     ceiling = None
     if not args.no_probe:
         ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2),
-                               pairs)
+                               dirty if n_total <= 8_000_000_000 else None)
+        del dirty
         ceiling["encode_kernel_frac_of_read2"] = round(comp_alg / t_enc / 1e9 /
                                                        ceiling["read2"]["gbps"], 4)
         ceiling["apply_kernel_frac_of_read1"] = round(dec_alg / t_app / 1e9 /
                                                       ceiling["read1"]["gbps"], 4)
         log(f"read ceiling: {ceiling['read2']['gbps']} GB/s over two arrays, "
             f"{ceiling['read1']['gbps']} GB/s over one")
-        # (the probe covers whole 8192-element blocks of the flat array: all
-        # but the last few thousand elements of the workload)
-        if "inplace_floor" in ceiling and ceiling["inplace_floor"]["elements"] >= 0.999 * n_total:
+        # (the probe covers whole 8192-element blocks of the receiver's buffer:
+        # all but the last few thousand elements of the workload)
+        if floor is not None and floor["elements"] >= 0.999 * n_total:
+            ceiling["inplace_floor"] = floor
             ceiling["apply_kernel_frac_of_inplace_floor"] = round(
-                ceiling["inplace_floor"]["ms"] / (1e3 * t_app), 4)
-            log(f"in-place floor: {ceiling['inplace_floor']['ms']} ms "
-                f"({ceiling['inplace_floor']['dirty_lines_pct']}% of 128-byte lines written)")
+                floor["ms"] / floor["apply_kernel_same_rounds_ms"], 4)
 
     gpu_payloads = [None] * len(pairs)
     cpu = None
