@@ -747,7 +747,14 @@ def main():
                     help="skip the change-rate sweep (one 1 GiB tensor at 0.085/1/3/5 %%)")
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--main-only", action="store_true",
+                    help="the main step and its probes only (profiling): none of the other "
+                         "measurements, so every compress and decompress kernel launched is "
+                         "one of the main workload's")
     args = ap.parse_args()
+    if args.main_only:
+        args.no_streamed = args.no_remapped = args.no_bound = args.no_race = True
+        args.no_sweep = True
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the delta path is "
                           "per-GPU (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
@@ -892,12 +899,15 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    small_ws = small_workspace(bd, pairs, comp, res, 5)
-    log(f"compress with 256-byte slots: workspace {small_ws['workspace_pct_of_weights']}% of "
-        f"the weights, {small_ws['ms']} ms ({small_ws['time_ratio']}x the full workspace)")
+    small_ws = None
+    if not args.main_only:
+        small_ws = small_workspace(bd, pairs, comp, res, 5)
+        log(f"compress with 256-byte slots: workspace {small_ws['workspace_pct_of_weights']}% "
+            f"of the weights, {small_ws['ms']} ms ({small_ws['time_ratio']}x the full workspace)")
 
     vf_info = None
-    if args.workload != "70b-half":   # two more receivers would not fit beside the 70B share
+    # (two more receivers would not fit beside the 70B share)
+    if args.workload != "70b-half" and not args.main_only:
         vf_info = verify_first(bd, pairs, payloads, cs_new, cs_old, 4)
         vf_info["hbm_pct"] = round(100 * dec_alg / (vf_info["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 2)
         log(f"verify-first decompress: {vf_info['ms']} ms ({vf_info['ratio_to_in_place']}x the "
