@@ -878,9 +878,10 @@ __device__ __forceinline__ void pass_step(const ApplyPlan &pc, const ApplyPlan &
 // been requested; the next tile's record is staged in LDS as soon as this
 // one's has been read, so its decode can start at once.  LDS is kept at
 // 20 KiB so that 8 workgroups (8 waves per SIMD) fit on a CU.
-// It visits the tiles of jobs marked for rollback (an XOR pass again) and of
-// overwrite jobs that passed verification (their values written); the tile's
-// plan entry says which.
+// It visits the tiles of jobs marked for rollback (an XOR pass again, or, for
+// an overwrite payload applied in place, the replaced values written back
+// from the undo area) and of overwrite jobs that passed verification (their
+// values written); the tile's plan entry says which.
 __device__ __forceinline__ void fixup_pass(const ApplyPlan *__restrict__ plan,
                                            DecompressState *__restrict__ state,
                                            uint64_t *__restrict__ partial, uint64_t tiles) {
@@ -1044,10 +1045,12 @@ void commit_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restri
 }
 
 // After the finalize step: the rollback of failed XOR jobs (applying the same
-// mask again restores the old weights exactly) and the writing of verified
-// overwrite payloads, in one persistent pass that exits at once when there
-// is neither.  Absolute values cannot be undone by applying them twice, so
-// they are written only once the whole result is known to be right.
+// mask again restores the old weights exactly), the restore of failed
+// overwrite jobs applied in place (from their undo area) and the writing of
+// verified overwrite payloads, in one persistent pass that exits at once when
+// there is none of these.  Absolute values cannot be undone by applying them
+// twice, so without an undo area they are written only once the whole result
+// is known to be right.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void fixup_kernel(const ApplyPlan *__restrict__ plan, DecompressState *__restrict__ state,
                   const Control *__restrict__ ctrl, uint64_t tiles) {
