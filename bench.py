@@ -574,12 +574,19 @@ def dirty_write_units(pairs):
 def change_rate_sweep(bd, dev, steps, with_floor=True):
     """Compress and verified in-place decompress of one 1 GiB tensor
     (536,870,912 elements, uniform changes, 95/4.5/0.5) at each change rate
-    of the sweep, timed like the main step: whole calls and their main
-    kernels, with events on the call's stream.  Each rate's payload is the
-    same bytes twice over the timed calls (checked), and the receiver ends
-    bit-exact.  With `with_floor`, every round also times the in-place floor
-    probe over the receiver (its reads plus the changed chunks written back
-    unchanged)."""
+    of the sweep: whole calls and their main kernels, with events on the
+    call's stream.  Each rate's payload is the same bytes over all the calls
+    (checked), and the receiver ends bit-exact.
+
+    A kernel that writes leaves dirty lines in the caches, and their
+    write-back lands in whatever runs next; on a 1 GiB call that is a
+    sizeable share.  With `with_floor` (the probe library), every timed
+    kernel starts after an untimed read of 1 GiB of other memory, so each is
+    charged its own traffic only, and every round also times the in-place
+    floor probe over the receiver (its reads plus the changed chunks written
+    back unchanged) and the read ceiling over old and new
+    (bf16d_probe_read).  Every round also times a compress right after the
+    decompress, as the main step runs them."""
     from lossless_bf16_weight_xor_amd import synth
     if with_floor:
         from lossless_bf16_weight_xor_amd import probe
@@ -600,60 +607,90 @@ def change_rate_sweep(bd, dev, steps, with_floor=True):
         del rev
         recv = src.clone()
         dec = bd.DecompressBatch([(recv, payload, cs_new)])
-        dirty = dirty_chunks([(src, dst)], n, dev)[0] if with_floor else None
         sink = torch.empty(1, dtype=torch.int64, device=dev)
-        tc, te, td, ta, tp = [], [], [], [], []
+        dirty = flush_buf = None
+        if with_floor:
+            dirty = dirty_chunks([(src, dst)], n, dev)[0]
+            flush_buf = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+
+        def flush():
+            if flush_buf is not None:
+                probe.probe_read(flush_buf, None, sink=sink)
+
+        t = {k: [] for k in ("call_c", "enc", "call_d", "app", "call_c2", "enc2", "floor",
+                             "read2")}
         direction = 0
         for i in range(steps + 2):
-            dec.jobs[0].checksum = cs_new if direction == 0 else cs_old
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+            flush()
             e[0].record()
             comp.run(events=(e[1], e[2]))
             e[3].record()
-            dec.run(events=(e[4], e[5]))
-            e[6].record()
+            flush()
+            dec.jobs[0].checksum = cs_new if direction == 0 else cs_old
+            e[4].record()
+            dec.run(events=(e[5], e[6]))
+            e[7].record()
+            # the main step's order: a compress right after a decompress
+            e[8].record()
+            comp.run(events=(e[9], e[10]))
+            e[11].record()
             torch.cuda.synchronize()
             assert dec.results()[0]["status"] == bd.OK, f"sweep {rate}: decompress"
             direction ^= 1
-            if dirty is not None:
-                # the in-place floor over the receiver itself, in the same round
-                e[7].record()
+            if with_floor:
+                flush()
+                e[12].record()
                 probe.probe_inplace(recv, dirty, sink=sink)
-                e[8].record()
+                e[13].record()
+                flush()
+                e[14].record()
+                probe.probe_read(src, dst, sink=sink)
+                e[15].record()
                 torch.cuda.synchronize()
             if i >= 2:
-                tc.append(e[0].elapsed_time(e[3]) / 1e3)
-                te.append(e[1].elapsed_time(e[2]) / 1e3)
-                td.append(e[3].elapsed_time(e[6]) / 1e3)
-                ta.append(e[4].elapsed_time(e[5]) / 1e3)
-                if dirty is not None:
-                    tp.append(e[7].elapsed_time(e[8]) / 1e3)
+                for k, (x, y) in (("call_c", (0, 3)), ("enc", (1, 2)), ("call_d", (4, 7)),
+                                  ("app", (5, 6)), ("call_c2", (8, 11)), ("enc2", (9, 10))):
+                    t[k].append(e[x].elapsed_time(e[y]) / 1e3)
+                if with_floor:
+                    t["floor"].append(e[12].elapsed_time(e[13]) / 1e3)
+                    t["read2"].append(e[14].elapsed_time(e[15]) / 1e3)
         assert torch.equal(payload, ref), f"sweep {rate}: payload changed between calls"
         want = dst if direction == 1 else src
         assert torch.equal(recv.view(torch.int16), want.view(torch.int16)), f"sweep {rate}"
         sectors, lines = dirty_write_units([(src, dst)])
         ca, da = 4 * n + P, 2 * n + P + 2 * c
-        tc_, te_, td_, ta_ = (float(np.mean(x)) for x in (tc, te, td, ta))
+        m = {k: float(np.median(v)) for k, v in t.items() if v}
         out.append({
             "rate": rate, "elements": n, "payload_pct_of_orig": round(100 * P / (2 * n), 4),
-            "compress_ms": round(1e3 * tc_, 4),
-            "compress_hbm_pct": round(100 * ca / tc_ / 1e9 / HBM_PEAK_GBPS, 2),
-            "encode_kernel_ms": round(1e3 * te_, 4),
-            "encode_kernel_frac": round(ca / te_ / 1e9 / HBM_PEAK_GBPS, 4),
-            "decompress_ms": round(1e3 * td_, 4),
-            "decompress_hbm_pct": round(100 * da / td_ / 1e9 / HBM_PEAK_GBPS, 2),
-            "apply_kernel_ms": round(1e3 * ta_, 4),
-            "apply_kernel_frac": round(da / ta_ / 1e9 / HBM_PEAK_GBPS, 4),
+            "caches_flushed_before_each_kernel": with_floor,
+            "compress_ms": round(1e3 * m["call_c"], 4),
+            "compress_hbm_pct": round(100 * ca / m["call_c"] / 1e9 / HBM_PEAK_GBPS, 2),
+            "encode_kernel_ms": round(1e3 * m["enc"], 4),
+            "encode_kernel_frac": round(ca / m["enc"] / 1e9 / HBM_PEAK_GBPS, 4),
+            "compress_after_decompress_ms": round(1e3 * m["call_c2"], 4),
+            "compress_after_decompress_hbm_pct": round(
+                100 * ca / m["call_c2"] / 1e9 / HBM_PEAK_GBPS, 2),
+            "encode_kernel_after_decompress_ms": round(1e3 * m["enc2"], 4),
+            "decompress_ms": round(1e3 * m["call_d"], 4),
+            "decompress_hbm_pct": round(100 * da / m["call_d"] / 1e9 / HBM_PEAK_GBPS, 2),
+            "apply_kernel_ms": round(1e3 * m["app"], 4),
+            "apply_kernel_frac": round(da / m["app"] / 1e9 / HBM_PEAK_GBPS, 4),
             "dirty_sectors_pct": round(100 * sectors / (n / 16), 3),
             "dirty_lines_pct": round(100 * lines / (n / 64), 3)})
-        if tp:
-            out[-1]["inplace_floor_ms"] = round(1e3 * float(np.median(tp)), 4)
-            out[-1]["apply_kernel_frac_of_inplace_floor"] = round(
-                float(np.median(tp)) / float(np.median(ta)), 4)
+        if with_floor:
+            out[-1]["inplace_floor_ms"] = round(1e3 * m["floor"], 4)
+            out[-1]["apply_kernel_frac_of_inplace_floor"] = round(m["floor"] / m["app"], 4)
+            out[-1]["read2_ms"] = round(1e3 * m["read2"], 4)
+            out[-1]["encode_kernel_frac_of_read2"] = round(m["read2"] / m["enc"], 4)
         log(f"sweep {rate}: compress {out[-1]['compress_ms']} ms "
-            f"({out[-1]['compress_hbm_pct']}%), decompress {out[-1]['decompress_ms']} ms "
-            f"({out[-1]['decompress_hbm_pct']}%)")
-        del comp, dec, recv, payload, ref, src, dst, dirty
+            f"({out[-1]['compress_hbm_pct']}%; {out[-1]['compress_after_decompress_ms']} ms "
+            f"right after a decompress), decompress {out[-1]['decompress_ms']} ms "
+            f"({out[-1]['decompress_hbm_pct']}%)"
+            + (f"; encode_kernel {out[-1]['encode_kernel_frac_of_read2']} of the read ceiling, "
+               f"apply_kernel {out[-1]['apply_kernel_frac_of_inplace_floor']} of the in-place "
+               f"floor" if with_floor else ""))
+        del comp, dec, recv, payload, ref, src, dst, dirty, flush_buf
         torch.cuda.empty_cache()
     return out
 
