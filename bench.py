@@ -1093,7 +1093,14 @@ def main():
                                 "dirty_lines_pct": round(100 * dirty_lines * 64 / n_total, 3),
                                 "target_pct": 60.0,
                                 "target_met": bool(100 * dec_alg / td / 1e9 / HBM_PEAK_GBPS
-                                                   >= 60.0)},
+                                                   >= 60.0),
+                                # the kernel against the in-place floor probe (the same
+                                # reads and changed-chunk writes, nothing else), timed in
+                                # the same rounds over the same buffer
+                                "inplace_floor_ms": floor["ms"] if floor else None,
+                                "frac_of_inplace_floor": (
+                                    round(floor["ms"] / floor["apply_kernel_same_rounds_ms"], 4)
+                                    if floor else None)},
         "change_rate_sweep": sweep,
         "compress_small_workspace": small_ws,
         "decompress_verify_first": vf_info,
