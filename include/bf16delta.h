@@ -68,6 +68,8 @@
  *   - `stream` is a HIP stream; NULL means the null stream.  All device work
  *     is enqueued on it, and results[] is valid once the stream has
  *     completed.
+ *   - Element counts and byte sizes (n, capacity, payload_bytes) are at
+ *     most 2^62; larger values are refused with BF16D_EINVAL.
  *   - The return value reports only errors the host can detect before
  *     enqueueing anything:
  *       BF16D_EINVAL  bad pointer, alignment, size, overlap, or a workspace

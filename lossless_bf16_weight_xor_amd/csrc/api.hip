@@ -15,6 +15,7 @@ using namespace bf16d;
 namespace {
 
 constexpr uint64_t kMaxTiles = 1ull << 24;   // grid limit: tiles * 256 threads < 2^32
+constexpr uint64_t kMaxSize = UINT64_MAX >> 2;   // element counts and byte sizes: at most 2^62
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,7 +62,7 @@ bool remap_valid(const bf16d_remap &m, uint64_t n) {
     for (uint32_t k = 0; k < m.count; ++k) {
         const bf16d_segment &g = m.segments[k];
         if (g.first != at || g.first % kBlock != 0 || g.count == 0 || !g.dst ||
-            !aligned16(g.dst) || g.count > (UINT64_MAX >> 2) - at)
+            !aligned16(g.dst) || g.count > kMaxSize - at)
             return false;
         if (k + 1 < m.count && g.count % kBlock != 0) return false;
         at += g.count;
@@ -84,7 +85,9 @@ int decompress_prep(const bf16d_decompress_job *jobs, uint32_t count, Decompress
         }
         // an empty payload may be NULL; it is then rejected on the device as too short
         if ((J.payload_bytes > 0 && !J.payload) || !aligned16(J.payload)) return BF16D_EINVAL;
-        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        // sizes beyond 2^62 cannot describe real buffers, and would wrap the
+        // address arithmetic of the overlap checks
+        if (J.n > kMaxSize || J.payload_bytes > kMaxSize) return BF16D_EINVAL;
         const uint64_t nb = blocks_of(J.n);
         p.bstart[j + 1] = p.bstart[j] + nb;
         p.dstart[j + 1] = p.dstart[j] + (nb + kDescTile - 1) / kDescTile;
@@ -282,7 +285,7 @@ int bf16d_remap_prepare(const bf16d_decompress_job *jobs, const bf16d_remap *rem
     uint64_t tiles = 0;
     for (uint32_t j = 0; j < count; ++j) {
         const bf16d_decompress_job &J = jobs[j];
-        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        if (J.n > kMaxSize) return BF16D_EINVAL;
         if (remaps && remaps[j].count > 0) {
             if (J.weights || !remap_valid(remaps[j], J.n)) return BF16D_EINVAL;
             for (uint32_t k = 0; k < remaps[j].count; ++k) {
@@ -444,7 +447,9 @@ int compress_call(const bf16d_compress_job *jobs, const bf16d_binding *bindings,
         if (J.n > 0 && (!J.src || !J.dst || !aligned16(J.src) || !aligned16(J.dst)))
             return BF16D_EINVAL;
         if (J.capacity > 0 && (!J.payload || !aligned16(J.payload))) return BF16D_EINVAL;
-        if (J.n > (UINT64_MAX >> 2)) return BF16D_EINVAL;
+        // records may be staged anywhere below `capacity`: it must describe
+        // a real buffer (and not wrap the overlap checks' address arithmetic)
+        if (J.n > kMaxSize || J.capacity > kMaxSize) return BF16D_EINVAL;
         start[j + 1] = start[j] + blocks_of(J.n);
         dstart[j + 1] = dstart[j] + (blocks_of(J.n) + kDescTile - 1) / kDescTile;
         ranges.push_back({reinterpret_cast<uintptr_t>(J.src),

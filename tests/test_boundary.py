@@ -140,6 +140,31 @@ def test_invalid_arguments_are_rejected_before_any_gpu_work(native):
                                 ws_ptr + 16, None) == native.EINVAL          # in the weights
 
 
+def test_sizes_beyond_two_to_the_62_are_refused(native):
+    """A capacity or payload size so large that buffer + size wraps the
+    address space would slip past the overlap checks (and compress stages
+    records just below `capacity`): such sizes are refused before any GPU
+    work.  Without the check these calls would go on to the runtime."""
+    lib = native.lib()
+    res = (native.Result * 1)()
+    ws = ctypes.create_string_buffer(1 << 16)
+    ws_ptr = (ctypes.addressof(ws) + 15) // 16 * 16
+    need = lib.bf16d_workspace_bytes(16, 1)
+    wrap = (1 << 64) - 4096
+    job = native.CompressJob(ws_ptr, ws_ptr + 64, 16, ws_ptr + 128, wrap)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, need,
+                              ctypes.addressof(res), None) == native.EINVAL
+    job = native.CompressJob(ws_ptr, ws_ptr + 64, 16, ws_ptr + 128, (1 << 62) + 1)
+    assert lib.bf16d_compress(ctypes.byref(job), 1, ws_ptr + 8192, need,
+                              ctypes.addressof(res), None) == native.EINVAL
+    djob = native.DecompressJob(ws_ptr, 16, ws_ptr + 128, wrap, 0)
+    assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, need,
+                                ctypes.addressof(res), None) == native.EINVAL
+    djob = native.DecompressJob(ws_ptr, (1 << 62) + 1, ws_ptr + 128, 64, 0)
+    assert lib.bf16d_decompress(ctypes.byref(djob), 1, ws_ptr + 8192, need,
+                                ctypes.addressof(res), None) == native.EINVAL
+
+
 def test_python_api_refuses_cpu_tensors(native):
     import torch
     from lossless_bf16_weight_xor_amd import delta_compress
