@@ -241,9 +241,11 @@ int bf16d_decompress_ex(const bf16d_decompress_job *jobs, uint32_t count,
  * memory before the call returns, as in bf16d_decompress.  Calls share
  * their GPU's scratch, so two calls that overlap in time on one GPU (for
  * example on two streams) race and give undefined results; calls in one
- * stream's order are safe.  Each call clears what it needs cleared, so the
- * contents left by the previous call do not matter.  This call allocates no
- * device memory. */
+ * stream's order are safe.  Each call clears what it needs cleared (with a
+ * kernel, not a memset), so the contents left by the previous call do not
+ * matter.  This call allocates no device memory.  It is not meant for HIP
+ * graph capture: its job table goes up with an asynchronous copy from a host
+ * buffer that the call frees before it returns. */
 #define BF16D_NOALLOC_SCRATCH_BYTES (64u << 20)
 int bf16d_decompress_noalloc(const bf16d_decompress_job *jobs, uint32_t count,
                              bf16d_result *results, hipStream_t stream);
