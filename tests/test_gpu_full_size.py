@@ -10,8 +10,10 @@ in-place decompress (`DecompressBatch`).
 - 70B-shaped half model (360 tensors, 3.4e10 elements): every tensor is
   compared with the oracle, byte for byte.  Every tensor is also checked by
   properties that hold at any size: the exact class counts the generator
-  planted, the round trip, and a payload that depends only on the XOR mask
-  (compressing new -> old gives the same bytes).
+  planted, the round trip, a payload that depends only on the XOR mask
+  (compressing new -> old gives the same bytes), and the same payloads from
+  a compress with 256-byte record slots.
+- The 7B-shaped checkpoint is also rebuilt by the verify-first call.
 
 The oracle is single-threaded; the checkpoints' tensors are compared on a
 pool of host threads (the oracle's C calls run without the interpreter lock),
@@ -128,6 +130,16 @@ def test_config2_7b_checkpoint_every_tensor():
         assert r["n_changed"] == k and r["n_rare"] == n_exp + n_sign, specs[j].name
     assert _check_all_against_oracle(pairs, comp, res, [sp.name for sp in specs]) == 291
     log("  oracle agrees on all 291 tensors")
+    # the verify-first call on copies of the old weights: the same new weights
+    copies = [s.clone() for s, _ in pairs]
+    vdec = bd.DecompressBatch([(c, comp.payload(j, r["payload_bytes"]), r["checksum"])
+                               for j, (c, r) in enumerate(zip(copies, res))], verify_first=True)
+    vdec.run()
+    assert all(r["status"] == bd.OK for r in vdec.results()), "verified decompress failed"
+    for j, (c, (_, d)) in enumerate(zip(copies, pairs)):
+        assert torch.equal(c.view(torch.int16), d.view(torch.int16)), specs[j].name
+    del copies, vdec
+    log("  verify-first decompress bit-exact")
     _apply_in_place_and_compare(pairs, comp, res)
 
 
@@ -154,6 +166,19 @@ def test_config5_70b_half_model_every_tensor():
                            comp.payload(j, res[j]["payload_bytes"])), specs[j].name
     del rev
     log("  reverse payloads identical")
+    # 256-byte record slots (a workspace under 2 % of the weights), the same
+    # first-guess capacities: the same payload bytes
+    small = bd.CompressBatch(pairs, [bd._first_capacity(s.numel()) for s, _ in pairs],
+                             slot_bytes=256)
+    assert small.ws_bytes <= 0.02 * 2 * sum(s.numel() for s, _ in pairs)
+    small.run()
+    for j, r in enumerate(small.results()):
+        assert r["status"] == bd.OK and r["payload_bytes"] == res[j]["payload_bytes"], j
+        assert r["checksum"] == res[j]["checksum"], specs[j].name
+        assert torch.equal(small.payload(j, r["payload_bytes"]),
+                           comp.payload(j, res[j]["payload_bytes"])), specs[j].name
+    del small
+    log("  256-byte slots give the same payloads")
     _apply_in_place_and_compare(pairs, comp, res)
     log("  round trip bit-exact")
 
