@@ -74,3 +74,29 @@ def test_dirty_chunk_bitmap_of_the_in_place_probe():
     assert abs(line_pct - 100 * want.reshape(-1, 8).any(1).mean()) < 1e-3
     start = n - 8192   # the all-zero last pair: its chunks are all clean
     assert want[-(-start // 8):].sum() == 0
+
+
+def test_flat_receiver_lays_the_tensors_end_to_end():
+    """bench.flat_receiver: copies of the tensors as views into one buffer,
+    back to back in order (so the in-place probe's bitmap of the tensors laid
+    end to end describes it), each starting 16-byte aligned; plain clones when
+    a size would break that alignment."""
+    sys.path.insert(0, ROOT)
+    import torch
+    import bench
+    g = torch.Generator().manual_seed(3)
+    ts = [torch.randint(-9, 9, (m,), generator=g, dtype=torch.int16).view(torch.bfloat16)
+          for m in (8192, 4096, 24, 8192 * 3)]
+    buf, views = bench.flat_receiver(ts, torch.device("cpu"))
+    assert buf.numel() == sum(t.numel() for t in ts)
+    at = 0
+    for t, v in zip(ts, views):
+        assert v.dtype == t.dtype and torch.equal(v.view(torch.int16), t.view(torch.int16))
+        assert v.data_ptr() == buf.data_ptr() + 2 * at and v.data_ptr() % 16 == buf.data_ptr() % 16
+        at += t.numel()
+    assert torch.equal(buf, torch.cat([t.view(torch.int16) for t in ts]))
+    buf2, views2 = bench.flat_receiver(ts + [torch.zeros(5, dtype=torch.bfloat16)],
+                                       torch.device("cpu"))
+    assert buf2 is None and len(views2) == 5
+    assert all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+               for a, b in zip(views2, ts))
