@@ -379,7 +379,7 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
 }
 
 // One workgroup per tile, no inter-workgroup waits.  Occupancy hides the
-// load latency: with 53 VGPRs and 18.8 KiB of LDS, eight workgroups fit on a
+// load latency: with 54 VGPRs and 18.8 KiB of LDS, eight workgroups fit on a
 // CU.  That measured faster than a persistent loop that keeps the next
 // tile's loads in registers at half the occupancy.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
