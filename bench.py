@@ -663,6 +663,8 @@ def change_rate_sweep(bd, dev, steps, with_floor=True):
         m = {k: float(np.median(v)) for k, v in t.items() if v}
         out.append({
             "rate": rate, "elements": n, "payload_pct_of_orig": round(100 * P / (2 * n), 4),
+            # the per-block position encoding chosen: bitmaps, the rest gap lists
+            "blocks": (n + 8191) // 8192, "bitmap_blocks": r["n_bitmap_blocks"],
             "caches_flushed_before_each_kernel": with_floor,
             "compress_ms": round(1e3 * m["call_c"], 4),
             "compress_hbm_pct": round(100 * ca / m["call_c"] / 1e9 / HBM_PEAK_GBPS, 2),
