@@ -796,7 +796,8 @@ def main():
         args.no_sweep = True
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the delta path is "
-                          "per-GPU (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+                          "per-GPU (each rank would compress and apply the tensors it holds)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
 
     ensure_built()
