@@ -470,18 +470,18 @@ def dirty_chunks(pairs, n, dev):
     return packed.view(torch.int32), chunk_pct, line_pct
 
 
-def read_ceiling(bd, n, dev, steps, dirty=None):
+def read_ceiling(a, b, steps, dirty=None):
     """The read ceiling of the encoder's access pattern (bf16d_probe_read: one
-    workgroup per 8192-element block, 16-byte loads, nothing else) over two
-    flat n-element arrays, as the encoder reads old and new, and over one, as
-    the apply pass reads old.  Their contents do not matter.  With the
-    workload's changed-chunk bitmap, also the apply pass's writes alone
-    (bf16d_probe_write: the changed 16-byte chunks, no reads)."""
+    workgroup per 8192-element block, 16-byte loads, nothing else) over the
+    two flat arrays a and b, as the encoder reads old and new, and over a
+    alone, as the apply pass reads old.  Their contents do not matter; they
+    are allocated before anything is timed (memory allocated right after a
+    large free reads slower for a while).  With the workload's changed-chunk
+    bitmap, also the apply pass's writes alone (bf16d_probe_write into b: the
+    changed 16-byte chunks, no reads)."""
     from lossless_bf16_weight_xor_amd import probe
-    a = torch.empty(n, dtype=torch.int16, device=dev)
-    b = torch.empty_like(a)
-    sink = torch.empty(1, dtype=torch.int64, device=dev)
-    full = n // 8192 * 8192
+    sink = torch.empty(1, dtype=torch.int64, device=a.device)
+    full = a.numel() // 8192 * 8192
     out = {}
     for key, arrays in (("read2", (a, b)), ("read1", (a, None))):
         probe.probe_read(*arrays, sink=sink)
@@ -507,8 +507,6 @@ def read_ceiling(bd, n, dev, steps, dirty=None):
             "ms": round(ev[0].elapsed_time(ev[1]) / steps, 4),
             "note": "the apply pass's writes alone (no reads); with read1 it splits the "
                     "in-place floor into its two parts"}
-    del a, b
-    torch.cuda.empty_cache()
     return out
 
 
@@ -810,6 +808,13 @@ def main():
     torch.cuda.synchronize()
     n_total = sum(s.numel() for s, _ in pairs)
     log(f"generated {len(pairs)} tensors, {n_total} elements in {time.time() - t0:.1f}s")
+    # the read probes' two flat arrays, held from here to the end: memory
+    # allocated right after a large free reads slower for a while
+    probe_arrays = None
+    if not args.no_probe:
+        n_probe = min(n_total, 8_000_000_000)
+        probe_arrays = (torch.empty(n_probe, dtype=torch.int16, device=dev),
+                        torch.empty(n_probe, dtype=torch.int16, device=dev))
 
     # payload capacity: framing + 1/16 of the weights, exact size on overflow
     caps = [bd._first_capacity(s.numel()) for s, _ in pairs]
@@ -931,6 +936,24 @@ def main():
                 f"rounds {floor['apply_kernel_same_rounds_ms']} ms "
                 f"({floor['dirty_lines_pct']}% of 128-byte lines written)")
 
+    ceiling = None
+    if probe_arrays is not None:
+        ceiling = read_ceiling(*probe_arrays, max(3, args.steps // 2),
+                               dirty if n_total <= 8_000_000_000 else None)
+        del dirty
+        ceiling["encode_kernel_frac_of_read2"] = round(comp_alg / t_enc / 1e9 /
+                                                       ceiling["read2"]["gbps"], 4)
+        ceiling["apply_kernel_frac_of_read1"] = round(dec_alg / t_app / 1e9 /
+                                                      ceiling["read1"]["gbps"], 4)
+        log(f"read ceiling: {ceiling['read2']['gbps']} GB/s over two arrays, "
+            f"{ceiling['read1']['gbps']} GB/s over one")
+        # (the probe covers whole 8192-element blocks of the receiver's buffer:
+        # all but the last few thousand elements of the workload)
+        if floor is not None and floor["elements"] >= 0.999 * n_total:
+            ceiling["inplace_floor"] = floor
+            ceiling["apply_kernel_frac_of_inplace_floor"] = round(
+                floor["ms"] / floor["apply_kernel_same_rounds_ms"], 4)
+
     if args.with_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -1012,24 +1035,9 @@ def main():
     if not args.no_sweep and args.workload == "7b":
         sweep = change_rate_sweep(bd, dev, 5, with_floor=not args.no_probe)
 
-    # last of the GPU measurements: it frees two checkpoint-sized buffers
-    ceiling = None
-    if not args.no_probe:
-        ceiling = read_ceiling(bd, min(n_total, 8_000_000_000), dev, max(3, args.steps // 2),
-                               dirty if n_total <= 8_000_000_000 else None)
-        del dirty
-        ceiling["encode_kernel_frac_of_read2"] = round(comp_alg / t_enc / 1e9 /
-                                                       ceiling["read2"]["gbps"], 4)
-        ceiling["apply_kernel_frac_of_read1"] = round(dec_alg / t_app / 1e9 /
-                                                      ceiling["read1"]["gbps"], 4)
-        log(f"read ceiling: {ceiling['read2']['gbps']} GB/s over two arrays, "
-            f"{ceiling['read1']['gbps']} GB/s over one")
-        # (the probe covers whole 8192-element blocks of the receiver's buffer:
-        # all but the last few thousand elements of the workload)
-        if floor is not None and floor["elements"] >= 0.999 * n_total:
-            ceiling["inplace_floor"] = floor
-            ceiling["apply_kernel_frac_of_inplace_floor"] = round(
-                floor["ms"] / floor["apply_kernel_same_rounds_ms"], 4)
+    # the probe arrays go last: a large free slows the streamed copies for a while
+    del probe_arrays
+    torch.cuda.empty_cache()
 
     gpu_payloads = [None] * len(pairs)
     cpu = None

@@ -19,7 +19,9 @@ extern "C" {
 /* Reads the first 8192 * floor(n / 8192) elements of a, and of b unless b is
  * NULL, with the encoder's whole-block access pattern (one workgroup per
  * 8192-element block, 16-byte loads, the blocks split into one contiguous
- * range per XCD as the main kernels take them) and does nothing else, so that
+ * range per XCD as the main kernels take them; with b, non-temporal loads as
+ * the encoder's, and without it plain loads as the apply pass's) and does
+ * nothing else, so that
  * its time is the read ceiling of that pattern: the "achievable" figure that
  * kernel times are compared against, beside the published HBM peak.  a and b
  * are device pointers to at least n elements each, 16-byte aligned; sink is 8

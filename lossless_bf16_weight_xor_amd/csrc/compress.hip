@@ -79,17 +79,17 @@ __device__ __forceinline__ TileRef tile_ref(const CompressJob &job, uint64_t t) 
 }
 
 // kFull (a whole block): eight unconditional 16-byte loads, all in flight
-// at once.  Otherwise (the short last block of a tensor) element by element
-// up to L, zero beyond.
+// at once, marked non-temporal (load_stream16).  Otherwise (the short last
+// block of a tensor) element by element up to L, zero beyond.
 template <bool kFull>
 __device__ __forceinline__ void load_tile(const TileRef &t, uint4 (&o)[kChunksPerThread],
                                           uint4 (&nw)[kChunksPerThread]) {
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
         const uint32_t e0 = 8 * (threadIdx.x + kThreads * i);
-        if (kFull) {
-            o[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(t.src + e0);
-            nw[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(t.dst + e0);
+        if (kFull) {   // both checkpoints are read once: streamed past the caches
+            o[i] = load_stream16(t.src + e0);
+            nw[i] = load_stream16(t.dst + e0);
         } else {
             o[i] = make_uint4(0, 0, 0, 0);
             nw[i] = make_uint4(0, 0, 0, 0);

@@ -7,7 +7,8 @@
 // else: one workgroup of 256 threads per 8192-element block, four 16-byte
 // loads per thread from each array, all in flight together.  Its time is the
 // read ceiling of that pattern on the device, against which the encoder
-// (both checkpoints) and the apply pass (one) are compared.
+// (both checkpoints, read with the encoder's non-temporal loads) and the
+// apply pass (one, read with its plain loads) are compared.
 //
 // probe_write_kernel: the apply pass's writes alone: each 16-byte chunk a
 // bitmap marks is written, in the same block order, and nothing is read.
@@ -42,9 +43,13 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint16_t *__
 #pragma unroll
     for (uint32_t i = 0; i < kChunksPerThread; ++i) {
         const uint64_t e0 = base + 8 * (threadIdx.x + kThreads * i);
-        x[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(a + e0);
-        y[i] = make_uint4(0, 0, 0, 0);
-        if constexpr (kTwo) y[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(b + e0);
+        if constexpr (kTwo) {   // the encoder's loads: non-temporal
+            x[i] = load_stream16(a + e0);
+            y[i] = load_stream16(b + e0);
+        } else {                // the apply pass's loads: plain
+            x[i] = *reinterpret_cast<BF16D_GMEM const uint4 *>(a + e0);
+            y[i] = make_uint4(0, 0, 0, 0);
+        }
     }
     uint64_t acc = 0;
 #pragma unroll
