@@ -369,7 +369,8 @@ __device__ __forceinline__ void encode_one(const TileRef &tr, uint64_t t, uint16
         if (dst) {
             uint4 *out = reinterpret_cast<uint4 *>(dst);
             const uint4 *rec = reinterpret_cast<const uint4 *>(s_rec);
-            for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads) out[u] = rec[u];
+            for (uint32_t u = tid; u < (k.len + 15) / 16; u += kThreads)
+                store_stream16(out + u, rec[u]);   // read next by the place kernel only
         }
     } else if (tid == 0) {
         overflow[atomicAdd(&ctrl->overflow_count, 1u)] = (uint32_t)t;

@@ -554,6 +554,20 @@ __device__ __forceinline__ uint4 load_stream16(BF16D_GMEM const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A 16-byte store of data that this kernel will not read again, marked
+// non-temporal.  The encoder's record stores take it: with the checkpoint
+// loads also non-temporal, they made the encoder 5 % faster on the 7B-shaped
+// workload (with plain loads the same stores measured no faster).
+__device__ __forceinline__ void store_stream16(void *p, const uint4 &q) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    v4u v;
+    v.x = q.x;
+    v.y = q.y;
+    v.z = q.z;
+    v.w = q.w;
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(p));
+}
+
 // Load 8 bf16 patterns at p, of which the first `valid` (<= 8) exist.
 __device__ __forceinline__ uint4 load_chunk(BF16D_GMEM const uint16_t *p, uint32_t valid) {
     if (valid >= 8) return *reinterpret_cast<BF16D_GMEM const uint4 *>(p);
