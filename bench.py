@@ -474,9 +474,8 @@ def read_ceiling(a, b, steps, dirty=None):
     """The read ceiling of the encoder's access pattern (bf16d_probe_read: one
     workgroup per 8192-element block, 16-byte loads, nothing else) over the
     two flat arrays a and b, as the encoder reads old and new, and over a
-    alone, as the apply pass reads old.  Their contents do not matter; they
-    are allocated before anything is timed (memory allocated right after a
-    large free reads slower for a while).  With the workload's changed-chunk
+    alone, as the apply pass reads old.  Their contents do not matter; the
+    caller allocates them before anything is timed.  With the workload's changed-chunk
     bitmap, also the apply pass's writes alone (bf16d_probe_write into b: the
     changed 16-byte chunks, no reads)."""
     from lossless_bf16_weight_xor_amd import probe
@@ -808,8 +807,8 @@ def main():
     torch.cuda.synchronize()
     n_total = sum(s.numel() for s, _ in pairs)
     log(f"generated {len(pairs)} tensors, {n_total} elements in {time.time() - t0:.1f}s")
-    # the read probes' two flat arrays, held from here to the end: memory
-    # allocated right after a large free reads slower for a while
+    # the read probes' two flat arrays, held from here to the end, so that the
+    # ceilings do not follow the other measurements' allocations and frees
     probe_arrays = None
     if not args.no_probe:
         n_probe = min(n_total, 8_000_000_000)
