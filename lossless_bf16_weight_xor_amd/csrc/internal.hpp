@@ -545,9 +545,9 @@ __device__ __forceinline__ uint32_t chunk_elem(const uint4 &v, int s) {
 // A 16-byte load of data that is read once and never written: marked
 // non-temporal (`nt`), so the lines of a checkpoint streamed through the
 // caches do not stay there at the cost of other data.  On the 7B-shaped
-// workload the encoder reads its two checkpoints 5 % faster this way, and a
-// read-only probe of the same pattern 8 %.  Not for a pass that writes back
-// what it reads: the in-place apply measured 29 % slower with it.
+// workload the encoder runs 2-5 % faster this way, and a read-only probe of
+// the same pattern 8 %.  Not for a pass that writes back what it reads: the
+// in-place apply measured 29 % slower with it.
 __device__ __forceinline__ uint4 load_stream16(BF16D_GMEM const void *p) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     const v4u v = __builtin_nontemporal_load(reinterpret_cast<BF16D_GMEM const v4u *>(p));
@@ -556,8 +556,9 @@ __device__ __forceinline__ uint4 load_stream16(BF16D_GMEM const void *p) {
 
 // A 16-byte store of data that this kernel will not read again, marked
 // non-temporal.  The encoder's record stores take it: with the checkpoint
-// loads also non-temporal, they made the encoder 5 % faster on the 7B-shaped
-// workload (with plain loads the same stores measured no faster).
+// loads also non-temporal, they made the encoder 3-5 % faster on the
+// 7B-shaped workload when it runs right after a decompress, as in a
+// benchmark step (with plain loads the same stores measured no faster).
 __device__ __forceinline__ void store_stream16(void *p, const uint4 &q) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     v4u v;
