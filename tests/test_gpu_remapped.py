@@ -88,12 +88,15 @@ def test_remapped_failure_leaves_the_physical_layout_old(prepared):
     assert torch.equal(fused.view(torch.int16), old.view(torch.int16))
 
 
+@pytest.mark.parametrize("prepared", [True, False])
 @pytest.mark.parametrize("overwrite", [False, True])
-def test_remapped_apply_of_version_2_payloads(overwrite):
+def test_remapped_apply_of_version_2_payloads(overwrite, prepared):
     """Bound payloads through the remapped call (the binding is not checked
-    there): overwrite records are verified on the physical layout and then
-    written at their remapped positions."""
-    log(f"case remapped version-2 overwrite={overwrite}")
+    there).  Overwrite records land at their remapped positions: the prepared
+    call verifies them first and writes them after; the plain remapped call,
+    whose workspace has room for an undo area, writes them in place and
+    restores the kept values of a job that fails."""
+    log(f"case remapped version-2 overwrite={overwrite} prepared={prepared}")
     R, C = 512, 128
     (g0, g1) = synth.make_pair((R, C), "0.3", synth.MIX_ADVERSARIAL, 6100, DEV)
     (u0, u1) = synth.make_pair((R, C), "0.03", synth.MIX_ADVERSARIAL, 6101, DEV)
@@ -103,15 +106,47 @@ def test_remapped_apply_of_version_2_payloads(overwrite):
     want = _paired(g1, u1)
     items = [((R * C, _segments(fused, 0, R, C)), out[0][0], out[0][1]),
              ((R * C, _segments(fused, 1, R, C)), out[1][0], out[1][1])]
-    res = bd.decompress_remapped(items)
+    res = bd.decompress_remapped(items, prepared=prepared)
     assert [r["status"] for r in res] == [bd.OK, bd.OK]
     assert torch.equal(fused.view(torch.int16), want.view(torch.int16))
-    # a wrong checksum on an overwrite payload leaves the fused layout untouched
+    # a wrong checksum leaves the fused layout as it was (untouched, or
+    # written and then restored)
     before = fused.clone()
     items[0] = (items[0][0], out[0][0], out[0][1] ^ 1)
-    res = bd.decompress_remapped(items[:1])
+    res = bd.decompress_remapped(items[:1], prepared=prepared)
     assert res[0]["status"] == bd.ECHECKSUM
     assert torch.equal(fused.view(torch.int16), before.view(torch.int16))
+
+
+def test_remapped_sparse_overwrite_payloads_in_place_and_restored():
+    """Sparse overwrite payloads through the plain remapped call, whose
+    workspace (bf16d_workspace_bytes_remapped) leaves room for the undo area:
+    they are written in place at their remapped positions.  A job given a
+    wrong checksum ends with its physical layout as it was (the kept values
+    written back), the other job rebuilt; the same batch then applies."""
+    log("case remapped sparse overwrite, undo path")
+    R, C = 1024, 256
+    (g0, g1) = synth.make_pair((R, C), "0.02", synth.MIX_DEFAULT, 6300, DEV)
+    (u0, u1) = synth.make_pair((R, C), "0.02", synth.MIX_DEFAULT, 6301, DEV)
+    out = bd.compress_batch([(g0.reshape(-1), g1.reshape(-1)), (u0.reshape(-1), u1.reshape(-1))],
+                            [(3, 4, True), (3, 4, True)])
+    n = R * C
+    payload_total = out[0][0].numel() + out[1][0].numel()
+    ws = bd._native.lib().bf16d_workspace_bytes_remapped(2 * n, 2, 2 * (R // 64))
+    assert payload_total < ws // 2   # room for the undo area beside the call's layout
+    fused = _paired(g0, u0)
+    old = fused.clone()
+    items = [((n, _segments(fused, 0, R, C)), out[0][0], out[0][1] ^ 1),
+             ((n, _segments(fused, 1, R, C)), out[1][0], out[1][1])]
+    res = bd.decompress_remapped(items, prepared=False)
+    assert [r["status"] for r in res] == [bd.ECHECKSUM, bd.OK]
+    want = _paired(g0, u1)   # job 0 restored, job 1 rebuilt
+    assert torch.equal(fused.view(torch.int16), want.view(torch.int16))
+    fused.copy_(old)
+    items[0] = (items[0][0], out[0][0], out[0][1])
+    res = bd.decompress_remapped(items, prepared=False)
+    assert [r["status"] for r in res] == [bd.OK, bd.OK]
+    assert torch.equal(fused.view(torch.int16), _paired(g1, u1).view(torch.int16))
 
 
 def test_a_prepared_layout_serves_many_steps():
