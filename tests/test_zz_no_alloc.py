@@ -56,13 +56,13 @@ def _workspace_form(items):
     return _results(res, count)
 
 
-def _batch(specs, seed0):
+def _batch(specs, seed0, bindings=None):
     """(old, new, payload, checksum) per spec (shape, rate); the payloads come
-    from the batched compress."""
+    from the batched compress (version-2 ones with `bindings`)."""
     pairs = [synth.make_pair(sh, rate, synth.MIX_ADVERSARIAL, seed0 + j, DEV)
              for j, (sh, rate) in enumerate(specs)]
     pairs = [(s.reshape(-1), d.reshape(-1)) for s, d in pairs]
-    out = bd.compress_batch(pairs)
+    out = bd.compress_batch(pairs, bindings)
     return [(s, d, p.clone(), cs) for (s, d), (p, cs, _) in zip(pairs, out)]
 
 
@@ -103,6 +103,18 @@ def test_two_calls_in_a_row_match_the_workspace_form():
     small = [((8192 + 13,), "0.05"), ((3,), "1.0"), ((1000, 37), "0.2")]
     st2 = _compare(_batch(small, 950), "second call, smaller")
     assert st2[0] == bd.OK and st2[1] == bd.ECHECKSUM
+
+
+def test_overwrite_payloads_match_the_workspace_form():
+    """Version-2 payloads, overwrite and XOR mixed, with the same failures:
+    both forms have room for the undo area (the scratch, and the workspace
+    bf16d_workspace_bytes sizes), so overwrite jobs are written in place and
+    the failing ones restored, with equal results and weights."""
+    specs = [((1024, 1024), "0.02"), ((3 * 8192 + 5,), "0.05"), ((4096,), "0.3"),
+             ((2 * 8192,), "0.02"), ((777,), "1.0"), ((8192,), "0.01"), ((5000,), "0.1")]
+    bindings = [(7, 8, j % 2 == 0) for j in range(len(specs))]
+    st = _compare(_batch(specs, 970, bindings), "version-2 payloads")
+    assert {bd.OK, bd.ECHECKSUM} <= set(st)
 
 
 def test_a_batch_larger_than_the_scratch_is_refused_untouched():
