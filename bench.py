@@ -23,25 +23,30 @@ Reported:
               timed with events recorded around it on its stream
   roofline_decompress : the apply kernel the same way, and on its effective
               bytes: 2n + P + every 32-byte sector that holds a change (the
-              device writes sectors, not the changed elements alone)
+              device writes sectors, not the changed elements alone); and its
+              fraction of the in-place floor probe timed in the same rounds
   decompress_verify_first : the two-pass decompress that checks every job
               before writing it (weights untouched on failure), against the
               single in-place pass
   compress_small_workspace : the same compress with 256-byte record slots
               (workspace about 1.9 % of the weights instead of 12.9 %)
   change_rate_sweep : compress and decompress of one 1 GiB tensor at 0.085,
-              1, 3 and 5 % uniform changes, with their main kernels'
-              fractions of 8 TB/s
+              1, 3 and 5 % uniform changes, each kernel timed after a cache
+              flush, with their main kernels' fractions of 8 TB/s, of the read
+              ceiling and of the in-place floor, and a compress timed right
+              after a decompress; the bitmap / gap-list histogram per rate
   achievable: the read ceiling of the encoder's access pattern (a probe
-              kernel that only reads), over old and new and over old alone,
-              and each main kernel's fraction of it; and the in-place floor
-              (a probe that reads old and writes back, unchanged, the 16-byte
-              chunks the delta changes: a reference point for that traffic,
-              not a strict bound) with the apply kernel's fraction of it
+              kernel that only reads, with the kernels' own loads), over old
+              and new and over old alone, and each main kernel's fraction of
+              it; the apply pass's changed-chunk writes alone; and the
+              in-place floor (a probe that reads old and writes back,
+              unchanged, the 16-byte chunks the delta changes: a reference
+              point for that traffic, not a strict bound), timed in the same
+              rounds as the apply kernel over the receiver's own buffer
   remapped_decompress : the same decompress onto a layout with each layer's
               gate and up projections paired in groups of 64 rows
   bound_overwrite : the same pair as version-2 overwrite payloads (absolute
-              values, verified then written, version words committed)
+              values, written in place with an undo log)
   codec_race : the host race of general-purpose codecs over every payload,
               and the payload % of the weights after it
   streamed_receiver : the same decompress with the payloads in pinned host
@@ -51,7 +56,8 @@ Reported:
               three slots and one lane, and two slots on one stream, for
               comparison);
               PCIe-inclusive, context, not `value`
-  cpu_baseline : the CPU oracle on a bounded sample of the same workload
+  cpu_baseline : the CPU oracle on a bounded sample of the same workload, on
+              one core, and beside it on up to 16 host threads
 
 Only one GPU is used; --gpus above 1 is refused.
 """
