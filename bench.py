@@ -402,9 +402,11 @@ def remapped(bd, names, shapes, pairs, payloads, cs_new, cs_old, steps):
 
 def bound_overwrite(bd, pairs, steps):
     """Version-2 payloads of the same checkpoint pair in overwrite form (each
-    change carries its new value; the apply is verified, then written), bound
-    from version 1 to 2, applied with the receiver's version words.  Reports
-    the payload size and whole-call times beside the XOR path's."""
+    change carries its new value; with the workspace bf16d_workspace_bytes
+    sizes, the apply writes in place and keeps the replaced values in an undo
+    area), bound from version 1 to 2, applied with the receiver's version
+    words.  Reports the payload size and whole-call times beside the XOR
+    path's."""
     n = sum(s.numel() for s, _ in pairs)
     binds = [(1, 2, True)] * len(pairs)
     caps = [bd._first_capacity(s.numel()) + bd.BOUND_EXTRA_BYTES for s, _ in pairs]
